@@ -1,0 +1,10 @@
+"""CPU fp64 attention oracle.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline leg
+of ``bench.py`` may import this package.  The GPU library never calls it.
+"""
+from .exact import (attention, attention_kvcache, attention_varlen, attend_head,
+                        default_scale, merge_partials)
+
+__all__ = ["attention", "attention_kvcache", "attention_varlen", "attend_head",
+           "default_scale", "merge_partials"]

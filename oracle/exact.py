@@ -1,0 +1,240 @@
+"""CPU fp64 oracle for exact scaled-dot-product attention.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The GPU library never calls it and shares no code with it.
+
+What it computes is the plain definition, written out and materialised:
+S = scale * Q K^T, P = softmax(S), O = P V ("FlashAttention完整说明", section 一,
+equations (1)-(3)).  The tiled method reaches this exactly up to rounding order
+(same page, section 二.1; Inference Cookbook FAQ Q10), so there is no tiling,
+no online softmax and no reordering here: every query row is scored against
+every key, masked, normalised by an ordinary softmax and multiplied with V, in
+float64 with numpy (matmul via the installed BLAS).
+
+Semantics, each from the pages, with the readings taken where they are silent:
+- layout (batch, seqlen, heads, head_dim) (FAQ Q5);
+- default scale 1/sqrt(head_dim) (FAQ Q12);
+- softcap c*tanh(s/c) applied to the scaled score before masking (FAQ Q22);
+  reading: the scale is applied first and c <= 0 means "off";
+- causal mask aligned to the bottom-right corner: with off = s_k - s_q, key j
+  is visible to row i iff j <= i + off (FAQ Q6);
+- window (left, right): row i sees keys in [i + off - left, i + off + right],
+  both ends inclusive, a negative bound meaning unbounded; right = 0 is the
+  causal case (FAQ Q21); reading: the same bottom-right offset applies to the
+  window when s_q != s_k, and ``causal`` forces right = 0;
+- a row with no visible key outputs O = 0 and LSE = -inf (reading of FAQ Q6's
+  "no K to attend");
+- LSE is the natural log of the sum of exp over the row's visible final scores
+  ("FlashAttention完整说明", section 二.2 keeps only O and the softmax
+  statistics);
+- grouped heads: query head h reads KV head h // (h_q // h_kv) (FAQ Q15);
+- variable length: sequences packed end to end and addressed by int32 prefix
+  sums cu_seqlens (FAQ Q8); every sequence is attended on its own;
+- KV-cache decode: the query attends to the first cache_seqlens[b] cache rows
+  (FAQ Q17), with the bottom-right offset s_k - 1.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x):
+    """Upcast a numpy array or a torch tensor (any float dtype) to a float64 numpy array."""
+    if hasattr(x, "detach"):  # torch tensor: fp16/bf16 -> fp32 is exact, fp32 -> fp64 is exact
+        x = x.detach().cpu().float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(d), the default softmax scale (FAQ Q12)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def scores(q2, k2, scale):
+    """S = scale * Q K^T for one head: (s_q, d) x (s_k, d) -> (s_q, s_k)."""
+    return scale * (q2 @ k2.T)
+
+
+def apply_softcap(s, softcap):
+    """c * tanh(s / c) for c > 0, identity otherwise (FAQ Q22)."""
+    if softcap is None or softcap <= 0.0:
+        return s
+    return softcap * np.tanh(s / softcap)
+
+
+def visible(rows, s_q, s_k, causal, window_left, window_right):
+    """Boolean (len(rows), s_k) mask: key j visible from query row i.
+
+    off = s_k - s_q aligns the causal diagonal to the bottom-right (FAQ Q6);
+    the window edges use the same offset (FAQ Q21).  Negative window bounds are
+    unbounded; causal forces the right bound to 0.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    off = s_k - s_q
+    wr = 0 if causal else window_right
+    j = np.arange(s_k, dtype=np.int64)[None, :]
+    i = rows[:, None]
+    m = np.ones((rows.size, s_k), dtype=bool)
+    if wr >= 0:
+        m &= j <= i + off + wr
+    if window_left >= 0:
+        m &= j >= i + off - window_left
+    return m
+
+
+def softmax_rows(s, mask):
+    """Row softmax over the visible entries; rows with nothing visible give P = 0.
+
+    Returns (P, LSE) with LSE = m + ln(sum exp(s - m)) and -inf for empty rows.
+    """
+    s = np.where(mask, s, NEG_INF)
+    any_vis = mask.any(axis=1)
+    m = np.where(any_vis, s.max(axis=1, initial=NEG_INF), 0.0)
+    e = np.where(mask, np.exp(s - m[:, None]), 0.0)
+    ell = e.sum(axis=1)
+    p = np.where(any_vis[:, None], e / np.where(ell > 0, ell, 1.0)[:, None], 0.0)
+    lse = np.where(any_vis, m + np.log(np.where(ell > 0, ell, 1.0)), NEG_INF)
+    return p, lse
+
+
+def attend_head(q2, k2, v2, *, scale, causal=False, window_left=-1, window_right=-1,
+                softcap=0.0, rows=None, return_probs=False):
+    """Attention for one (query head, KV head) pair.
+
+    q2 (s_q, d), k2 and v2 (s_k, d) as float64.  ``rows`` restricts the output to
+    those query rows (each row depends only on itself), which keeps the
+    16384-token shapes affordable.  Returns O (len(rows), d) and LSE (len(rows),)
+    and, if asked, P (len(rows), s_k).
+    """
+    s_q, s_k = q2.shape[0], k2.shape[0]
+    if rows is None:
+        rows = np.arange(s_q)
+    rows = np.asarray(rows, dtype=np.int64)
+    if s_k == 0 or rows.size == 0:
+        o = np.zeros((rows.size, v2.shape[1]))
+        lse = np.full(rows.size, NEG_INF)
+        p = np.zeros((rows.size, s_k))
+        return (o, lse, p) if return_probs else (o, lse)
+    s = scores(q2[rows], k2, scale)
+    s = apply_softcap(s, softcap)
+    mask = visible(rows, s_q, s_k, causal, window_left, window_right)
+    p, lse = softmax_rows(s, mask)
+    o = p @ v2
+    return (o, lse, p) if return_probs else (o, lse)
+
+
+def _kv_head(h, h_q, h_kv):
+    if h_q % h_kv != 0:
+        raise ValueError("heads_q must be a multiple of heads_kv")
+    return h // (h_q // h_kv)
+
+
+def attention(q, k, v, *, softmax_scale=None, causal=False, window_size=(-1, -1),
+              softcap=0.0, rows=None, heads=None, return_probs=False):
+    """Dense attention.  q (b, s_q, h_q, d); k, v (b, s_k, h_kv, d).
+
+    Returns O (b, s_q, h_q, d) and LSE (b, h_q, s_q) as float64 (and P
+    (b, h_q, s_q, s_k) if asked).  With ``rows`` (query indices) and/or ``heads``
+    (query head indices) only those entries are computed; the others stay NaN.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    b, s_q, h_q, d = q.shape
+    s_k, h_kv = k.shape[1], k.shape[2]
+    dv = v.shape[3]
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    row_idx = np.arange(s_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    head_idx = range(h_q) if heads is None else heads
+    o = np.full((b, s_q, h_q, dv), np.nan)
+    lse = np.full((b, h_q, s_q), np.nan)
+    p_all = np.zeros((b, h_q, s_q, s_k)) if return_probs else None
+    wl, wr = window_size
+    for bi in range(b):
+        for h in head_idx:
+            hk = _kv_head(h, h_q, h_kv)
+            res = attend_head(q[bi, :, h, :], k[bi, :, hk, :], v[bi, :, hk, :], scale=scale,
+                              causal=causal, window_left=wl, window_right=wr, softcap=softcap,
+                              rows=row_idx, return_probs=return_probs)
+            o[bi, row_idx, h, :] = res[0]
+            lse[bi, h, row_idx] = res[1]
+            if return_probs:
+                p_all[bi, h][row_idx] = res[2]
+    return (o, lse, p_all) if return_probs else (o, lse)
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, softmax_scale=None, causal=False,
+                     window_size=(-1, -1), softcap=0.0):
+    """Packed variable-length attention (FAQ Q8).
+
+    q (total_q, h_q, d); k, v (total_k, h_kv, d); cu_seqlens_* int prefix sums
+    of length batch + 1.  Each sequence is attended on its own, with its own
+    bottom-right offset.  Returns O (total_q, h_q, d) and LSE (h_q, total_q).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    ck = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+    total_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    o = np.zeros((total_q, h_q, v.shape[2]))
+    lse = np.full((h_q, total_q), NEG_INF)
+    wl, wr = window_size
+    for bi in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[bi], cq[bi + 1], ck[bi], ck[bi + 1]
+        for h in range(h_q):
+            hk = _kv_head(h, h_q, h_kv)
+            ob, lb = attend_head(q[q0:q1, h, :], k[k0:k1, hk, :], v[k0:k1, hk, :], scale=scale,
+                                 causal=causal, window_left=wl, window_right=wr, softcap=softcap)
+            o[q0:q1, h, :] = ob
+            lse[h, q0:q1] = lb
+    return o, lse
+
+
+def attention_kvcache(q, k_cache, v_cache, cache_seqlens=None, *, softmax_scale=None,
+                      causal=False, window_size=(-1, -1), softcap=0.0, heads=None):
+    """KV-cache decode (FAQ Q17): q (b, s_q, h_q, d) attends to the first
+    cache_seqlens[b] rows of k_cache/v_cache (b, s_cache, h_kv, d).
+
+    ``cache_seqlens`` None means the full cache.  Returns O (b, s_q, h_q, d) and
+    LSE (b, h_q, s_q).
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    b = q.shape[0]
+    if cache_seqlens is None:
+        lens = [kc.shape[1]] * b
+    else:
+        lens = [int(x) for x in np.asarray(cache_seqlens).tolist()]
+    os_, ls_ = [], []
+    for bi in range(b):
+        n = lens[bi]
+        ob, lb = attention(q[bi:bi + 1], kc[bi:bi + 1, :n], vc[bi:bi + 1, :n],
+                           softmax_scale=softmax_scale, causal=causal, window_size=window_size,
+                           softcap=softcap, heads=heads)
+        os_.append(ob)
+        ls_.append(lb)
+    return np.concatenate(os_, axis=0), np.concatenate(ls_, axis=0)
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention results over disjoint key sets by their log-sum-exp.
+
+    The merge of the online softmax ("FlashAttention完整说明", section 二.1):
+    LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.  A part with
+    LSE_s = -inf has weight 0; if every part is empty the result is O = 0,
+    LSE = -inf.  o_parts: (S, ..., d); lse_parts: (S, ...).
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    finite = np.isfinite(m)
+    m0 = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m0[None]), 0.0)
+    tot = w.sum(axis=0)
+    lse = np.where(finite, m0 + np.log(np.where(tot > 0, tot, 1.0)), NEG_INF)
+    wn = w / np.where(tot > 0, tot, 1.0)[None]
+    o = (wn[..., None] * o_parts).sum(axis=0)
+    o = np.where(finite[..., None], o, 0.0)
+    return o, lse
