@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention forward on one MI355X.
+
+One step is one forward call of the causal prefill workload: packed qkv
+(2, 1024, 3, 16, 128) bf16, causal, scale 1/sqrt(128) ("FlashAttention完整说明",
+section 六.1).  Inputs are resident in device memory before the timed region.
+The FLOP count is the pages' 4*b*h*s_q*s_k*d halved for causal (Inference
+Cookbook FAQ Q16).  The KV-cache decode workload (batch 8, 16384 cached
+tokens, 32 query / 8 KV heads, d 128, bf16, automatic num_splits) is timed in
+the same run and reported as HBM GB/s under "decode".
+
+Prints one JSON line.  Options:
+  --gpus N            only 1 is supported (the method runs on one GPU here)
+  --steps K --warmup W
+  --no-cpu-baseline   skip the CPU oracle timing
+  --no-decode         skip the decode measurement
+  --only {prefill,decode,copy}  run one part only (for profiler runs)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "attn fwd TFLOPS (% bf16 MFMA peak) at b2 s1024 h16 d128; decode HBM GB/s"
+PREFILL_SOURCES = ["exact_attention_43_amd/csrc/fwd_prefill.hip",
+                   "exact_attention_43_amd/csrc/device_common.h"]
+DECODE_SOURCES = ["exact_attention_43_amd/csrc/fwd_decode.hip",
+                  "exact_attention_43_amd/csrc/device_common.h"]
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, paths):
+    """HBM bytes per launch from a committed counter summary, if it matches the current kernel."""
+    fn = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != sources_sha(paths):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    return ap.parse_args()
+
+
+def prefill_step_fn(ex, qkv, out, lse, causal=True):
+    """Build the C-ABI call once; the returned closure only launches."""
+    import ctypes as C
+    import torch
+    b, s, _, h, d = qkv.shape
+    a = ex.FwdArgs()
+    a.dtype = ex.EXATTN_BF16 if qkv.dtype == torch.bfloat16 else ex.EXATTN_F16
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = b, s, s, h, h, d
+    es = qkv.element_size()
+    base = qkv.data_ptr()
+    a.q, a.k, a.v = base, base + h * d * es, base + 2 * h * d * es
+    a.o, a.lse = out.data_ptr(), lse.data_ptr()
+    st = list(qkv.stride())
+    for n in ("q_stride", "k_stride", "v_stride"):
+        getattr(a, n)[:] = [st[0], st[1], st[3]]
+    a.o_stride[:] = list(out.stride()[:3])
+    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    a.softmax_scale = 0.0
+    a.softcap = 0.0
+    a.causal = 1 if causal else 0
+    a.window_left = a.window_right = -1
+    L = ex.lib()
+    ref = C.byref(a)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        rc = L.exattn_fwd(ref, stream)
+        if rc != 0:
+            ex._raise_for(rc, "exattn_fwd")
+    return step
+
+
+def time_steps(step, steps, warmup, between=None):
+    """Warm up, then time `steps` calls: wall clock over the whole region (synchronised on both
+    sides) and a HIP event pair around each call on the launching stream."""
+    import torch
+    for _ in range(warmup):
+        if between:
+            between()
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if between:
+            between()
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return wall_ms / steps, sum(durs) / len(durs), durs[len(durs) // 2], durs[0]
+
+
+def cpu_baseline(w, flops_full):
+    """The fp64 oracle on the host cores, on the same workload (bounded to ~10-30 s)."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from exact_attention_43_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    qkv = W.packed_qkv(w.batch, w.seqlen_q, w.heads_q, w.head_dim, seed=w.seed)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    heads = list(range(w.heads_q))
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.attention(q, k, v, causal=True, heads=heads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or passes >= 20:
+            break
+    sec = el / passes
+    return {"value": round(flops_full / sec / 1e12, 6), "unit": "TFLOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"full causal_prefill workload (b2 s1024 h16 d128, all 32 heads), "
+                      f"{passes} pass(es), {sec:.2f} s per pass, numpy fp64 materialising S and P"}
+
+
+def run_prefill(ex, W, args):
+    import torch
+    w = W.WORKLOADS["causal_prefill"]
+    qkv = W.packed_qkv(w.batch, w.seqlen_q, w.heads_q, w.head_dim, seed=w.seed).cuda()
+    out = torch.empty((w.batch, w.seqlen_q, w.heads_q, w.head_dim), dtype=qkv.dtype, device="cuda")
+    lse = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
+    step = prefill_step_fn(ex, qkv, out, lse)
+    ms_step, ms_kernel_avg, ms_kernel_med, ms_kernel_min = time_steps(step, args.steps, args.warmup)
+    fl = W.flops(w)
+    return w, fl, ms_step, ms_kernel_avg, ms_kernel_med, ms_kernel_min
+
+
+def run_decode(ex, W, args):
+    import torch
+    w = W.WORKLOADS["decode"]
+    q, kc, vc = W.kvcache(w.batch, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    q, kc, vc = q.cuda(), kc.cuda(), vc.cuda()
+    lens = torch.tensor(w.cache_seqlens, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads_q, 1), dtype=torch.float32, device="cuda")
+    ns, wb = ex.decode_plan(q[:, 0], kc, vc, lens)
+    ws = torch.empty(max(wb, 256), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def step():
+        ex.attn_with_kvcache(q, kc, vc, cache_seqlens=lens, out=out, lse=lse, workspace=ws)
+
+    def between():
+        flush.fill_(1)  # 512 MiB write evicts the KV cache from L2 and the MALL
+
+    steps = max(10, min(args.steps, 50))
+    ms_step, ms_avg, ms_med, ms_min = time_steps(step, steps, max(2, args.warmup // 4), between)
+    nbytes = W.algorithmic_bytes(w)
+    gbs = nbytes / (ms_avg * 1e-3) / 1e9
+    traffic = measured_traffic("decode_b8_h32x8_d128_cache16384", DECODE_SOURCES)
+    return {
+        "workload": "kvcache decode b8 s_q1 cache16384 h_q32 h_kv8 d128 bf16",
+        "num_splits": ns, "value": round(gbs, 2), "unit": "GB/s",
+        "ms_per_call_avg": round(ms_avg, 5), "ms_per_call_median": round(ms_med, 5),
+        "ms_per_call_min": round(ms_min, 5), "calls": steps,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": nbytes},
+        "cache_flush": "512 MiB write between calls (outside the event pairs)",
+    }
+
+
+def run_copy_calibration():
+    """A plain 256 MiB device copy, for scaling the HBM byte counters."""
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 256 << 20, "copies": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this attention forward is measured on "
+              f"one GPU (multi-GPU sharding is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(1)
+    import exact_attention_43_amd as ex
+    from exact_attention_43_amd import workloads as W
+    ex.lib()
+    torch.cuda.set_device(0)
+
+    if args.only == "copy":
+        run_copy_calibration()
+        return
+    if args.only == "decode":
+        print(json.dumps(run_decode(ex, W, args)))
+        return
+
+    w, fl, ms_step, k_avg, k_med, k_min = run_prefill(ex, W, args)
+    if args.only == "prefill":
+        print(json.dumps({"ms_step": ms_step, "kernel_ms_avg": k_avg, "kernel_ms_median": k_med}))
+        return
+    value = fl / (ms_step * 1e-3) / 1e12
+    achieved = fl / (k_avg * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal prefill, packed qkv (2, 1024, 3, 16, 128) bf16, causal, "
+                               "scale 1/sqrt(128)",
+                   "batch": w.batch, "seqlen": w.seqlen_q, "heads": w.heads_q, "head_dim": w.head_dim,
+                   "flops_per_step": fl, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill_causal_b2_s1024_h16_d128", PREFILL_SOURCES),
+                     "kernel_ms_avg": round(k_avg, 6), "kernel_ms_median": round(k_med, 6),
+                     "kernel_ms_min": round(k_min, 6)},
+    }
+    if not args.no_decode:
+        rec["decode"] = run_decode(ex, W, args)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, fl)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

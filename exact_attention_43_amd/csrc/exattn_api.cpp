@@ -1,0 +1,215 @@
+// C ABI entry points of libexattn: check, plan, launch.  No allocation, no
+// synchronisation, no host read of device memory.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <set>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "exattn.h"
+#include "kernels.h"
+#include "validate.h"
+
+namespace exattn {
+namespace {
+
+std::mutex g_mu;
+std::vector<int> g_cus;  // per-device compute-unit count, 0 = not queried yet
+
+exattn_status device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_mu);
+  if ((int)g_cus.size() <= dev) g_cus.resize(dev + 1, 0);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+      return fail(EXATTN_E_HIP, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e));
+    g_cus[dev] = n > 0 ? n : 1;
+  }
+  *out = g_cus[dev];
+  return EXATTN_OK;
+}
+
+int debug_level() {
+  const char* s = getenv("EXATTN_DEBUG");
+  return s ? atoi(s) : 0;
+}
+
+// EXATTN_DEBUG=1: print the plan once per distinct launch shape.
+void debug_once(const std::string& key, const std::string& text) {
+  if (debug_level() < 1) return;
+  static std::set<std::string> seen;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (seen.insert(key).second) fprintf(stderr, "[exattn] %s\n", text.c_str());
+}
+
+}  // namespace
+}  // namespace exattn
+
+using namespace exattn;
+
+extern "C" {
+
+exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
+  try {
+    clear_error();
+    FwdPlan pl;
+    exattn_status st = plan_fwd(a, prefill_rows_per_tile(), &pl);
+    if (st != EXATTN_OK || pl.empty) return st;
+    FwdParams p{};
+    p.q = static_cast<const uint16_t*>(a->q);
+    p.k = static_cast<const uint16_t*>(a->k);
+    p.v = static_cast<const uint16_t*>(a->v);
+    p.o = static_cast<uint16_t*>(a->o);
+    p.lse = a->lse;
+    p.q_sb = a->q_stride[0], p.q_ss = a->q_stride[1], p.q_sh = a->q_stride[2];
+    p.k_sb = a->k_stride[0], p.k_ss = a->k_stride[1], p.k_sh = a->k_stride[2];
+    p.v_sb = a->v_stride[0], p.v_ss = a->v_stride[1], p.v_sh = a->v_stride[2];
+    p.o_sb = a->o_stride[0], p.o_ss = a->o_stride[1], p.o_sh = a->o_stride[2];
+    p.lse_sb = a->lse_stride[0], p.lse_sh = a->lse_stride[1];
+    p.cu_q = pl.varlen ? a->cu_seqlens_q : nullptr;
+    p.cu_k = pl.varlen ? a->cu_seqlens_k : nullptr;
+    p.batch = a->batch;
+    p.s_q = pl.s_q;
+    p.s_k = pl.s_k;
+    p.h_q = a->heads_q;
+    p.h_kv = a->heads_kv;
+    p.group = pl.group;
+    p.n_qt = pl.n_qt;
+    p.xcd_group = pl.xcd_group;
+    p.scale_log2 = pl.scale_log2;
+    p.cap_in = pl.cap_in;
+    p.cap_out_log2 = pl.cap_out_log2;
+    p.wl = pl.wl;
+    p.wr = pl.wr;
+    char buf[256];
+    snprintf(buf, sizeof buf,
+             "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d x256",
+             pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, (int)pl.varlen, a->batch,
+             pl.s_q, pl.s_k, a->heads_q, a->heads_kv, pl.wl, pl.wr, pl.grid);
+    debug_once(buf, buf);
+    hipError_t e = launch_prefill(p, pl.bf16, pl.head_dim, pl.softcap, pl.grid,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
+    return EXATTN_OK;
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
+exattn_status exattn_decode_plan(const exattn_decode_args* a, int32_t* num_splits_out,
+                                 size_t* workspace_bytes_out) {
+  try {
+    clear_error();
+    DecodePlan pl;
+    exattn_status st = plan_decode(a, 1, &pl);  // argument checks need no device
+    if (st != EXATTN_OK) return st;
+    int cus = 1;
+    if (a->num_splits == 0) {
+      st = device_cus(&cus);
+      if (st != EXATTN_OK) return st;
+      st = plan_decode(a, cus, &pl);
+      if (st != EXATTN_OK) return st;
+    }
+    if (num_splits_out) *num_splits_out = pl.n_split;
+    if (workspace_bytes_out) *workspace_bytes_out = pl.ws_bytes;
+    return EXATTN_OK;
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
+exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  try {
+    clear_error();
+    DecodePlan pl;
+    exattn_status st = plan_decode(a, 1, &pl);
+    if (st != EXATTN_OK) return st;
+    if (a->num_splits == 0) {
+      int cus = 1;
+      st = device_cus(&cus);
+      if (st != EXATTN_OK) return st;
+      st = plan_decode(a, cus, &pl);
+      if (st != EXATTN_OK) return st;
+    }
+    if (pl.empty) return EXATTN_OK;
+    if (pl.n_split > 1) {
+      if (workspace == nullptr || workspace_bytes < pl.ws_bytes)
+        return fail(EXATTN_E_WORKSPACE, "workspace of " + std::to_string(pl.ws_bytes) +
+                                            " bytes required, got " +
+                                            std::to_string(workspace ? workspace_bytes : 0));
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(EXATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    DecParams p{};
+    p.q = static_cast<const uint16_t*>(a->q);
+    p.k = static_cast<const uint16_t*>(a->k_cache);
+    p.v = static_cast<const uint16_t*>(a->v_cache);
+    p.o = static_cast<uint16_t*>(a->o);
+    p.lse = a->lse;
+    p.q_sb = a->q_stride[0], p.q_sh = a->q_stride[1];
+    p.o_sb = a->o_stride[0], p.o_sh = a->o_stride[1];
+    p.k_sb = a->k_stride[0], p.k_ss = a->k_stride[1], p.k_sh = a->k_stride[2];
+    p.v_sb = a->v_stride[0], p.v_ss = a->v_stride[1], p.v_sh = a->v_stride[2];
+    p.cache_seqlens = a->cache_seqlens;
+    p.ws_o = pl.n_split > 1 ? static_cast<float*>(workspace) : nullptr;
+    p.ws_lse = pl.n_split > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_lse_offset)
+                   : nullptr;
+    p.batch = a->batch;
+    p.h_q = a->heads_q;
+    p.h_kv = a->heads_kv;
+    p.group = pl.group;
+    p.s_cache = a->seqlen_cache;
+    p.n_split = pl.n_split;
+    p.n_hg = pl.n_hg;
+    p.scale_log2 = pl.scale_log2;
+    p.cap_in = pl.cap_in;
+    p.cap_out_log2 = pl.cap_out_log2;
+    p.wl = pl.wl;
+    char buf[256];
+    snprintf(buf, sizeof buf, "decode %s d=%d softcap=%d b=%d hq=%d hkv=%d cache=%d splits=%d wl=%d",
+             pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, a->batch, a->heads_q,
+             a->heads_kv, a->seqlen_cache, pl.n_split, pl.wl);
+    debug_once(buf, buf);
+    hipError_t e = launch_decode(p, pl.bf16, pl.head_dim, pl.softcap, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+    return EXATTN_OK;
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
+int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                  int32_t seqlen_k, int32_t head_dim, int32_t num_cus) {
+  return auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus);
+}
+
+size_t exattn_args_size(int32_t which) {
+  return which == 0 ? sizeof(exattn_fwd_args) : which == 1 ? sizeof(exattn_decode_args) : 0;
+}
+
+const char* exattn_status_string(int32_t status) {
+  switch (status) {
+    case EXATTN_OK: return "EXATTN_OK";
+    case EXATTN_E_INVALID: return "EXATTN_E_INVALID";
+    case EXATTN_E_UNSUPPORTED: return "EXATTN_E_UNSUPPORTED";
+    case EXATTN_E_WORKSPACE: return "EXATTN_E_WORKSPACE";
+    case EXATTN_E_HIP: return "EXATTN_E_HIP";
+    default: return "EXATTN_E_UNKNOWN";
+  }
+}
+
+const char* exattn_last_error(void) { return last_error(); }
+
+int32_t exattn_abi_version(void) { return EXATTN_ABI_VERSION; }
+
+}  // extern "C"

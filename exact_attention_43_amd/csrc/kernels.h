@@ -1,0 +1,59 @@
+// Kernel parameter blocks and launcher entry points (internal to libexattn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exattn {
+
+// Prefill forward: one work group per (query tile of 128 rows, query head,
+// batch entry or sequence).  All strides are in elements.
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh;
+  const int32_t* cu_q;  // varlen prefix sums, or nullptr
+  const int32_t* cu_k;
+  int32_t batch, s_q, s_k;  // s_q / s_k: lengths (fixed) or maxima (varlen)
+  int32_t h_q, h_kv, group;
+  int32_t n_qt;        // query tiles per (batch, head)
+  int32_t xcd_group;   // 1: co-locate the query heads of one KV head on one XCD
+  float scale_log2;    // softmax_scale * log2(e)
+  float cap_in;        // softmax_scale / softcap
+  float cap_out_log2;  // softcap * log2(e)
+  int32_t wl, wr;      // window; wr = 0 for causal; < 0 unbounded
+};
+
+// Split-KV decode: one work group per (split, KV head x query-head group, batch).
+struct DecParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_sb, q_sh, o_sb, o_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  const int32_t* cache_seqlens;  // or nullptr
+  float* ws_o;                   // [split][batch][h_q][D] fp32 partial outputs
+  float* ws_lse;                 // [split][batch][h_q] fp32 partial LSE
+  int32_t batch, h_q, h_kv, group, s_cache;
+  int32_t n_split, n_hg;  // splits; query-head groups of 16 per KV head
+  float scale_log2, cap_in, cap_out_log2;
+  int32_t wl;
+};
+
+int prefill_rows_per_tile();
+hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,
+                          hipStream_t stream);
+hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softcap,
+                         hipStream_t stream);
+
+}  // namespace exattn

@@ -1,0 +1,195 @@
+// Host-side argument checks and launch planning (no HIP dependency).
+#include "validate.h"
+
+#include <math.h>
+
+#include <string>
+
+namespace exattn {
+namespace {
+
+thread_local std::string g_error;
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool stride_ok(int64_t s) { return s >= 0 && s % 8 == 0; }
+
+std::string str(int64_t v) { return std::to_string(v); }
+
+exattn_status check_common(int32_t dtype, int32_t head_dim, int32_t heads_q, int32_t heads_kv,
+                           int32_t batch) {
+  if (dtype != EXATTN_F16 && dtype != EXATTN_BF16)
+    return fail(EXATTN_E_UNSUPPORTED,
+                "dtype " + str(dtype) + " is not supported: inputs must be fp16 or bf16");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(EXATTN_E_UNSUPPORTED,
+                "head_dim " + str(head_dim) + " is not supported (64, 128 or 256)");
+  if (batch < 0) return fail(EXATTN_E_INVALID, "batch is negative");
+  if (heads_q < 1 || heads_kv < 1) return fail(EXATTN_E_INVALID, "heads must be >= 1");
+  if (heads_q % heads_kv != 0)
+    return fail(EXATTN_E_INVALID, "heads_q (" + str(heads_q) + ") is not a multiple of heads_kv (" +
+                                      str(heads_kv) + ")");
+  return EXATTN_OK;
+}
+
+exattn_status resolve_scales(float softmax_scale, float softcap, int head_dim, float* scale_log2,
+                             float* cap_in, float* cap_out_log2, bool* use_cap) {
+  float scale = softmax_scale;
+  if (isnan(scale) || scale == 0.0f) scale = 1.0f / sqrtf((float)head_dim);
+  if (!isfinite(scale)) return fail(EXATTN_E_INVALID, "softmax_scale is not finite");
+  if (isnan(softcap) || isinf(softcap)) return fail(EXATTN_E_INVALID, "softcap is not finite");
+  *use_cap = softcap > 0.0f;
+  *scale_log2 = scale * kLog2eHost;
+  *cap_in = *use_cap ? scale / softcap : 0.0f;
+  *cap_out_log2 = *use_cap ? softcap * kLog2eHost : 0.0f;
+  return EXATTN_OK;
+}
+
+}  // namespace
+
+exattn_status fail(exattn_status st, const std::string& msg) {
+  g_error = msg;
+  return st;
+}
+
+void clear_error() { g_error.clear(); }
+
+const char* last_error() { return g_error.c_str(); }
+
+exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl) {
+  if (a == nullptr || pl == nullptr) return fail(EXATTN_E_INVALID, "args is NULL");
+  *pl = FwdPlan{};
+  exattn_status st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->batch);
+  if (st != EXATTN_OK) return st;
+  const bool varlen = a->cu_seqlens_q != nullptr;
+  if (varlen != (a->cu_seqlens_k != nullptr))
+    return fail(EXATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+  int s_q, s_k;
+  if (varlen) {
+    if (a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
+      return fail(EXATTN_E_INVALID, "max_seqlen_q / max_seqlen_k is negative");
+    s_q = a->max_seqlen_q;
+    s_k = a->max_seqlen_k;
+  } else {
+    if (a->seqlen_q < 0 || a->seqlen_k < 0)
+      return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k is negative");
+    s_q = a->seqlen_q;
+    s_k = a->seqlen_k;
+  }
+  st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &pl->scale_log2, &pl->cap_in,
+                      &pl->cap_out_log2, &pl->softcap);
+  if (st != EXATTN_OK) return st;
+
+  pl->bf16 = a->dtype == EXATTN_BF16;
+  pl->head_dim = a->head_dim;
+  pl->varlen = varlen;
+  pl->s_q = s_q;
+  pl->s_k = s_k;
+  pl->group = a->heads_q / a->heads_kv;
+  pl->wl = a->window_left < 0 ? -1 : a->window_left;
+  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  pl->empty = a->batch == 0 || s_q == 0;
+  if (pl->empty) return EXATTN_OK;
+
+  if (a->q == nullptr || a->o == nullptr) return fail(EXATTN_E_INVALID, "q or o is NULL");
+  if (s_k > 0 && (a->k == nullptr || a->v == nullptr))
+    return fail(EXATTN_E_INVALID, "k or v is NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(EXATTN_E_INVALID, "q, k, v and o must be 16-byte aligned");
+  const int64_t* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t) {
+    for (int i = varlen ? 1 : 0; i < 3; ++i)
+      if (!stride_ok(strides[t][i]))
+        return fail(EXATTN_E_INVALID, std::string(names[t]) + "_stride[" + str(i) + "] = " +
+                                          str(strides[t][i]) +
+                                          " must be a non-negative multiple of 8 elements");
+  }
+  if (a->lse != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0)
+      return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
+    if (a->lse_stride[1] < 0 || (!varlen && a->lse_stride[0] < 0))
+      return fail(EXATTN_E_INVALID, "lse strides must be non-negative");
+  }
+  if (varlen && a->batch > 0 && (a->cu_seqlens_q == nullptr || a->cu_seqlens_k == nullptr))
+    return fail(EXATTN_E_INVALID, "cu_seqlens is NULL");
+
+  pl->n_qt = (s_q + rows_per_tile - 1) / rows_per_tile;
+  const int64_t units = (int64_t)a->batch * a->heads_q;
+  const int64_t grid = units * pl->n_qt;
+  if (grid > 0x7fffffffLL) return fail(EXATTN_E_INVALID, "problem too large for one launch");
+  pl->grid = (int)grid;
+  pl->xcd_group = (pl->group > 1 && ((int64_t)a->batch * a->heads_kv) % 8 == 0) ? 1 : 0;
+  return EXATTN_OK;
+}
+
+int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,
+                    int32_t head_dim, int32_t num_cus) {
+  (void)head_dim;
+  if (batch <= 0 || seqlen_k <= 0 || heads_kv <= 0 || heads_q <= 0 || num_cus <= 0) return 1;
+  const int64_t group = heads_q / heads_kv;
+  const int64_t units = (int64_t)batch * heads_kv * ((group + 15) / 16);
+  const int64_t target_wgs = 2LL * num_cus;  // about two work groups per compute unit
+  if (units >= target_wgs) return 1;
+  int64_t splits = (target_wgs + units - 1) / units;
+  const int64_t by_len = seqlen_k / 256 > 1 ? seqlen_k / 256 : 1;  // >= 256 keys per split
+  if (splits > by_len) splits = by_len;
+  if (splits > 256) splits = 256;
+  return (int32_t)(splits < 1 ? 1 : splits);
+}
+
+exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* pl) {
+  if (a == nullptr || pl == nullptr) return fail(EXATTN_E_INVALID, "args is NULL");
+  *pl = DecodePlan{};
+  exattn_status st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->batch);
+  if (st != EXATTN_OK) return st;
+  if (a->seqlen_cache < 0) return fail(EXATTN_E_INVALID, "seqlen_cache is negative");
+  if (a->num_splits < 0) return fail(EXATTN_E_INVALID, "num_splits is negative");
+  st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &pl->scale_log2, &pl->cap_in,
+                      &pl->cap_out_log2, &pl->softcap);
+  if (st != EXATTN_OK) return st;
+  pl->bf16 = a->dtype == EXATTN_BF16;
+  pl->head_dim = a->head_dim;
+  pl->group = a->heads_q / a->heads_kv;
+  pl->n_hg = (pl->group + 15) / 16;
+  pl->wl = a->window_left < 0 ? -1 : a->window_left;
+  int64_t ns = a->num_splits == 0
+                   ? auto_splits(a->batch, a->heads_q, a->heads_kv, a->seqlen_cache, a->head_dim,
+                                 num_cus)
+                   : a->num_splits;
+  const int64_t chunks = (a->seqlen_cache + 31) / 32;
+  if (ns > chunks) ns = chunks;
+  if (ns > 256) ns = 256;
+  if (ns < 1) ns = 1;
+  pl->n_split = (int)ns;
+  pl->empty = a->batch == 0;
+  if (pl->n_split > 1) {
+    const size_t rows = (size_t)pl->n_split * (size_t)a->batch * (size_t)a->heads_q;
+    const size_t o_bytes = rows * (size_t)a->head_dim * 4;
+    pl->ws_lse_offset = (o_bytes + 255) & ~(size_t)255;
+    pl->ws_bytes = (pl->ws_lse_offset + rows * 4 + 255) & ~(size_t)255;
+  }
+  if (pl->empty) return EXATTN_OK;
+
+  if (a->q == nullptr || a->o == nullptr) return fail(EXATTN_E_INVALID, "q or o is NULL");
+  if (a->seqlen_cache > 0 && (a->k_cache == nullptr || a->v_cache == nullptr))
+    return fail(EXATTN_E_INVALID, "k_cache or v_cache is NULL");
+  if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->o))
+    return fail(EXATTN_E_INVALID, "q, k_cache, v_cache and o must be 16-byte aligned");
+  const int64_t s2[4] = {a->q_stride[0], a->q_stride[1], a->o_stride[0], a->o_stride[1]};
+  for (int i = 0; i < 4; ++i)
+    if (!stride_ok(s2[i]))
+      return fail(EXATTN_E_INVALID, "q/o strides must be non-negative multiples of 8 elements");
+  for (int i = 0; i < 3; ++i)
+    if (!stride_ok(a->k_stride[i]) || !stride_ok(a->v_stride[i]))
+      return fail(EXATTN_E_INVALID, "k/v strides must be non-negative multiples of 8 elements");
+  if (a->lse != nullptr && (reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0)
+    return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
+  if ((int64_t)a->heads_kv * pl->n_hg > 65535 || a->batch > 65535)
+    return fail(EXATTN_E_INVALID, "too many heads or batch entries for one launch");
+  return EXATTN_OK;
+}
+
+}  // namespace exattn

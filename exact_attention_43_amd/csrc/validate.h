@@ -1,0 +1,60 @@
+// Host-side argument checks and launch planning for the exattn C ABI.
+//
+// Pure C++ (no HIP): everything here runs before any launch and can be built
+// and tested on a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "exattn.h"
+
+namespace exattn {
+
+// Set the calling thread's error text and return `st`.
+exattn_status fail(exattn_status st, const std::string& msg);
+void clear_error();
+const char* last_error();
+
+// Resolved prefill launch: the kernel variant and grid plus the folded scales.
+struct FwdPlan {
+  bool empty;  // nothing to launch
+  bool bf16;
+  int head_dim;
+  bool softcap;
+  bool varlen;
+  int s_q, s_k;  // lengths (fixed) or maxima (varlen)
+  int group;
+  int n_qt;      // query tiles per (batch, head)
+  int grid;      // work groups
+  int xcd_group;
+  float scale_log2, cap_in, cap_out_log2;
+  int wl, wr;
+};
+
+// Check `a` and fill `plan`.  rows_per_tile is the kernel's query tile height.
+exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* plan);
+
+struct DecodePlan {
+  bool empty;
+  bool bf16;
+  int head_dim;
+  bool softcap;
+  int group;
+  int n_hg;      // groups of 16 query heads per KV head
+  int n_split;
+  size_t ws_bytes;
+  size_t ws_lse_offset;  // byte offset of the LSE partials inside the workspace
+  float scale_log2, cap_in, cap_out_log2;
+  int wl;
+};
+
+// Check `a` and fill `plan` for a device with `num_cus` compute units.
+exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* plan);
+
+int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,
+                    int32_t head_dim, int32_t num_cus);
+
+}  // namespace exattn

@@ -1,0 +1,177 @@
+/*
+ * exattn: exact scaled-dot-product attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI of libexattn.so.  Plain C types only; device buffers are passed as raw
+ * device pointers and the stream as an opaque hipStream_t handle (void *, NULL
+ * means the default stream).
+ *
+ * What is computed (per batch entry / sequence b and query head h, with KV head
+ * h / (heads_q / heads_kv)):
+ *   S = scale * Q K^T, P = softmax(S), O = P V
+ * ("FlashAttention完整说明", section 一, equations (1)-(3)), evaluated tile by
+ * tile with an online softmax so that S and P never reach device memory (same
+ * page, section 二.1).  The forward keeps only O and the per-row softmax
+ * statistics, returned as the natural-log LSE (same page, section 二.2).
+ *
+ * Masking semantics (Inference Cookbook FAQ):
+ *   - causal: aligned to the bottom-right corner, off = seqlen_k - seqlen_q,
+ *     key j visible to row i iff j <= i + off (Q6);
+ *   - window (left, right): row i sees [i + off - left, i + off + right],
+ *     inclusive; a negative bound is unbounded; causal forces right = 0 (Q21);
+ *   - softcap c > 0: score -> c * tanh(score / c) after scaling and before
+ *     masking (Q22); c <= 0 disables it;
+ *   - a row that sees no key gets O = 0 and LSE = -inf.
+ * The default scale is 1/sqrt(head_dim) (Q12).
+ *
+ * Ownership and threading: the caller allocates and owns every buffer.  The
+ * library keeps no pointer after a call returns, never allocates or frees
+ * device memory, never synchronises and never reads device memory on the host,
+ * so a call can be captured into a HIP graph with fixed addresses (Q19).  Its
+ * only global state is a per-device cache of the compute-unit count.  Calls on
+ * different streams may run concurrently; a call's kernels run in order on the
+ * stream it is given.
+ *
+ * Errors: arguments are checked on the host before anything is launched; on a
+ * failed check nothing is launched and the status says why, with detail text
+ * from exattn_last_error() (thread-local).  Launch failures return
+ * EXATTN_E_HIP.  Device-resident cu_seqlens / cache_seqlens cannot be checked
+ * without a host read, so their validity is a precondition (see below).
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXATTN_ABI_VERSION 1
+
+typedef enum {
+  EXATTN_OK = 0,
+  EXATTN_E_INVALID = 1,     /* bad argument: null pointer, negative size, head ratio, stride */
+  EXATTN_E_UNSUPPORTED = 2, /* valid but not provided: dtype, head_dim */
+  EXATTN_E_WORKSPACE = 3,   /* decode workspace missing or too small */
+  EXATTN_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} exattn_status;
+
+/* Storage type of Q, K, V and O.  fp16/bf16 only ("FlashAttention完整说明",
+ * section 八: half-precision types only).  Accumulation is fp32. */
+typedef enum { EXATTN_F16 = 0, EXATTN_BF16 = 1 } exattn_dtype;
+
+/*
+ * Prefill / general forward: flash_attn_func and its packed and varlen forms
+ * (FAQ Q5 layout (batch, seqlen, heads, head_dim); Q7 kv-packed and
+ * cross-attention; Q8 varlen; "FlashAttention完整说明" section 六.1 qkv-packed).
+ *
+ * Tensors are addressed by element strides over (batch, token, head); the
+ * head_dim stride must be 1.  Packed layouts are passed as strided views with
+ * no copy, e.g. qkv (b, s, 3, h, d) gives q, k, v with token stride 3*h*d and
+ * base pointers offset by 0, h*d and 2*h*d elements.
+ *
+ * Fixed length (cu_seqlens_q == NULL): q (batch, seqlen_q, heads_q, head_dim),
+ *   k and v (batch, seqlen_k, heads_kv, head_dim), o like q.
+ * Variable length (cu_seqlens_q != NULL, cu_seqlens_k != NULL): sequences are
+ *   packed end to end, q (total_q, heads_q, head_dim), k/v (total_k, heads_kv,
+ *   head_dim); the batch stride is ignored; sequence b spans tokens
+ *   [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q and [cu_seqlens_k[b],
+ *   cu_seqlens_k[b+1]) of k/v.  Precondition: both arrays are int32 device
+ *   arrays of batch + 1 non-decreasing entries starting at 0, and no sequence
+ *   is longer than max_seqlen_q / max_seqlen_k (host values that size the grid).
+ *
+ * lse: fp32 device buffer, element (b, h, i) at
+ *   lse[b * lse_stride[0] + h * lse_stride[1] + i]; for fixed length the usual
+ *   layout is (batch, heads_q, seqlen_q); for varlen i is the packed token
+ *   index and the batch stride is ignored (layout (heads_q, total_q)).
+ *   lse may be NULL when the caller does not want it.
+ */
+typedef struct {
+  int32_t dtype; /* exattn_dtype */
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3]; /* elements: batch, token, head */
+  int64_t lse_stride[2];                                       /* elements: batch, head */
+  const int32_t *cu_seqlens_q, *cu_seqlens_k;                  /* device int32[batch+1] or NULL */
+  int32_t max_seqlen_q, max_seqlen_k;                          /* varlen only */
+  float softmax_scale; /* 0 or NaN: 1/sqrt(head_dim) */
+  float softcap;       /* <= 0: off */
+  int32_t causal;      /* nonzero: bottom-right causal, forces window_right = 0 */
+  int32_t window_left, window_right; /* < 0: unbounded */
+} exattn_fwd_args;
+
+/* Run the forward.  head_dim must be 64, 128 or 256; heads_q % heads_kv == 0.
+ * Sizes of 0 (batch, seqlen_q) launch nothing and return EXATTN_OK; seqlen_k
+ * of 0 writes O = 0 and LSE = -inf. */
+exattn_status exattn_fwd(const exattn_fwd_args *args, void *stream);
+
+/*
+ * KV-cache decode: flash_attn_with_kvcache with seqlen_q = 1 (FAQ Q17), split
+ * over the key axis into num_splits parts whose partial results are merged by
+ * their log-sum-exp (FAQ Q14; the merge is the online-softmax merge of
+ * "FlashAttention完整说明" section 二.1).
+ *
+ * q (batch, 1, heads_q, head_dim) addressed by q_stride (batch, head); o the
+ * same by o_stride; k_cache and v_cache (batch, seqlen_cache, heads_kv,
+ * head_dim) by k_stride / v_stride (batch, token, head); lse fp32 (batch,
+ * heads_q) contiguous, or NULL.
+ * cache_seqlens: device int32[batch], the number of valid cache rows per batch
+ * entry, or NULL for seqlen_cache.  The caller maintains it (FAQ Q17: the call
+ * never advances it).  Precondition: 0 <= cache_seqlens[b] <= seqlen_cache.
+ * The single query sits at position cache_seqlens[b] - 1 (bottom-right), so
+ * causal changes nothing and only window_left narrows the keys.
+ * num_splits: 0 = automatic (compute-unit count, KV size per split, length);
+ * otherwise the number of key ranges, clamped to [1, 256].
+ */
+typedef struct {
+  int32_t dtype; /* exattn_dtype */
+  int32_t batch, heads_q, heads_kv, head_dim, seqlen_cache;
+  const void *q, *k_cache, *v_cache;
+  void *o;
+  float *lse;
+  int64_t q_stride[2], o_stride[2];  /* elements: batch, head */
+  int64_t k_stride[3], v_stride[3];  /* elements: batch, token, head */
+  const int32_t *cache_seqlens;      /* device int32[batch] or NULL */
+  float softmax_scale;               /* 0 or NaN: 1/sqrt(head_dim) */
+  float softcap;                     /* <= 0: off */
+  int32_t causal;
+  int32_t window_left, window_right; /* < 0: unbounded */
+  int32_t num_splits;                /* 0: automatic */
+} exattn_decode_args;
+
+/* Host-only: resolve num_splits and the workspace size (bytes) that
+ * exattn_decode needs for these arguments on the current device.  Either
+ * output pointer may be NULL. */
+exattn_status exattn_decode_plan(const exattn_decode_args *args, int32_t *num_splits_out,
+                                 size_t *workspace_bytes_out);
+
+/* Run the decode.  workspace: device buffer of at least the planned size,
+ * 256-byte aligned, owned by the caller, used as scratch for the partial
+ * results (fp32 O and LSE per split); its contents on entry do not matter.
+ * With one split the workspace may be NULL.  Calls that share a workspace
+ * must be ordered on one stream. */
+exattn_status exattn_decode(const exattn_decode_args *args, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* The automatic split count, as a pure function (no device query): the key
+ * axis is split so that batch * heads_kv * splits work groups fill about twice
+ * num_cus, while each split keeps at least 256 keys (FAQ Q14's rules). */
+int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                  int32_t seqlen_k, int32_t head_dim, int32_t num_cus);
+
+/* sizeof(exattn_fwd_args) for which = 0, sizeof(exattn_decode_args) for which = 1,
+ * 0 otherwise: lets a binding check its mirror of the structs. */
+size_t exattn_args_size(int32_t which);
+
+const char *exattn_status_string(int32_t status);
+const char *exattn_last_error(void);
+int32_t exattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */

@@ -1,0 +1,172 @@
+"""The C ABI on the CPU: the library loads, exports what include/exattn.h
+declares, its struct layout matches the binding, and every host-side argument
+check fails with the documented status before anything is launched.
+
+No call here reaches a GPU: each one is rejected (or is empty) on the host.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import exact_attention_43_amd as ex
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ex.library_path()):
+        pytest.fail("libexattn.so is not built (run __graft_entry__.build())")
+    return ex.lib()
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(exattn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in exattn.h but not exported"
+
+
+def test_struct_layout_and_version(L):
+    assert L.exattn_args_size(0) == C.sizeof(ex.FwdArgs)
+    assert L.exattn_args_size(1) == C.sizeof(ex.DecodeArgs)
+    assert L.exattn_args_size(7) == 0
+    assert L.exattn_abi_version() == 1
+    assert L.exattn_status_string(0) == b"EXATTN_OK"
+    assert L.exattn_status_string(3) == b"EXATTN_E_WORKSPACE"
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (rejected on the host)
+
+
+def _fwd(**kw):
+    a = ex.FwdArgs()
+    a.dtype, a.batch, a.seqlen_q, a.seqlen_k = 1, 2, 64, 64
+    a.heads_q, a.heads_kv, a.head_dim = 4, 4, 128
+    a.q = a.k = a.v = a.o = FAKE
+    for n in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(a, n)[:] = [64 * 4 * 128, 4 * 128, 128]
+    a.lse_stride[:] = [4 * 64, 64]
+    a.window_left = a.window_right = -1
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(a, key)[:] = val
+        else:
+            setattr(a, key, val)
+    return a
+
+
+BAD_FWD = [
+    ("dtype", dict(dtype=2), ex.EXATTN_E_UNSUPPORTED),
+    ("head_dim 96", dict(head_dim=96), ex.EXATTN_E_UNSUPPORTED),
+    ("head_dim 60", dict(head_dim=60), ex.EXATTN_E_UNSUPPORTED),
+    ("heads ratio", dict(heads_q=6, heads_kv=4), ex.EXATTN_E_INVALID),
+    ("heads zero", dict(heads_kv=0), ex.EXATTN_E_INVALID),
+    ("negative batch", dict(batch=-1), ex.EXATTN_E_INVALID),
+    ("negative seqlen", dict(seqlen_k=-3), ex.EXATTN_E_INVALID),
+    ("null q", dict(q=None), ex.EXATTN_E_INVALID),
+    ("null v", dict(v=None), ex.EXATTN_E_INVALID),
+    ("misaligned k", dict(k=FAKE + 8), ex.EXATTN_E_INVALID),
+    ("odd stride", dict(q_stride=[64 * 4 * 128, 4 * 128 + 4, 128]), ex.EXATTN_E_INVALID),
+    ("negative stride", dict(o_stride=[-8, 512, 128]), ex.EXATTN_E_INVALID),
+    ("half varlen", dict(cu_seqlens_q=FAKE), ex.EXATTN_E_INVALID),
+    ("inf scale", dict(softmax_scale=float("inf")), ex.EXATTN_E_INVALID),
+    ("nan softcap", dict(softcap=float("nan")), ex.EXATTN_E_INVALID),
+    ("misaligned lse", dict(lse=FAKE + 2), ex.EXATTN_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_FWD, ids=[c[0] for c in BAD_FWD])
+def test_fwd_rejects(L, name, kw, status):
+    st = L.exattn_fwd(C.byref(_fwd(**kw)), None)
+    assert st == status, (name, st, L.exattn_last_error())
+    assert L.exattn_last_error()  # a reason is given
+
+
+def test_fwd_empty_is_ok_without_launch(L):
+    assert L.exattn_fwd(C.byref(_fwd(batch=0)), None) == ex.EXATTN_OK
+    assert L.exattn_fwd(C.byref(_fwd(seqlen_q=0)), None) == ex.EXATTN_OK
+    assert L.exattn_fwd(C.byref(_fwd(batch=0, q=None, o=None)), None) == ex.EXATTN_OK
+
+
+def test_fwd_null_args(L):
+    assert L.exattn_fwd(None, None) == ex.EXATTN_E_INVALID
+
+
+def _dec(**kw):
+    a = ex.DecodeArgs()
+    a.dtype, a.batch, a.heads_q, a.heads_kv, a.head_dim, a.seqlen_cache = 1, 8, 32, 8, 128, 16384
+    a.q = a.k_cache = a.v_cache = a.o = FAKE
+    a.q_stride[:] = [32 * 128, 128]
+    a.o_stride[:] = [32 * 128, 128]
+    a.k_stride[:] = [16384 * 8 * 128, 8 * 128, 128]
+    a.v_stride[:] = [16384 * 8 * 128, 8 * 128, 128]
+    a.window_left = a.window_right = -1
+    a.num_splits = 4
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(a, key)[:] = val
+        else:
+            setattr(a, key, val)
+    return a
+
+
+BAD_DEC = [
+    ("dtype", dict(dtype=5), ex.EXATTN_E_UNSUPPORTED),
+    ("head_dim", dict(head_dim=80), ex.EXATTN_E_UNSUPPORTED),
+    ("heads ratio", dict(heads_q=12, heads_kv=8), ex.EXATTN_E_INVALID),
+    ("negative splits", dict(num_splits=-1), ex.EXATTN_E_INVALID),
+    ("negative cache", dict(seqlen_cache=-1), ex.EXATTN_E_INVALID),
+    ("null cache", dict(k_cache=None), ex.EXATTN_E_INVALID),
+    ("odd stride", dict(k_stride=[16384 * 8 * 128, 8 * 128 + 2, 128]), ex.EXATTN_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_DEC, ids=[c[0] for c in BAD_DEC])
+def test_decode_rejects(L, name, kw, status):
+    a = _dec(**kw)
+    assert L.exattn_decode_plan(C.byref(a), None, None) == status, L.exattn_last_error()
+    assert L.exattn_decode(C.byref(a), None, 0, None) == status, L.exattn_last_error()
+
+
+def test_decode_workspace_checks(L):
+    a = _dec(num_splits=4)
+    ns, wb = C.c_int32(0), C.c_size_t(0)
+    assert L.exattn_decode_plan(C.byref(a), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
+    assert ns.value == 4
+    rows = 4 * 8 * 32
+    o_bytes = rows * 128 * 4
+    assert wb.value == ((o_bytes + 255) // 256 * 256 + rows * 4 + 255) // 256 * 256
+    assert L.exattn_decode(C.byref(a), None, 0, None) == ex.EXATTN_E_WORKSPACE
+    assert L.exattn_decode(C.byref(a), C.c_void_p(FAKE), wb.value - 1, None) == ex.EXATTN_E_WORKSPACE
+    assert L.exattn_decode(C.byref(a), C.c_void_p(FAKE + 16), wb.value, None) == ex.EXATTN_E_WORKSPACE
+    # one split needs no workspace
+    a1 = _dec(num_splits=1)
+    assert L.exattn_decode_plan(C.byref(a1), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
+    assert ns.value == 1 and wb.value == 0
+    # more splits than 32-key chunks are clamped
+    a2 = _dec(num_splits=200, seqlen_cache=100)
+    assert L.exattn_decode_plan(C.byref(a2), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
+    assert ns.value == 4
+    assert L.exattn_decode(C.byref(_dec(batch=0)), None, 0, None) == ex.EXATTN_OK
+
+
+def test_auto_splits_rules(L):
+    # FAQ Q14: enough (batch x heads) work -> 1 split; few units -> split toward the CU count;
+    # a split never gets fewer than 256 keys.
+    assert ex.auto_splits(8, 32, 8, 16384, 128, 256) == 8       # 64 units -> 512 work groups
+    assert ex.auto_splits(64, 32, 8, 16384, 128, 256) == 1      # 512 units already
+    assert ex.auto_splits(1, 32, 8, 16384, 128, 256) == 64      # 8 units -> 64 splits
+    assert ex.auto_splits(1, 32, 8, 1024, 128, 256) == 4        # capped by length / 256
+    assert ex.auto_splits(1, 32, 8, 100, 128, 256) == 1
+    assert ex.auto_splits(1, 8, 8, 0, 128, 256) == 1
+    assert ex.auto_splits(2, 64, 1, 1 << 20, 128, 256) == 64    # 64 query heads = 4 groups of 16

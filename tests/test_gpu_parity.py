@@ -1,0 +1,329 @@
+"""GPU parity: the HIP kernels through the C ABI against the CPU fp64 oracle.
+
+Inputs are seeded N(0,1) draws (exact_attention_43_amd.workloads) rounded to
+fp16/bf16; the oracle sees exactly the rounded values.  Every configuration the
+benchmark names is covered, at full size where the oracle finishes in seconds
+and on sampled rows plus size-independent properties otherwise, together with
+the extra shapes that make each mask rule bite, ragged tails, empty rows and
+sequences, split counts, packed layouts and determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_43_amd as ex
+import oracle
+from exact_attention_43_amd import workloads as W
+from parity import assert_lse_close, assert_o_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    ex.lib()  # the HIP library must load on a GPU machine: no fallback
+
+
+def _dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def _poison_out(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+def _poison_lse(shape):
+    return torch.full(shape, 123.0, dtype=torch.float32, device=DEV)
+
+
+def run_dense(q, k, v, where, **kw):
+    """Run attn_func on poisoned outputs and compare everything with the oracle."""
+    dq, dk, dv = _dev(q, k, v)
+    b, s_q, h_q, d = q.shape
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((b, h_q, s_q))
+    ex.attn_func(dq, dk, dv, out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, **kw)
+    assert_o_close(out, o_ref, q.dtype, where)
+    assert_lse_close(lse, l_ref, where)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# the named workloads
+# --------------------------------------------------------------------------
+def test_tiny_fp16():
+    w = W.WORKLOADS["tiny"]
+    q, k, v = W.qkv(1, 64, 64, 4, 4, 64, seed=w.seed, dtype=torch.float16)
+    run_dense(q, k, v, "tiny")
+
+
+def test_causal_prefill_qkvpacked():
+    w = W.WORKLOADS["causal_prefill"]
+    qkv = W.packed_qkv(w.batch, w.seqlen_q, w.heads_q, w.head_dim, seed=w.seed)
+    out, lse = ex.attn_qkvpacked_func(qkv.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], causal=True)
+    assert_o_close(out, o_ref, torch.bfloat16, "causal_prefill")
+    assert_lse_close(lse, l_ref, "causal_prefill")
+
+
+@pytest.mark.parametrize("name", ["hdim64", "hdim128", "hdim256"])
+def test_head_dim_sweep(name):
+    w = W.WORKLOADS[name]
+    q, k, v = W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed,
+                    dtype=torch.float16)
+    out, _ = run_dense(q, k, v, name)
+    assert out.shape == q.shape
+
+
+def test_varlen_gqa_window_softcap():
+    w = W.WORKLOADS["varlen_gqa"]
+    q, k, v, cu_q, cu_k = W.varlen_qkv(w.seqlens, w.seqlens, w.heads_q, w.heads_kv, w.head_dim,
+                                       seed=w.seed)
+    dq, dk, dv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((w.heads_q, q.shape[0]))
+    ex.attn_varlen_func(dq, dk, dv, dcq, dck, max(w.seqlens), max(w.seqlens), causal=True,
+                        window_size=w.window, softcap=w.softcap, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal=True, window_size=w.window,
+                                           softcap=w.softcap)
+    assert_o_close(out, o_ref, q.dtype, "varlen")
+    assert_lse_close(lse, l_ref, "varlen")
+
+
+def test_cross_attention():
+    w = W.WORKLOADS["cross"]
+    q, k, v = W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    run_dense(q, k, v, "cross", causal=False)
+
+
+def test_long_prefill_sampled():
+    """16384-token causal prefill: sampled rows against the oracle, properties everywhere."""
+    w = W.WORKLOADS["long_prefill"]
+    q, k, v = W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    dq, dk, dv = _dev(q, k, v)
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((1, w.heads_q, w.seqlen_q))
+    ex.attn_func(dq, dk, dv, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and torch.isfinite(lse).all()
+    # convex combination: |O| never exceeds the largest |V| of its column
+    vmax = dv.abs().amax(dim=1, keepdim=True).float()
+    assert (out.float().abs() <= vmax * (1 + 1e-2) + 1e-6).all()
+    rows = np.array(sorted({0, 1, 63, 64, 127, 128, 129, 4095, 8191, 8192, 12345, 16255, 16256,
+                            16382, 16383}))
+    heads = [0, 7, 15]
+    o_ref, l_ref = oracle.attention(q, k, v, causal=True, rows=rows, heads=heads)
+    o_cpu, l_cpu = out.cpu(), lse.cpu()
+    for h in heads:
+        assert_o_close(o_cpu[:, rows, h], o_ref[:, rows, h], q.dtype, f"long h{h}")
+        assert_lse_close(l_cpu[:, h, rows], l_ref[:, h, rows], f"long h{h}")
+
+
+def test_decode_kvcache():
+    w = W.WORKLOADS["decode"]
+    q, kc, vc = W.kvcache(w.batch, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    lens = torch.tensor(w.cache_seqlens, dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens)
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((w.batch, w.heads_q, 1))
+    ns, _ = ex.decode_plan(dq[:, 0], dkc, dvc, dl)
+    assert ns > 1
+    ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens, causal=True)
+    assert_o_close(out, o_ref, q.dtype, "decode")
+    assert_lse_close(lse, l_ref, "decode")
+
+
+# --------------------------------------------------------------------------
+# masks, tails and degenerate cases
+# --------------------------------------------------------------------------
+MASK_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, dtype, causal, window, softcap, seed
+    (1, 1024, 1024, 4, 4, 128, torch.bfloat16, True, (256, 0), 0.0, 101),     # window bites
+    (2, 128, 64, 4, 2, 128, torch.bfloat16, True, (-1, -1), 0.0, 102),        # s_q > s_k: empty rows
+    (1, 512, 2048, 4, 1, 128, torch.bfloat16, True, (-1, -1), 0.0, 103),      # s_q < s_k
+    (1, 300, 300, 4, 4, 128, torch.float16, False, (-1, -1), 2.0, 104),       # saturating softcap
+    (2, 200, 333, 4, 2, 64, torch.float16, False, (17, 5), 0.0, 105),         # ragged both, 2-sided
+    (1, 77, 1000, 2, 1, 256, torch.bfloat16, True, (100, -1), 30.0, 106),
+    (3, 129, 129, 6, 2, 128, torch.float16, True, (-1, -1), 0.0, 107),
+    (1, 65, 1, 2, 2, 64, torch.bfloat16, False, (-1, -1), 0.0, 108),          # s_k = 1: O = V
+    (1, 40, 3000, 2, 2, 256, torch.float16, False, (-1, 0), 0.0, 109),        # right edge only
+    (2, 260, 260, 8, 8, 64, torch.bfloat16, True, (0, 0), 0.0, 110),          # window of one key
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"m{c[-1]}" for c in MASK_CASES])
+def test_masks_and_tails(case):
+    b, s_q, s_k, h_q, h_kv, d, dt, causal, window, cap, seed = case
+    q, k, v = W.qkv(b, s_q, s_k, h_q, h_kv, d, seed=seed, dtype=dt)
+    if cap == 2.0:
+        q, k = (q.float() * 4).to(dt), (k.float() * 4).to(dt)
+    run_dense(q, k, v, f"mask case {seed}", causal=causal, window_size=window, softcap=cap)
+
+
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (False, (9, 3)), (True, (33, -1))])
+def test_zero_q_counts(causal, window):
+    """Q = 0: every visible score is 0, so O is the mean of the visible V rows and LSE = ln(count)."""
+    s_q, s_k = 150, 230
+    _, k, v = W.qkv(2, s_q, s_k, 4, 2, 128, seed=120, dtype=torch.bfloat16)
+    q = torch.zeros((2, s_q, 4, 128), dtype=torch.bfloat16)
+    run_dense(q, k, v, "zero q", causal=causal, window_size=window, softcap=5.0)
+
+
+def test_large_shift_stability():
+    """Scores of order 1e3 (K + c): the online rescaling must stay finite and exact."""
+    q, k, v = W.qkv(1, 256, 256, 2, 2, 128, seed=121, dtype=torch.float32)
+    c = torch.randn(128, generator=torch.Generator().manual_seed(5)) * 40
+    q = q.to(torch.bfloat16)
+    k = (k + c).to(torch.bfloat16)
+    v = v.to(torch.bfloat16)
+    run_dense(q, k, v, "shift", causal=True)
+
+
+def test_empty_keys_and_batch():
+    q, k, v = W.qkv(2, 70, 0, 4, 4, 64, seed=122, dtype=torch.float16)
+    out, lse = ex.attn_func(*_dev(q, torch.zeros((2, 0, 4, 64), dtype=torch.float16),
+                                  torch.zeros((2, 0, 4, 64), dtype=torch.float16)))
+    torch.cuda.synchronize()
+    assert (out == 0).all() and torch.isneginf(lse).all()
+    q0 = torch.zeros((0, 16, 4, 64), dtype=torch.float16, device=DEV)
+    out0, lse0 = ex.attn_func(q0, q0, q0)
+    assert out0.shape == (0, 16, 4, 64) and lse0.shape == (0, 4, 16)
+
+
+def test_varlen_ragged_and_empty_sequences():
+    lens_q = [1, 0, 600, 129, 64]
+    lens_k = [5, 3, 600, 1, 300]
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, 8, 2, 128, seed=123)
+    dq, dk, dv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    for causal, window, cap in [(True, (-1, -1), 0.0), (False, (40, 7), 0.0), (True, (256, 0), 50.0)]:
+        out = _poison_out(q.shape, q.dtype)
+        lse = _poison_lse((8, q.shape[0]))
+        ex.attn_varlen_func(dq, dk, dv, dcq, dck, max(lens_q), max(lens_k), causal=causal,
+                            window_size=window, softcap=cap, out=out, lse=lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal=causal, window_size=window,
+                                               softcap=cap)
+        assert_o_close(out, o_ref, q.dtype, f"varlen {causal} {window}")
+        assert_lse_close(lse, l_ref, f"varlen {causal} {window}")
+
+
+def test_packed_layouts_equal_contiguous():
+    qkv = W.packed_qkv(2, 200, 4, 128, seed=124)
+    d = qkv.to(DEV)
+    o1, l1 = ex.attn_qkvpacked_func(d, causal=True)
+    o2, l2 = ex.attn_func(d[:, :, 0].contiguous(), d[:, :, 1].contiguous(), d[:, :, 2].contiguous(),
+                          causal=True)
+    q = d[:, :, 0]
+    kv = torch.stack([d[:, :, 1], d[:, :, 2]], dim=2)
+    o3, l3 = ex.attn_kvpacked_func(q, kv, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_bitwise_determinism():
+    q, k, v = _dev(*W.qkv(2, 700, 900, 8, 2, 128, seed=125))
+    a = ex.attn_func(q, k, v, causal=True)
+    b = ex.attn_func(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    q, k, v = _dev(*W.qkv(1, 100, 100, 2, 2, 64, seed=126, dtype=torch.float16))
+    a = ex.attn_func(q, k, v)
+    b = ex.attn_func(q, k, v, softmax_scale=1 / 8.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------
+# decode: ragged cache lengths, split counts, grouped heads, window, softcap
+# --------------------------------------------------------------------------
+DECODE_CASES = [
+    # b, s_cache, h_q, h_kv, d, dtype, lens, window, softcap, splits, seed
+    (6, 16384, 32, 8, 128, torch.bfloat16, [1, 17, 1000, 16384, 0, 4097], (-1, -1), 0.0, 0, 130),
+    (2, 3000, 32, 1, 128, torch.bfloat16, [3000, 1234], (-1, -1), 0.0, 0, 131),    # 32 heads per KV head
+    (3, 2048, 8, 8, 64, torch.float16, [2048, 100, 1500], (255, 0), 0.0, 3, 132),
+    (2, 1024, 16, 4, 256, torch.bfloat16, [1024, 999], (-1, -1), 50.0, 5, 133),
+    (1, 33, 4, 2, 128, torch.float16, [33], (-1, -1), 0.0, 1, 134),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"d{c[-1]}" for c in DECODE_CASES])
+def test_decode_cases(case):
+    b, s_cache, h_q, h_kv, d, dt, lens, window, cap, splits, seed = case
+    q, kc, vc = W.kvcache(b, s_cache, h_q, h_kv, d, seed=seed, dtype=dt)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens_t)
+    out = _poison_out(q.shape, dt)
+    lse = _poison_lse((b, h_q, 1))
+    ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, window_size=window, softcap=cap,
+                         num_splits=splits, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens, window_size=window, softcap=cap)
+    assert_o_close(out, o_ref, dt, f"decode {seed}")
+    assert_lse_close(lse, l_ref, f"decode {seed}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 16, 64, 0])
+def test_decode_split_sweep(splits):
+    q, kc, vc = W.kvcache(2, 4096, 16, 4, 128, seed=135)
+    lens = torch.tensor([4096, 2500], dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens)
+    out, lse = ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens)
+    assert_o_close(out, o_ref, torch.bfloat16, f"splits {splits}")
+    assert_lse_close(lse, l_ref, f"splits {splits}")
+
+
+def test_decode_matches_prefill_row():
+    """s_q = 1 through the prefill kernel and through the decode kernel agree with each other."""
+    q, kc, vc = W.kvcache(2, 777, 8, 2, 128, seed=136)
+    dq, dkc, dvc = _dev(q, kc, vc)
+    o1, l1 = ex.attn_with_kvcache(dq, dkc, dvc, causal=True)
+    o2, l2 = ex.attn_func(dq, dkc, dvc, causal=True)
+    torch.cuda.synchronize()
+    assert_o_close(o1.cpu(), o2.cpu().double().numpy(), torch.bfloat16, "decode vs prefill")
+    assert (l1 - l2).abs().max().item() < 1e-4
+
+
+def test_graph_capture_decode_replays():
+    """The decode call captured in a graph (fixed addresses, FAQ Q19) replays correctly."""
+    q, kc, vc = W.kvcache(2, 2048, 16, 4, 128, seed=137)
+    lens = torch.tensor([2048, 1000], dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens)
+    out = torch.empty_like(dq)
+    lse = torch.empty((2, 16, 1), dtype=torch.float32, device=DEV)
+    ns, wb = ex.decode_plan(dq[:, 0], dkc, dvc, dl)
+    ws = torch.empty(max(wb, 256), dtype=torch.uint8, device=DEV)
+    ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    eager_o, eager_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
