@@ -2,7 +2,9 @@
 
 Every HIP source is compiled with packed-fp32 instruction selection switched
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass of
-hipcc warns that it does not know that feature, which is harmless.
+hipcc warns that it does not know that feature, which is harmless.  MFMA
+accumulators are kept in architectural VGPRs (``-amdgpu-mfma-vgpr-form``), so
+the softmax and the rare O rescale touch them without AGPR copies.
 
     python -m exact_attention_43_amd.build          # build
     python -m exact_attention_43_amd.build --check  # also build the host-only checker
@@ -53,7 +55,8 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         jobs.append([hipcc, f"--offload-arch={ARCH}", *common, "-Xclang", "-target-feature",
-                     "-Xclang", "-packed-fp32-ops", *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+                     "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", *lang, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         jobs.append(["g++", *common, "-c", os.path.join(CSRC, src), "-o", obj])

@@ -85,19 +85,15 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 // Transpose helper: from four 16-byte rows (8 x 16-bit each) take column t of
 // every row and return those four 16-bit values packed (row 0 in the low half
-// of the first word).
+// of the first word).  One v_perm_b32 per output word.
 __device__ __forceinline__ u32x2_t column4(const u32x4_t& r0, const u32x4_t& r1,
                                            const u32x4_t& r2, const u32x4_t& r3, int t) {
   const int w = t >> 1;
-  const uint32_t a = r0[w], b = r1[w], c = r2[w], d = r3[w];
+  // v_perm_b32(s0, s1, sel): selector bytes 0-3 pick bytes of s1, 4-7 bytes of s0.
+  const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
   u32x2_t out;
-  if (t & 1) {
-    out[0] = (a >> 16) | (b & 0xffff0000u);
-    out[1] = (c >> 16) | (d & 0xffff0000u);
-  } else {
-    out[0] = (a & 0xffffu) | (b << 16);
-    out[1] = (c & 0xffffu) | (d << 16);
-  }
+  out[0] = __builtin_amdgcn_perm(r1[w], r0[w], sel);
+  out[1] = __builtin_amdgcn_perm(r3[w], r2[w], sel);
   return out;
 }
 

@@ -89,6 +89,7 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     p.cap_out_log2 = pl.cap_out_log2;
     p.wl = pl.wl;
     p.wr = pl.wr;
+    p.q_sign = pl.q_sign;
     char buf[256];
     snprintf(buf, sizeof buf,
              "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d x256",

@@ -29,6 +29,7 @@ struct FwdParams {
   float cap_in;        // softmax_scale / softcap
   float cap_out_log2;  // softcap * log2(e)
   int32_t wl, wr;      // window; wr = 0 for causal; < 0 unbounded
+  uint32_t q_sign;     // 0x80008000 when the scale is negative: Q is negated, scale_log2 = |.|
 };
 
 // Split-KV decode: one work group per (split, KV head x query-head group, batch).

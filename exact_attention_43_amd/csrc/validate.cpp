@@ -81,6 +81,14 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &pl->scale_log2, &pl->cap_in,
                       &pl->cap_out_log2, &pl->softcap);
   if (st != EXATTN_OK) return st;
+  // The prefill kernel takes its row max on raw scores and scales afterwards,
+  // which needs a positive scale: a negative one is applied by negating Q.
+  pl->q_sign = 0u;
+  if (pl->scale_log2 < 0.0f) {
+    pl->q_sign = 0x80008000u;
+    pl->scale_log2 = -pl->scale_log2;
+    pl->cap_in = -pl->cap_in;
+  }
 
   pl->bf16 = a->dtype == EXATTN_BF16;
   pl->head_dim = a->head_dim;

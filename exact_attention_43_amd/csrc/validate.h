@@ -31,6 +31,7 @@ struct FwdPlan {
   int grid;      // work groups
   int xcd_group;
   float scale_log2, cap_in, cap_out_log2;
+  uint32_t q_sign;  // 0x80008000: negative scale, applied by negating Q (scale_log2 holds |scale|)
   int wl, wr;
 };
 
