@@ -8,29 +8,35 @@
 // log-sum-exp are written (same page, section 二.2).
 //
 // gfx950 design (not the pages' CUDA design):
-// - work group = 4 waves x 32 query rows = 128 rows of one query head; KV
-//   blocks of 64 keys;
+// - a work group owns 128 query rows of one query head.  It has NG groups of
+//   4 waves; every group covers all 128 rows (32 per wave) and the groups split
+//   the KV blocks between them (group g takes blocks n_lo + g, n_lo + g + NG,
+//   ...), each with its own double-buffered K/V tiles.  With NG = 2 every SIMD
+//   runs two waves: one wave's softmax issues while the other's MFMAs run, and
+//   LDS reads reach about 200 B/clk/CU instead of about 120 with one wave per
+//   SIMD (measured).  The groups' partial (m, l, O) are merged through LDS at
+//   the end, the same log-sum-exp merge as between tiles;
 // - the wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (bf16/f16, fp32
 //   accumulate): K is the A operand read from LDS, Q^T the B operand held in
 //   registers for the whole loop.  In the 32x32 accumulator layout every lane
-//   owns ONE query row, so row max and row sum are in-lane, plus one
-//   exchange between the two 32-lane halves;
+//   owns ONE query row, so row max and row sum are in-lane, plus one exchange
+//   between the two 32-lane halves;
 // - the A-operand row -> key map is permuted so that accumulator registers
 //   8c..8c+7 of lane half H are 8 consecutive keys (16c + 8H + 0..7); rounded
 //   to 16 bits they are directly the B operand (P^T) of O^T = V^T P^T;
-// - K tiles go from global memory straight into LDS (global_load_lds_dwordx4,
-//   no staging registers); V tiles are staged in registers and written to LDS
-//   transposed, so the V^T operand is one ds_read_b128 per MFMA (a measured
-//   1.6x cheaper per byte than the LDS transpose read);
+// - K tiles go from global memory straight into LDS (buffer_load ... lds, no
+//   staging registers); V tiles are staged in registers and written to LDS
+//   transposed, so the V^T operand is one ds_read_b128 per MFMA (the LDS
+//   transpose read delivers about half the bytes per clock, measured);
 // - 16-byte chunks are XOR-swizzled per row, which keeps every operand read
-//   and every V^T write free of bank conflicts, and makes all LDS addresses
+//   and every V^T write free of bank conflicts and all LDS addresses
 //   loop-invariant;
-// - software pipeline: the MFMAs of S(n+1) = K(n+1) Q^T are issued before the
-//   softmax of block n, so the VALU work of one block overlaps the matrix work
-//   of the next; K/V tiles are double-buffered, one barrier per block;
+// - loads use per-block buffer descriptors whose range ends at the last key of
+//   the sequence: the hardware range check returns zeros past the end, so
+//   block tails need no extra code;
 // - scores stay in the log2 domain: p = 2^(s * scale * log2 e - m) is one FMA
 //   and one v_exp_f32;
-// - lazy rescaling: the reference max m of a row only moves when a block's max
+// - lazy rescaling: a row's reference max m only moves when a block's max
 //   exceeds it by more than 2^8, so O is rescaled rarely (exact: O and the sum
 //   always share one reference);
 // - masks (bottom-right causal, window, sequence tail) are evaluated only on
@@ -44,19 +50,24 @@
 namespace exattn {
 namespace {
 
-constexpr int kBM = 128;  // query rows per work group
-constexpr int kBN = 64;   // keys per KV block
-constexpr int kThreads = 256;
+constexpr int kBM = 128;          // query rows per work group
 constexpr float kLazyTau = 8.0f;  // rescale only when the row max grows by > 2^8
+
+// Groups per work group and keys per KV block for a head dimension (LDS: NG
+// groups x 2 stages x (K + V^T) tiles of BN x D bf16 = NG * 4 * BN * D bytes).
+template <int D> struct Cfg;
+template <> struct Cfg<64> { static constexpr int NG = 2, BN = 64; };
+template <> struct Cfg<128> { static constexpr int NG = 2, BN = 64; };
+template <> struct Cfg<256> { static constexpr int NG = 1, BN = 64; };
 
 // K tile: row `key` is D*2 bytes; 16-byte chunk c is stored at c ^ kswz(key).
 // The 8 lanes of one A-operand read phase read keys {b..b+3, b+8..b+11}; the
 // swizzle gives them distinct low 3 bits.
 __device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 1) << 2); }
 
-// V^T tile: row d holds the block's 64 keys (8 chunks of 8 keys, 128 bytes);
-// chunk kc is stored at kc ^ vswz(d).  Bijective on each aligned group of 8
-// rows (conflict-free operand reads) and spreads the 16 lanes of a transposed
+// V^T tile: row d holds the block's BN keys (BN/8 chunks of 8 keys); chunk kc
+// is stored at kc ^ vswz(d).  Bijective on each aligned group of 8 rows
+// (conflict-free operand reads) and spreads the 16 lanes of a transposed
 // 8-byte write over distinct banks.
 __device__ __forceinline__ int vswz(int d) { return (d ^ (2 * (d >> 3))) & 7; }
 
@@ -65,9 +76,7 @@ __device__ __forceinline__ int row_key(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
-// max / sum over the two 32-lane halves, broadcast to all lanes.  (The
-// compiler folds the two results of v_permlane32_swap(x, x) into one, so the
-// exchange goes through ds_bpermute.)
+// max / sum over the two 32-lane halves, broadcast to all lanes.
 __device__ __forceinline__ float halves_max(float x) { return fmaxf(x, xor32(x)); }
 __device__ __forceinline__ float halves_sum(float x) { return x + xor32(x); }
 
@@ -98,27 +107,39 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t rs, uint
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <bool BF16, int D, bool SOFTCAP>
-__global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(256 * Cfg<D>::NG)
+prefill_kernel(const FwdParams p) {
   using E = Elem<BF16>;
+  constexpr int NG = Cfg<D>::NG;
+  constexpr int BN = Cfg<D>::BN;
+  constexpr int NT2 = BN / 32;                 // 32-key MFMA tiles per KV block
   constexpr int DCH = D / 8;                   // 16-byte chunks per row
   constexpr int KS = D / 16;                   // k-steps of the 32x32x16 MFMA over head_dim
   constexpr int DT = D / 32;                   // 32-wide head_dim tiles of O^T
-  constexpr int KTILE = kBN * D * 2;           // bytes
-  constexpr int VTILE = D * kBN * 2;
+  constexpr int KTILE = BN * D * 2;            // bytes
+  constexpr int VTILE = D * BN * 2;
+  constexpr int GROUP_LDS = 2 * KTILE + 2 * VTILE;
   constexpr int ROWS_PER_KB = 1024 / (D * 2);  // K rows per 1 KiB direct-load slice
   constexpr int KINST = KTILE / 4096;          // direct loads per wave per K tile
   constexpr int G4 = DCH / 4;                  // 4-chunk groups per V row
-  constexpr int VUNITS = 64 * G4;              // (4 keys x 8 columns) V pieces per tile
-  constexpr int VLD = (VUNITS + kThreads - 1) / kThreads;
+  constexpr int VUNITS = (BN / 4) * DCH;       // (4 keys x 8 columns) V pieces per tile
+  constexpr int VLD = (VUNITS + 255) / 256;
   static_assert(KINST >= 1 && KTILE % 4096 == 0, "tile/thread mismatch");
+  static_assert(NG * GROUP_LDS <= 160 * 1024, "LDS budget");
+  // the end-of-loop merge reuses the tile buffers: 4 waves x (16 DT + 2) floats per lane
+  static_assert(NG == 1 || NG * GROUP_LDS >= 4 * 64 * (16 * DT + 2) * 4, "merge buffer");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE + 2 * VTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NG * GROUP_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;   // KV-block group
+  const int wg = wave & 3;     // wave within the group: query rows 32 wg .. 32 wg + 31
+  const int gtid = tid & 255;  // thread index within the group
   const int hsel = lane >> 5;  // which 32-lane half
   const int l32 = lane & 31;
+  uint8_t* gsm = smem + grp * GROUP_LDS;
 
   // ---- tile scheduler: heaviest query tiles first; (batch, head) fastest.
   const int units = p.batch * p.h_q;
@@ -176,12 +197,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
   if (p.wr >= 0) kmax = min(kmax, q_last + off + p.wr);
   int n_lo = 0, n_hi = 0;
   if (kmax >= kmin) {
-    n_lo = kmin / kBN;
-    n_hi = kmax / kBN + 1;
+    n_lo = kmin / BN;
+    n_hi = kmax / BN + 1;
   }
 
   // ---- Q^T fragments: lane holds Q[row][16 ks + 8 hsel .. +7] for every ks.
-  const int qrow = q0 + wave * 32 + l32;
+  const int qrow = q0 + wg * 32 + l32;
   u32x4_t qf[KS];
   if (qrow < sq) {
     const uint16_t* qp = qg + (int64_t)qrow * p.q_ss + 8 * hsel;
@@ -208,90 +229,70 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
     kaddr[bq] = krow * (D * 2) + 32 * (bq ^ (ksw >> 1)) + 16 * (hsel ^ (ksw & 1));
   // V^T operand: row d = 32 dt + l32 (vswz does not depend on dt); chunk
   // kc = 4 t2 + 2 c + hsel for MFMA (t2, c).
-  int vaddr[4];
+  int vaddr[NT2 * 2];
   {
     const int vs = vswz(l32);
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) vaddr[2 * t2 + c] = l32 * (kBN * 2) + 16 * ((4 * t2 + 2 * c + hsel) ^ vs);
+      for (int c = 0; c < 2; ++c) vaddr[2 * t2 + c] = l32 * (BN * 2) + 16 * ((4 * t2 + 2 * c + hsel) ^ vs);
   }
 
-  // ---- K/V loads through buffer descriptors built per KV block: the base is
-  // the block's first row and the range ends after the last valid row, so rows
-  // past the sequence end read as zeros (hardware range check, no tail code).
-
-  // K goes straight into LDS: wave `wave`, instruction i fills 1 KiB slice
-  // 4 i + wave; lane l writes slot l = (row l / DCH of the slice, stored chunk
-  // l % DCH), so it fetches global chunk (l % DCH) ^ kswz(row).  Lane offsets
-  // are loop-invariant bytes (token strides are checked on the host).
+  // ---- K straight into LDS: wave wg of the group, instruction i fills 1 KiB
+  // slice 4 i + wg; lane l writes slot l = (row l / DCH of the slice, stored
+  // chunk l % DCH), so it fetches global chunk (l % DCH) ^ kswz(row).  Lane
+  // offsets are loop-invariant bytes (token strides are checked on the host).
   uint32_t kofs_ld[KINST];
 #pragma unroll
   for (int i = 0; i < KINST; ++i) {
-    const int row = (4 * i + wave) * ROWS_PER_KB + lane / DCH;
+    const int row = (4 * i + wg) * ROWS_PER_KB + lane / DCH;
     kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ (kswz(row) & (DCH - 1)))) * 2u;
   }
   auto issue_k = [&](int n, int stage) {
-    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(kg, p.k_ss, n * kBN, sk);
-    uint8_t* dst = smem + stage * KTILE;
+    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(kg, p.k_ss, n * BN, sk);
+    uint8_t* dst = gsm + stage * KTILE;
 #pragma unroll
-    for (int i = 0; i < KINST; ++i)
-      buffer_load_lds16(rs, dst + (4 * i + wave) * 1024, kofs_ld[i]);
+    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rs, dst + (4 * i + wg) * 1024, kofs_ld[i]);
   };
 
-  // V is staged in registers: unit un -> (kq, dc) with dc = a + 4 dc_hi,
+  // ---- V staged in registers: unit un -> (kq, dc) with dc = a + 4 dc_hi,
   // kq = b + 4 kq_hi, a = un & 3, b = (un >> 2) & 3, c = un >> 4, dc_hi = c % G4,
   // kq_hi = c / G4.  One wave instruction covers whole rows (coalesced) and each
   // 16-lane group's transposed 8-byte writes hit 16 distinct bank slots.
   int vkq[VLD], vdc[VLD];
-  uint32_t vofs[VLD][4];
+  uint32_t vofs[VLD];
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
-    const int un = tid + i * kThreads;
+    const int un = gtid + i * 256;
     const int cc = un >> 4;
     vdc[i] = (un & 3) + 4 * (cc % G4);
     vkq[i] = ((un >> 2) & 3) + 4 * (cc / G4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vofs[i][r] = (uint32_t)((4 * vkq[i] + r) * p.v_ss + 8 * vdc[i]) * 2u;
+    vofs[i] = (uint32_t)(4 * vkq[i] * p.v_ss + 8 * vdc[i]) * 2u;
   }
+  const uint32_t vrow_bytes = (uint32_t)p.v_ss * 2u;
   u32x4_t vst[VLD][4];
   auto issue_v = [&](int n) {
-    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(vg, p.v_ss, n * kBN, sk);
+    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(vg, p.v_ss, n * BN, sk);
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
-      if (VUNITS % kThreads == 0 || tid + i * kThreads < VUNITS)
+      if (VUNITS % 256 == 0 || gtid + i * 256 < VUNITS)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vst[i][r] = buffer_load16(rs, vofs[i][r]);
+        for (int r = 0; r < 4; ++r) vst[i][r] = buffer_load16(rs, vofs[i] + r * vrow_bytes);
   };
   auto store_v = [&](int stage) {
-    uint8_t* vs_ = smem + 2 * KTILE + stage * VTILE;
+    uint8_t* vs_ = gsm + 2 * KTILE + stage * VTILE;
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
-      if (VUNITS % kThreads == 0 || tid + i * kThreads < VUNITS) {
+      if (VUNITS % 256 == 0 || gtid + i * 256 < VUNITS) {
         const int kq = vkq[i];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int d = 8 * vdc[i] + t;
-          *(u32x2_t*)(vs_ + d * (kBN * 2) + 16 * ((kq >> 1) ^ vswz(d)) + 8 * (kq & 1)) =
+          *(u32x2_t*)(vs_ + d * (BN * 2) + 16 * ((kq >> 1) ^ vswz(d)) + 8 * (kq & 1)) =
               column4(vst[i][0], vst[i][1], vst[i][2], vst[i][3], t);
         }
       }
     }
-  };
-
-  auto qk = [&](int stage, f32x16_t (&s)[2]) {
-    const uint8_t* ks_ = smem + stage * KTILE;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) s[t2] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x4_t a =
-            *(const u32x4_t*)(ks_ + kaddr[ks & 3] + 128 * (ks >> 2) + t2 * 32 * (D * 2));
-        s[t2] = E::mfma32x32x16(a, qf[ks], s[t2]);
-      }
   };
 
   f32x16_t oacc[DT];
@@ -300,40 +301,40 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
   float m_ref = kNegInf;  // reference max (log2 domain) of this lane's row
   float l_run = 0.f;      // this lane's share of the row sum, relative to m_ref
 
-  // One pipeline step: S(n+1) on the MFMAs while block n is softmaxed, then
-  // O += P(n) V(n).  s_c holds S(n) on entry; s_n receives S(n+1).
-  auto step = [&](int n, f32x16_t (&s_c)[2], f32x16_t (&s_n)[2]) {
-    const int j = n - n_lo;
-    const bool has_next = n + 1 < n_hi;
-    // K(n+1) has landed in LDS, V^T(n) is written; every wave is done with block n-1.
-    wait_vmem_all();
-    __syncthreads();
-    if (n + 2 < n_hi) issue_k(n + 2, j & 1);
-    if (has_next) {
-      issue_v(n + 1);
-      qk((j + 1) & 1, s_n);
-    }
+  // ---- one KV block: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
+  auto block = [&](int n, int stage) {
+    const uint8_t* ks_ = gsm + stage * KTILE;
+    f32x16_t s[NT2];
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2) s[t2] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2) {
+        const u32x4_t a =
+            *(const u32x4_t*)(ks_ + kaddr[ks & 3] + 128 * (ks >> 2) + t2 * 32 * (D * 2));
+        s[t2] = E::mfma32x32x16(a, qf[ks], s[t2]);
+      }
 
-    // ---- softmax of block n (overlaps the MFMAs above).
-    const int kb = n * kBN;
-    const bool need_mask = (kb + kBN > sk) || (p.wr >= 0 && kb + kBN - 1 > q0 + off + p.wr) ||
+    const int kb = n * BN;
+    const bool need_mask = (kb + BN > sk) || (p.wr >= 0 && kb + BN - 1 > q0 + off + p.wr) ||
                            (p.wl >= 0 && kb < q_last + off - p.wl);
     if (need_mask) {
       const int hi = (p.wr >= 0 ? min(sk - 1, qrow + off + p.wr) : sk - 1) - kb - 8 * hsel;
       const int lo = (p.wl >= 0 ? qrow + off - p.wl : -0x3fffffff) - kb - 8 * hsel;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = 32 * t2 + 16 * (r >> 3) + (r & 7);  // key - kb - 8 hsel
-          if (kk > hi || kk < lo) s_c[t2][r] = kNegInf;
+          if (kk > hi || kk < lo) s[t2][r] = kNegInf;
         }
     }
-    float mraw = s_c[0][0];
+    float mraw = s[0][0];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s_c[t2][r]);
+      for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[t2][r]);
     mraw = halves_max(mraw);
     float m_blk;
     if constexpr (SOFTCAP)
@@ -354,20 +355,20 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
     m_ref = m_new;
     const float base = m_ref == kNegInf ? 0.f : m_ref;
     float psum = 0.f;
-    u32x4_t pf[2][2];
+    u32x4_t pf[NT2][2];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float x0, x1;
         if constexpr (SOFTCAP) {
           // masked scores are -inf and must stay so (tanh(-inf) would give -1)
-          const float a0 = s_c[t2][r], a1 = s_c[t2][r + 1];
+          const float a0 = s[t2][r], a1 = s[t2][r + 1];
           x0 = a0 == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(a0 * p.cap_in) - base;
           x1 = a1 == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(a1 * p.cap_in) - base;
         } else {
-          x0 = __builtin_fmaf(s_c[t2][r], p.scale_log2, -base);
-          x1 = __builtin_fmaf(s_c[t2][r + 1], p.scale_log2, -base);
+          x0 = __builtin_fmaf(s[t2][r], p.scale_log2, -base);
+          x1 = __builtin_fmaf(s[t2][r + 1], p.scale_log2, -base);
         }
         x0 = fast_exp2(x0);
         x1 = fast_exp2(x1);
@@ -377,40 +378,77 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
       }
     l_run += psum;
 
-    // ---- O^T += V^T P^T.
-    const uint8_t* vs_ = smem + 2 * KTILE + (j & 1) * VTILE;
+    const uint8_t* vs_ = gsm + 2 * KTILE + stage * VTILE;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const u32x4_t a = *(const u32x4_t*)(vs_ + vaddr[2 * t2 + c] + dt * 32 * (kBN * 2));
+          const u32x4_t a = *(const u32x4_t*)(vs_ + vaddr[2 * t2 + c] + dt * 32 * (BN * 2));
           oacc[dt] = E::mfma32x32x16(a, pf[t2][c], oacc[dt]);
         }
-
-    if (has_next) store_v((j + 1) & 1);
   };
 
-  f32x16_t sa[2], sb[2];
-  if (n_lo < n_hi) {
-    issue_k(n_lo, 0);
-    issue_v(n_lo);
-    if (n_lo + 1 < n_hi) issue_k(n_lo + 1, 1);
+  // ---- main loop: step i, group g works on block n_lo + NG i + g; every group
+  // runs the same number of steps so one work-group barrier per step suffices.
+  const int nblk = n_hi - n_lo;
+  const int steps = (nblk + NG - 1) / NG;
+  if (steps > 0) {
+    const int n0 = n_lo + grp;
+    if (n0 < n_hi) {
+      issue_k(n0, 0);
+      issue_v(n0);
+      wait_vmem_all();
+      store_v(0);
+    }
+  }
+  for (int i = 0; i < steps; ++i) {
+    const int n = n_lo + NG * i + grp;
+    const int nn = n + NG;  // this group's next block
+    // K(n) has landed in LDS and V^T(n) is written; every wave is done with step i-1.
     wait_vmem_all();
-    store_v(0);
     __syncthreads();
-    qk(0, sa);
+    if (nn < n_hi) {
+      issue_k(nn, (i + 1) & 1);
+      issue_v(nn);
+    }
+    if (n < n_hi) block(n, i & 1);
+    if (nn < n_hi) store_v((i + 1) & 1);
   }
-  int n = n_lo;
-  for (; n + 1 < n_hi; n += 2) {
-    step(n, sa, sb);
-    step(n + 1, sb, sa);
+
+  // ---- merge the groups: group 1 hands (m, l, O) to group 0 through LDS.
+  float l_tot = halves_sum(l_run);
+  if constexpr (NG > 1) {
+    __syncthreads();  // tile buffers are free
+    float* xm = reinterpret_cast<float*>(smem);  // [wave in group][2][lane]: m, l
+    float* xo = xm + 2 * 4 * 64;                  // [wave in group][reg][lane]: O^T
+    if (grp == 1) {
+      xm[(wg * 2 + 0) * 64 + lane] = m_ref;
+      xm[(wg * 2 + 1) * 64 + lane] = l_tot;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[((wg * DT + dt) * 16 + r) * 64 + lane] = oacc[dt][r];
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    const float m1 = xm[(wg * 2 + 0) * 64 + lane];
+    const float l1 = xm[(wg * 2 + 1) * 64 + lane];
+    const float mm = fmaxf(m_ref, m1);
+    const float bm = mm == kNegInf ? 0.f : mm;
+    const float a0 = fast_exp2(m_ref - bm);  // 0 for an empty side
+    const float a1 = fast_exp2(m1 - bm);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[dt][r] = oacc[dt][r] * a0 + xo[((wg * DT + dt) * 16 + r) * 64 + lane] * a1;
+    l_tot = l_tot * a0 + l1 * a1;
+    m_ref = mm;
   }
-  if (n < n_hi) step(n, sa, sb);
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; empty rows: 0 and -inf.
-  const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < sq) {
     uint16_t* op = og + (int64_t)qrow * p.o_ss;
@@ -430,10 +468,11 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const FwdParams p) {
 
 template <bool BF16, int D>
 hipError_t launch_d(const FwdParams& p, bool softcap, int grid, hipStream_t stream) {
+  const dim3 block(256 * Cfg<D>::NG);
   if (softcap)
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<BF16, D, true>), dim3(grid), block, 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<BF16, D, false>), dim3(grid), block, 0, stream, p);
   return hipGetLastError();
 }
 
