@@ -172,6 +172,7 @@ exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t
     p.s_cache = a->seqlen_cache;
     p.n_split = pl.n_split;
     p.n_hg = pl.n_hg;
+    p.hpw = pl.hpw;
     p.scale_log2 = pl.scale_log2;
     p.cap_in = pl.cap_in;
     p.cap_out_log2 = pl.cap_out_log2;

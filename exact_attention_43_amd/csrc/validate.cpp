@@ -133,12 +133,18 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   return EXATTN_OK;
 }
 
+int decode_heads_per_group(int head_dim, int heads_kv) {
+  int hpw = head_dim <= 64 ? 4 : head_dim <= 128 ? 2 : 1;
+  while (hpw > 1 && hpw > heads_kv) hpw >>= 1;
+  return hpw;
+}
+
 int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,
                     int32_t head_dim, int32_t num_cus) {
-  (void)head_dim;
   if (batch <= 0 || seqlen_k <= 0 || heads_kv <= 0 || heads_q <= 0 || num_cus <= 0) return 1;
   const int64_t group = heads_q / heads_kv;
-  const int64_t units = (int64_t)batch * heads_kv * ((group + 15) / 16);
+  const int64_t hpw = decode_heads_per_group(head_dim, heads_kv);
+  const int64_t units = (int64_t)batch * ((heads_kv + hpw - 1) / hpw) * ((group + 15) / 16);
   const int64_t target_wgs = 2LL * num_cus;  // about two work groups per compute unit
   if (units >= target_wgs) return 1;
   int64_t splits = (target_wgs + units - 1) / units;
@@ -162,6 +168,8 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
   pl->head_dim = a->head_dim;
   pl->group = a->heads_q / a->heads_kv;
   pl->n_hg = (pl->group + 15) / 16;
+  pl->hpw = decode_heads_per_group(a->head_dim, a->heads_kv);
+  pl->n_hk = (a->heads_kv + pl->hpw - 1) / pl->hpw;
   pl->wl = a->window_left < 0 ? -1 : a->window_left;
   int64_t ns = a->num_splits == 0
                    ? auto_splits(a->batch, a->heads_q, a->heads_kv, a->seqlen_cache, a->head_dim,
@@ -195,7 +203,7 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
       return fail(EXATTN_E_INVALID, "k/v strides must be non-negative multiples of 8 elements");
   if (a->lse != nullptr && (reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0)
     return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
-  if ((int64_t)a->heads_kv * pl->n_hg > 65535 || a->batch > 65535)
+  if ((int64_t)pl->n_hk * pl->n_hg > 65535 || a->batch > 65535)
     return fail(EXATTN_E_INVALID, "too many heads or batch entries for one launch");
   return EXATTN_OK;
 }
