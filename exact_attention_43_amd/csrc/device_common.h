@@ -18,6 +18,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -38,6 +40,11 @@ struct Elem<true> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
+  // 16x16x16: A lane l holds A[l%16][4(l/16)..+3], B lane l holds B[4(l/16)..+3][l%16].
+  static __device__ __forceinline__ f32x4_t mfma16x16x16(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
@@ -53,6 +60,10 @@ struct Elem<false> {
   static __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16x16x16(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f32x2_t v = {lo, hi};
@@ -71,6 +82,14 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float tanh_exp2(float y) {
   float e = fast_exp2(y * (2.0f * kLog2e));
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+// LDS transposing read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// output lane i element t is element (i & 3) of the 4 16-bit values that
+// source lane (i >> 2) + 4 t addresses (8 bytes per lane).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t* lds) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)lds));
 }
 
 // Swap values between the two 32-lane halves of the wave (lane i <-> lane i ^ 32).

@@ -80,13 +80,14 @@ __device__ __forceinline__ int row_key(int m) {
 __device__ __forceinline__ float halves_max(float x) { return fmaxf(x, xor32(x)); }
 __device__ __forceinline__ float halves_sum(float x) { return x + xor32(x); }
 
-// Buffer descriptor for the rows kb .. sk-1 of one head (row stride ss
-// elements): loads past the last valid element return zeros (the hardware
-// range check of raw buffer loads is per dword).  Word 3 is the gfx9 default.
+// Buffer descriptor for the rows kb .. min(sk, kb + rows) - 1 of one head (row
+// stride ss elements): loads past the last valid element return zeros (the
+// hardware range check of raw buffer loads is per dword).  Word 3 is the gfx9
+// default.
 template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* g, int64_t ss, int kb,
-                                                             int sk) {
-  const int64_t last = (int64_t)(sk - 1 - kb) * ss + D;  // elements up to the end of row sk-1
+                                                             int sk, int rows) {
+  const int64_t last = (int64_t)min(sk - 1 - kb, rows - 1) * ss + D;  // elements to the end of the last row
   return __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)kb * ss), 0, (int)(last * 2),
                                            0x00020000);
 }
@@ -249,7 +250,7 @@ prefill_kernel(const FwdParams p) {
     kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ (kswz(row) & (DCH - 1)))) * 2u;
   }
   auto issue_k = [&](int n, int stage) {
-    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(kg, p.k_ss, n * BN, sk);
+    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
     uint8_t* dst = gsm + stage * KTILE;
 #pragma unroll
     for (int i = 0; i < KINST; ++i) buffer_load_lds16(rs, dst + (4 * i + wg) * 1024, kofs_ld[i]);
@@ -272,7 +273,7 @@ prefill_kernel(const FwdParams p) {
   const uint32_t vrow_bytes = (uint32_t)p.v_ss * 2u;
   u32x4_t vst[VLD][4];
   auto issue_v = [&](int n) {
-    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(vg, p.v_ss, n * BN, sk);
+    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
       if (VUNITS % 256 == 0 || gtid + i * 256 < VUNITS)

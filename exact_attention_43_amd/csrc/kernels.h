@@ -47,7 +47,7 @@ struct DecParams {
   float* ws_lse;                 // [split][batch][h_q] fp32 partial LSE
   int32_t batch, h_q, h_kv, group, s_cache;
   int32_t n_split, n_hg;  // splits; query-head groups of 16 per KV head
-  int32_t hpw;            // adjacent KV heads per work group (1, 2 or 4)
+  int32_t hpw;            // adjacent KV heads per work group (a power of two)
   float scale_log2, cap_in, cap_out_log2;
   int32_t wl;
 };

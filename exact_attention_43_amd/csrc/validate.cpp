@@ -134,7 +134,7 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
 }
 
 int decode_heads_per_group(int head_dim, int heads_kv) {
-  int hpw = head_dim <= 64 ? 4 : head_dim <= 128 ? 2 : 1;
+  int hpw = head_dim <= 64 ? 16 : head_dim <= 128 ? 8 : 4;
   while (hpw > 1 && hpw > heads_kv) hpw >>= 1;
   return hpw;
 }
@@ -145,7 +145,7 @@ int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t se
   const int64_t group = heads_q / heads_kv;
   const int64_t hpw = decode_heads_per_group(head_dim, heads_kv);
   const int64_t units = (int64_t)batch * ((heads_kv + hpw - 1) / hpw) * ((group + 15) / 16);
-  const int64_t target_wgs = 2LL * num_cus;  // about two work groups per compute unit
+  const int64_t target_wgs = num_cus;  // one work group (two 64 KiB LDS stages) per compute unit
   if (units >= target_wgs) return 1;
   int64_t splits = (target_wgs + units - 1) / units;
   const int64_t by_len = seqlen_k / 256 > 1 ? seqlen_k / 256 : 1;  // >= 256 keys per split

@@ -45,7 +45,7 @@ struct DecodePlan {
   bool softcap;
   int group;
   int n_hg;      // groups of 16 query heads per KV head
-  int hpw;       // KV heads per work group (adjacent heads: contiguous key-row pieces)
+  int hpw;       // adjacent KV heads per work group (contiguous key-row pieces)
   int n_hk;      // KV-head groups: ceil(heads_kv / hpw)
   int n_split;
   size_t ws_bytes;
@@ -57,9 +57,10 @@ struct DecodePlan {
 // Check `a` and fill `plan` for a device with `num_cus` compute units.
 exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* plan);
 
-// KV heads one decode work group covers: as many adjacent heads as make a
-// 512-byte piece of each key row (4 at d = 64, 2 at d = 128, 1 at d = 256),
-// rounded down to a power of two that does not exceed heads_kv.
+
+// Adjacent KV heads one decode work group covers: enough for a 2 KiB piece of
+// every key row (16 at d = 64, 8 at d = 128, 4 at d = 256), rounded down to a
+// power of two no larger than heads_kv.
 int decode_heads_per_group(int head_dim, int heads_kv);
 
 int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,

@@ -157,11 +157,11 @@ exattn_status exattn_decode(const exattn_decode_args *args, void *workspace,
                             size_t workspace_bytes, void *stream);
 
 /* The automatic split count, as a pure function (no device query).  One work
- * group covers up to 512/(2*head_dim) adjacent KV heads (4 at d = 64, 2 at
- * d = 128, 1 at d = 256; a power of two no larger than heads_kv) and 16 of
- * their query heads.  The key axis is split so that these units times splits
- * fill about twice num_cus work groups, while each split keeps at least 256
- * keys (FAQ Q14's rules). */
+ * group covers up to 1024/head_dim adjacent KV heads (16 at d = 64, 8 at
+ * d = 128, 4 at d = 256; a power of two no larger than heads_kv) and 16 of
+ * their query heads, and one work group runs per compute unit.  The key axis
+ * is split so that these units times splits fill num_cus work groups, while
+ * each split keeps at least 256 keys (FAQ Q14's rules). */
 int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv,
                                   int32_t seqlen_k, int32_t head_dim, int32_t num_cus);
 

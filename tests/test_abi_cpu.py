@@ -162,16 +162,16 @@ def test_decode_workspace_checks(L):
 
 def test_auto_splits_rules(L):
     # FAQ Q14: enough (batch x heads) work -> 1 split; few units -> split toward the CU count;
-    # a split never gets fewer than 256 keys.  A work group covers 2 adjacent KV heads at
-    # d = 128, 4 at d = 64, 1 at d = 256.
-    assert ex.auto_splits(8, 32, 8, 16384, 128, 256) == 16      # 32 units -> 512 work groups
-    assert ex.auto_splits(8, 32, 8, 16384, 64, 256) == 32       # 16 units
-    assert ex.auto_splits(8, 32, 8, 16384, 256, 256) == 8       # 64 units
-    assert ex.auto_splits(128, 32, 8, 16384, 128, 256) == 1     # 512 units already
-    assert ex.auto_splits(64, 32, 8, 16384, 128, 256) == 2      # 256 units
-    assert ex.auto_splits(1, 32, 8, 16384, 128, 256) == 64      # 4 units -> capped at length / 256
+    # a split never gets fewer than 256 keys.  A work group covers 8 adjacent KV heads at
+    # d = 128, 16 at d = 64, 4 at d = 256, and one work group runs per CU.
+    assert ex.auto_splits(8, 32, 8, 16384, 128, 256) == 32      # 8 units -> 256 work groups
+    assert ex.auto_splits(8, 32, 8, 16384, 64, 256) == 32       # 8 KV heads make one unit too
+    assert ex.auto_splits(8, 32, 8, 16384, 256, 256) == 16      # 16 units
+    assert ex.auto_splits(256, 32, 8, 16384, 128, 256) == 1     # 256 units already
+    assert ex.auto_splits(64, 32, 8, 16384, 128, 256) == 4      # 64 units
+    assert ex.auto_splits(1, 32, 8, 16384, 128, 256) == 64      # 1 unit -> capped at length / 256
     assert ex.auto_splits(1, 32, 8, 1024, 128, 256) == 4        # capped by length / 256
     assert ex.auto_splits(1, 32, 8, 100, 128, 256) == 1
     assert ex.auto_splits(1, 8, 8, 0, 128, 256) == 1
-    assert ex.auto_splits(2, 64, 1, 1 << 20, 128, 256) == 64    # one KV head, 4 groups of 16 queries
-    assert ex.auto_splits(2, 6, 3, 1 << 20, 64, 256) == 128     # 3 KV heads -> 2 per work group, 4 units
+    assert ex.auto_splits(2, 64, 1, 1 << 20, 128, 256) == 32    # one KV head, 4 groups of 16 queries
+    assert ex.auto_splits(2, 6, 3, 1 << 20, 64, 256) == 64      # 3 KV heads -> 2 per work group

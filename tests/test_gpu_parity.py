@@ -291,6 +291,32 @@ def test_decode_split_sweep(splits):
     assert_lse_close(lse, l_ref, f"splits {splits}")
 
 
+def test_decode_back_to_back_calls_reuse_workspace():
+    """Many queued calls on one workspace, with changing split counts: every call equals the
+    first call with the same split count bit for bit, and those match the oracle."""
+    q, kc, vc = W.kvcache(4, 3000, 32, 8, 128, seed=138)
+    lens = torch.tensor([3000, 1, 2047, 0], dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens)
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=DEV)
+    split_seq = [16, 16, 7, 93, 16, 2, 7, 0, 93, 16] * 3
+    outs = []
+    for ns in split_seq:
+        out, lse = ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, num_splits=ns, workspace=ws)
+        outs.append((ns, out, lse))
+    torch.cuda.synchronize()
+    first = {}
+    for ns, out, lse in outs:
+        if ns not in first:
+            first[ns] = (out, lse)
+            o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens)
+            assert_o_close(out, o_ref, torch.bfloat16, f"splits {ns}")
+            assert_lse_close(lse, l_ref, f"splits {ns}")
+        else:
+            assert torch.equal(out, first[ns][0]) and torch.equal(lse, first[ns][1]), ns
+    ns, wb = ex.decode_plan(dq[:, 0], dkc, dvc, dl, num_splits=93)
+    assert wb <= ws.numel()
+
+
 def test_decode_matches_prefill_row():
     """s_q = 1 through the prefill kernel and through the decode kernel agree with each other."""
     q, kc, vc = W.kvcache(2, 777, 8, 2, 128, seed=136)
@@ -310,7 +336,7 @@ def test_graph_capture_decode_replays():
     out = torch.empty_like(dq)
     lse = torch.empty((2, 16, 1), dtype=torch.float32, device=DEV)
     ns, wb = ex.decode_plan(dq[:, 0], dkc, dvc, dl)
-    ws = torch.empty(max(wb, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wb, 256), dtype=torch.uint8, device=DEV)
     ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     eager_o, eager_l = out.clone(), lse.clone()
