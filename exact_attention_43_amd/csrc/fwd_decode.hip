@@ -132,11 +132,11 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     kofs[t] = (uint32_t)((key * p.k_ss + head * p.k_sh) * 2 + 16 * (pos ^ kswz(key)));
     vofs[t] = (uint32_t)((key * p.v_ss + head * p.v_sh) * 2 + 16 * (pos ^ vswz<D>(key)));
   }
-  auto issue = [&](int st, int stage) {
+  // DMA of step st's K and V tiles into the stage at dst.
+  auto issue = [&](int st, uint8_t* dst) {
     const int kbase = kb + st * KSTEP;
     const __amdgpu_buffer_rsrc_t rk = rows_rsrc<D>(kg, p.k_ss, p.k_sh, kbase, nk, nh_valid, KSTEP);
     const __amdgpu_buffer_rsrc_t rv = rows_rsrc<D>(vg, p.v_ss, p.v_sh, kbase, nk, nh_valid, KSTEP);
-    uint8_t* dst = smem + stage * STAGE;
 #pragma unroll
     for (int t = 0; t < KI; ++t) buffer_load_lds16(rk, dst + (wave + NW * t) * 1024, kofs[t]);
 #pragma unroll
@@ -159,6 +159,12 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     for (int ks = 0; ks < KS; ++ks)
       qf[i][ks] = qv ? *(const u32x4_t*)(qp + 32 * ks) : u32x4_t{0, 0, 0, 0};
   }
+  // Consume Q here: the compiler then waits for these loads before the loop
+  // instead of, conservatively, inside every step behind the step's DMA.
+#pragma unroll
+  for (int i = 0; i < HPWV; ++i)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[i][ks]));
 
   // ---- loop-invariant LDS operand offsets within a stage.
   const int krow = 16 * sub + l16;                      // K A-operand row (key in the tile)
@@ -177,16 +183,14 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     for (int dt = 0; dt < DT; ++dt) oacc[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (s_lo < s_hi) issue(s_lo, 0);
-  for (int st = s_lo; st < s_hi; ++st) {
-    const int stage = (st - s_lo) & 1;
-    // this work group's loads of step st have landed, and every wave is done
-    // with step st - 1, whose stage the next loads refill
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (st + 1 < s_hi) issue(st + 1, stage ^ 1);
-    const uint8_t* kt = smem + stage * STAGE;
-    const uint8_t* vt = kt + KTILE;
+  // One step: start the DMA of step st + 1 into stage nxt, then compute step st
+  // from stage cur.  The two stages never overlap; restrict tells the compiler
+  // so, which lets the operand reads of cur proceed while the DMA into nxt is
+  // in flight (without it every LDS read waits for all outstanding DMA).
+  auto step = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int st) {
+    if (st + 1 < s_hi) issue(st + 1, nxt);
+    const uint8_t* kt = cur;
+    const uint8_t* vt = cur + KTILE;
     const int key0 = kb + st * KSTEP + 16 * sub;  // first key of this wave's sub-block
 #pragma unroll
     for (int i = 0; i < HPWV; ++i) {
@@ -227,6 +231,18 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
         oacc[i][dt] = E::mfma16x16x16(a, pf, oacc[i][dt] * alpha);
       }
     }
+  };
+
+  if (s_lo < s_hi) issue(s_lo, smem);
+  for (int st = s_lo; st < s_hi; ++st) {
+    // this work group's loads of step st have landed, and every wave is done
+    // with step st - 1, whose stage the next loads refill
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (((st - s_lo) & 1) == 0)
+      step(smem, smem + STAGE, st);
+    else
+      step(smem + STAGE, smem, st);
   }
 
   // ---- row sums over the four lane groups; merge the waves of a head slot.

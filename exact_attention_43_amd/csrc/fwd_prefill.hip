@@ -52,6 +52,7 @@ namespace {
 
 constexpr int kBM = 128;          // query rows per work group
 constexpr float kLazyTau = 8.0f;  // rescale only when the row max grows by > 2^8
+constexpr float kSumCap = 256.0f;  // 2^tau: a block sum below it means every p <= 2^tau
 
 // Groups per work group and keys per KV block for a head dimension (LDS: NG
 // groups x 2 stages x (K + V^T) tiles of BN x D bf16 = NG * 4 * BN * D bytes).
@@ -61,15 +62,30 @@ template <> struct Cfg<128> { static constexpr int NG = 2, BN = 64; };
 template <> struct Cfg<256> { static constexpr int NG = 1, BN = 64; };
 
 // K tile: row `key` is D*2 bytes; 16-byte chunk c is stored at c ^ kswz(key).
-// The 8 lanes of one A-operand read phase read keys {b..b+3, b+8..b+11}; the
-// swizzle gives them distinct low 3 bits.
-__device__ __forceinline__ int kswz(int key) { return (key & 3) | (((key >> 3) & 1) << 2); }
+// ds_read_b128 serves 16 lanes per clock (256 bytes over the 64 banks), and the
+// 16 lanes of an A-operand read read keys k0..k0+15 of one chunk column, so
+// their stored chunks must fall in 16 distinct 16-byte bank groups: rows of 256
+// bytes or more need 16 distinct positions; two 128-byte rows share one bank
+// width, so for d = 64 even and odd keys each need 8.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  if constexpr (D == 64)
+    return (key >> 1) & 7;
+  else
+    return key & 15;
+}
 
-// V^T tile: row d holds the block's BN keys (BN/8 chunks of 8 keys); chunk kc
-// is stored at kc ^ vswz(d).  Bijective on each aligned group of 8 rows
-// (conflict-free operand reads) and spreads the 16 lanes of a transposed
-// 8-byte write over distinct banks.
-__device__ __forceinline__ int vswz(int d) { return (d ^ (2 * (d >> 3))) & 7; }
+// V tile, stored row-major like K: chunk c of row `key` is stored at
+// c ^ vswz(key).  A transposing read takes 8 bytes from each of 4 consecutive
+// keys x 2 adjacent chunks per 16 lanes; even offsets keep those 8 chunks in
+// distinct bank groups (16 for 8 keys when d >= 128).
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  if constexpr (D >= 128)
+    return 2 * (key & 7);
+  else
+    return 2 * (key & 3);
+}
 
 // A-operand row m of a 32-key tile -> key: row 8J + 4H + I is key 16(J/2) + 8H + 4(J%2) + I.
 __device__ __forceinline__ int row_key(int m) {
@@ -122,9 +138,6 @@ prefill_kernel(const FwdParams p) {
   constexpr int GROUP_LDS = 2 * KTILE + 2 * VTILE;
   constexpr int ROWS_PER_KB = 1024 / (D * 2);  // K rows per 1 KiB direct-load slice
   constexpr int KINST = KTILE / 4096;          // direct loads per wave per K tile
-  constexpr int G4 = DCH / 4;                  // 4-chunk groups per V row
-  constexpr int VUNITS = (BN / 4) * DCH;       // (4 keys x 8 columns) V pieces per tile
-  constexpr int VLD = (VUNITS + 255) / 256;
   static_assert(KINST >= 1 && KTILE % 4096 == 0, "tile/thread mismatch");
   static_assert(NG * GROUP_LDS <= 160 * 1024, "LDS budget");
   // the end-of-loop merge reuses the tile buffers: 4 waves x (16 DT + 2) floats per lane
@@ -217,83 +230,62 @@ prefill_kernel(const FwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] ^= u32x4_t{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
   }
+  // Consume Q here: the compiler then waits for these loads before the loop.
+  // Otherwise it cannot tell that the loop's own waits covered them and waits
+  // inside every step for all newer loads, the next block's prefetch included.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
 
   // ---- loop-invariant LDS addresses.
   // K operand: tile t2 row key = 32 t2 + row_key(l32); chunk 2 ks + hsel lives
-  // at (2 ks + hsel) ^ kswz = 2 (ks ^ s1) + (hsel ^ s0); with ks = 4 a + bq the
-  // offset is 128 a + 32 (bq ^ s1) + 16 (hsel ^ s0), so 4 bases cover all ks.
+  // at (2 ks + hsel) ^ kswz = 2 (ks ^ s1) + (hsel ^ s0) with s1 < NKA; with
+  // ks = NKA a + bq the offset is 32 NKA a + 32 (bq ^ s1) + 16 (hsel ^ s0), so
+  // NKA bases cover all ks.
+  constexpr int NKA = D == 64 ? 4 : 8;
   const int krow = row_key(l32);
-  const int ksw = kswz(krow);
-  int kaddr[4];
+  const int ksw = kswz<D>(krow);
+  int kaddr[NKA];
 #pragma unroll
-  for (int bq = 0; bq < 4; ++bq)
+  for (int bq = 0; bq < NKA; ++bq)
     kaddr[bq] = krow * (D * 2) + 32 * (bq ^ (ksw >> 1)) + 16 * (hsel ^ (ksw & 1));
-  // V^T operand: row d = 32 dt + l32 (vswz does not depend on dt); chunk
-  // kc = 4 t2 + 2 c + hsel for MFMA (t2, c).
-  int vaddr[NT2 * 2];
-  {
-    const int vs = vswz(l32);
+  // V operand (A of O^T += V^T P^T, from V stored row-major in LDS): for MFMA
+  // (t2, c) the lane of d row d0 + i in 16-lane group gi (d0 = 32 dt + 16
+  // (gi & 1), lane half H = gi >> 1) needs V[k + t][d0 + i], t = 0..7, with
+  // k = 32 t2 + 16 c + 8 H.  Two transposing reads give keys k..k+3 and
+  // k+4..k+7: source lane s of the group addresses the 4 values
+  // V[k + 4 half + (s >> 2)][d0 + 4 (s & 3) .. + 3].  The key row offset and the
+  // swizzle depend only on the lane and on half, the chunk on dt; t2 and c add
+  // whole rows.
+  const int gi = lane >> 4, li = lane & 15;
+  int vtr[2][DT];
 #pragma unroll
-    for (int t2 = 0; t2 < NT2; ++t2)
+  for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) vaddr[2 * t2 + c] = l32 * (BN * 2) + 16 * ((4 * t2 + 2 * c + hsel) ^ vs);
-  }
+    for (int dt = 0; dt < DT; ++dt) {
+      const int key = 8 * (gi >> 1) + 4 * half + (li >> 2);
+      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
+      vtr[half][dt] = key * (D * 2) + 16 * ((dcol >> 3) ^ vswz<D>(key)) + 2 * (dcol & 7);
+    }
 
-  // ---- K straight into LDS: wave wg of the group, instruction i fills 1 KiB
-  // slice 4 i + wg; lane l writes slot l = (row l / DCH of the slice, stored
-  // chunk l % DCH), so it fetches global chunk (l % DCH) ^ kswz(row).  Lane
-  // offsets are loop-invariant bytes (token strides are checked on the host).
-  uint32_t kofs_ld[KINST];
+  // ---- K and V straight into LDS by DMA: wave wg of the group, instruction i
+  // fills 1 KiB slice 4 i + wg; lane l writes slot l = (row l / DCH of the
+  // slice, stored chunk l % DCH), so it fetches global chunk (l % DCH) ^
+  // swizzle(row).  Lane offsets are loop-invariant bytes (token strides are
+  // checked on the host).
+  uint32_t kofs_ld[KINST], vofs_ld[KINST];
 #pragma unroll
   for (int i = 0; i < KINST; ++i) {
     const int row = (4 * i + wg) * ROWS_PER_KB + lane / DCH;
-    kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ (kswz(row) & (DCH - 1)))) * 2u;
+    kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    vofs_ld[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ vswz<D>(row))) * 2u;
   }
-  auto issue_k = [&](int n, int stage) {
-    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
-    uint8_t* dst = gsm + stage * KTILE;
+  auto issue = [&](int n, uint8_t* kdst, uint8_t* vdst) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
 #pragma unroll
-    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rs, dst + (4 * i + wg) * 1024, kofs_ld[i]);
-  };
-
-  // ---- V staged in registers: unit un -> (kq, dc) with dc = a + 4 dc_hi,
-  // kq = b + 4 kq_hi, a = un & 3, b = (un >> 2) & 3, c = un >> 4, dc_hi = c % G4,
-  // kq_hi = c / G4.  One wave instruction covers whole rows (coalesced) and each
-  // 16-lane group's transposed 8-byte writes hit 16 distinct bank slots.
-  int vkq[VLD], vdc[VLD];
-  uint32_t vofs[VLD];
+    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rk, kdst + (4 * i + wg) * 1024, kofs_ld[i]);
 #pragma unroll
-  for (int i = 0; i < VLD; ++i) {
-    const int un = gtid + i * 256;
-    const int cc = un >> 4;
-    vdc[i] = (un & 3) + 4 * (cc % G4);
-    vkq[i] = ((un >> 2) & 3) + 4 * (cc / G4);
-    vofs[i] = (uint32_t)(4 * vkq[i] * p.v_ss + 8 * vdc[i]) * 2u;
-  }
-  const uint32_t vrow_bytes = (uint32_t)p.v_ss * 2u;
-  u32x4_t vst[VLD][4];
-  auto issue_v = [&](int n) {
-    __amdgpu_buffer_rsrc_t rs = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
-#pragma unroll
-    for (int i = 0; i < VLD; ++i)
-      if (VUNITS % 256 == 0 || gtid + i * 256 < VUNITS)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vst[i][r] = buffer_load16(rs, vofs[i] + r * vrow_bytes);
-  };
-  auto store_v = [&](int stage) {
-    uint8_t* vs_ = gsm + 2 * KTILE + stage * VTILE;
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      if (VUNITS % 256 == 0 || gtid + i * 256 < VUNITS) {
-        const int kq = vkq[i];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int d = 8 * vdc[i] + t;
-          *(u32x2_t*)(vs_ + d * (BN * 2) + 16 * ((kq >> 1) ^ vswz(d)) + 8 * (kq & 1)) =
-              column4(vst[i][0], vst[i][1], vst[i][2], vst[i][3], t);
-        }
-      }
-    }
+    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rv, vdst + (4 * i + wg) * 1024, vofs_ld[i]);
   };
 
   f32x16_t oacc[DT];
@@ -302,9 +294,43 @@ prefill_kernel(const FwdParams p) {
   float m_ref = kNegInf;  // reference max (log2 domain) of this lane's row
   float l_run = 0.f;      // this lane's share of the row sum, relative to m_ref
 
+  // p = 2^(score - base) for the block, rounded into the P^T operand (the B
+  // operand of MFMA (t2, c) is registers 8c .. 8c+7 of tile t2).  Returns this
+  // lane's fp32 sum of p: the row sum, and so the LSE, is taken before rounding
+  // (a sum of the 16-bit values can be off by 2^-9 relative, too much for LSE).
+  auto exps = [&](const f32x16_t (&s)[NT2], u32x4_t (&pf)[NT2][2], float base) {
+    float psum = 0.f;
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float x0, x1;
+        if constexpr (SOFTCAP) {
+          // masked scores are -inf and must stay so (tanh(-inf) would give -1)
+          const float a0 = s[t2][r], a1 = s[t2][r + 1];
+          x0 = a0 == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(a0 * p.cap_in) - base;
+          x1 = a1 == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(a1 * p.cap_in) - base;
+        } else {
+          x0 = __builtin_fmaf(s[t2][r], p.scale_log2, -base);
+          x1 = __builtin_fmaf(s[t2][r + 1], p.scale_log2, -base);
+        }
+        x0 = fast_exp2(x0);
+        x1 = fast_exp2(x1);
+        pf[t2][r >> 3][(r & 7) >> 1] = E::pack2(x0, x1);
+        psum += x0 + x1;
+      }
+    return psum;
+  };
+
   // ---- one KV block: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
-  auto block = [&](int n, int stage) {
-    const uint8_t* ks_ = gsm + stage * KTILE;
+  // The exponentials are taken against the current reference right away; the
+  // block's row max is needed only when a lane's block sum exceeds 2^tau (some
+  // p may exceed 2^tau, or overflowed) or a row has no reference yet.  Then the
+  // reference moves lazily (only when the block max exceeds it by more than
+  // 2^tau, never while the block is fully masked), O and l are rescaled and the
+  // exponentials recomputed.  Exact in all cases: O and l always share the
+  // reference, and every p stays <= 2^tau.
+  auto block = [&](int n, const uint8_t* __restrict__ ks_, const uint8_t* __restrict__ vs_) {
     f32x16_t s[NT2];
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2) s[t2] = f32x16_t{};
@@ -313,7 +339,7 @@ prefill_kernel(const FwdParams p) {
 #pragma unroll
       for (int t2 = 0; t2 < NT2; ++t2) {
         const u32x4_t a =
-            *(const u32x4_t*)(ks_ + kaddr[ks & 3] + 128 * (ks >> 2) + t2 * 32 * (D * 2));
+            *(const u32x4_t*)(ks_ + kaddr[ks % NKA] + 32 * NKA * (ks / NKA) + t2 * 32 * (D * 2));
         s[t2] = E::mfma32x32x16(a, qf[ks], s[t2]);
       }
 
@@ -331,91 +357,92 @@ prefill_kernel(const FwdParams p) {
           if (kk > hi || kk < lo) s[t2][r] = kNegInf;
         }
     }
-    float mraw = s[0][0];
-#pragma unroll
-    for (int t2 = 0; t2 < NT2; ++t2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[t2][r]);
-    mraw = halves_max(mraw);
-    float m_blk;
-    if constexpr (SOFTCAP)
-      m_blk = mraw == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(mraw * p.cap_in);
-    else
-      m_blk = mraw * p.scale_log2;
-    // Lazy rescale: move the reference only when the block max exceeds it by
-    // more than 2^tau (never while the block is fully masked: m_blk = -inf).
-    const bool need = m_blk > m_ref + kLazyTau;
-    const float m_new = need ? m_blk : m_ref;
-    const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
-    if (__ballot(need && m_ref != kNegInf) != 0) {
-      // rare: a row that already holds mass moves its reference
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-    }
-    l_run *= alpha;
-    m_ref = m_new;
-    const float base = m_ref == kNegInf ? 0.f : m_ref;
-    float psum = 0.f;
     u32x4_t pf[NT2][2];
-#pragma unroll
-    for (int t2 = 0; t2 < NT2; ++t2)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float x0, x1;
-        if constexpr (SOFTCAP) {
-          // masked scores are -inf and must stay so (tanh(-inf) would give -1)
-          const float a0 = s[t2][r], a1 = s[t2][r + 1];
-          x0 = a0 == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(a0 * p.cap_in) - base;
-          x1 = a1 == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(a1 * p.cap_in) - base;
-        } else {
-          x0 = __builtin_fmaf(s[t2][r], p.scale_log2, -base);
-          x1 = __builtin_fmaf(s[t2][r + 1], p.scale_log2, -base);
-        }
-        x0 = fast_exp2(x0);
-        x1 = fast_exp2(x1);
-        psum += x0 + x1;
-        // P^T fragment: the B operand of MFMA (t2, c) is registers 8c .. 8c+7 of tile t2.
-        pf[t2][r >> 3][(r & 7) >> 1] = E::pack2(x0, x1);
-      }
-    l_run += psum;
-
-    const uint8_t* vs_ = gsm + 2 * KTILE + stage * VTILE;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    float psum = 0.f;
+    bool ok = false;
+    if (__ballot(m_ref == kNegInf) == 0) {
+      psum = exps(s, pf, m_ref);
+      ok = __ballot(!(psum <= kSumCap)) == 0;  // !(<=) also catches inf and NaN
+    }
+    if (!ok) {
+      float mraw = s[0][0];
 #pragma unroll
       for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u32x4_t a = *(const u32x4_t*)(vs_ + vaddr[2 * t2 + c] + dt * 32 * (BN * 2));
+        for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[t2][r]);
+      mraw = halves_max(mraw);
+      float m_blk;
+      if constexpr (SOFTCAP)
+        m_blk = mraw == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(mraw * p.cap_in);
+      else
+        m_blk = mraw * p.scale_log2;
+      const bool need = m_blk > m_ref + kLazyTau;
+      const float m_new = need ? m_blk : m_ref;
+      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
+      if (__ballot(need && m_ref != kNegInf) != 0) {
+        // a row that already holds mass moves its reference
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      }
+      l_run *= alpha;
+      m_ref = m_new;
+      psum = exps(s, pf, m_ref == kNegInf ? 0.f : m_ref);
+    }
+    l_run += psum;
+
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rows = (32 * t2 + 16 * c) * (D * 2);
+          u32x4_t a;
+          const u32x2_t lo = lds_read_tr16(vs_ + vtr[0][dt] + rows);
+          const u32x2_t hi = lds_read_tr16(vs_ + vtr[1][dt] + rows);
+          a[0] = lo[0];
+          a[1] = lo[1];
+          a[2] = hi[0];
+          a[3] = hi[1];
           oacc[dt] = E::mfma32x32x16(a, pf[t2][c], oacc[dt]);
         }
   };
 
   // ---- main loop: step i, group g works on block n_lo + NG i + g; every group
   // runs the same number of steps so one work-group barrier per step suffices.
+  // K(n) and V(n) live in stage i & 1.  A step starts the DMA of the group's
+  // next block into the other stage and computes block n.  The stages never
+  // overlap; restrict tells the compiler so, which lets the operand reads of
+  // this step proceed while the DMA into the other stage is in flight (without
+  // it every LDS read waits for all outstanding DMA).
+  uint8_t* const k0 = gsm;
+  uint8_t* const k1 = gsm + KTILE;
+  uint8_t* const v0 = gsm + 2 * KTILE;
+  uint8_t* const v1 = gsm + 2 * KTILE + VTILE;
+  auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                  uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
+    if (n + NG < n_hi) issue(n + NG, kn, vn);
+    if (n < n_hi) block(n, kc, vc);
+  };
   const int nblk = n_hi - n_lo;
   const int steps = (nblk + NG - 1) / NG;
-  if (steps > 0) {
-    const int n0 = n_lo + grp;
-    if (n0 < n_hi) {
-      issue_k(n0, 0);
-      issue_v(n0);
-      wait_vmem_all();
-      store_v(0);
-    }
-  }
-  for (int i = 0; i < steps; ++i) {
+  if (n_lo + grp < n_hi) issue(n_lo + grp, k0, v0);
+  // Unrolled by two so each call sees fixed stages.  Before each step: block
+  // n has landed in LDS and every wave is done with the previous step.
+  int i = 0;
+  for (; i + 1 < steps; i += 2) {
     const int n = n_lo + NG * i + grp;
-    const int nn = n + NG;  // this group's next block
-    // K(n) has landed in LDS and V^T(n) is written; every wave is done with step i-1.
     wait_vmem_all();
     __syncthreads();
-    if (nn < n_hi) {
-      issue_k(nn, (i + 1) & 1);
-      issue_v(nn);
-    }
-    if (n < n_hi) block(n, i & 1);
-    if (nn < n_hi) store_v((i + 1) & 1);
+    step(k0, v0, k1, v1, n);
+    wait_vmem_all();
+    __syncthreads();
+    step(k1, v1, k0, v0, n + NG);
+  }
+  if (i < steps) {
+    wait_vmem_all();
+    __syncthreads();
+    step(k0, v0, k1, v1, n_lo + NG * i + grp);
   }
 
   // ---- merge the groups: group 1 hands (m, l, O) to group 0 through LDS.
