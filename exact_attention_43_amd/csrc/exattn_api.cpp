@@ -84,6 +84,18 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     p.group = pl.group;
     p.n_qt = pl.n_qt;
     p.xcd_group = pl.xcd_group;
+    // When the key range depends on the row (causal or windowed) and the grid
+    // is about one work group per CU, the launch lasts as long as its heaviest
+    // work group, so light and heavy tiles are paired; with more work groups
+    // the dispatch order already balances the CUs and pairing would only idle
+    // waves.
+    p.pair_tiles = 0;
+    if (pl.head_dim <= 128 && (pl.wr >= 0 || pl.wl >= 0)) {
+      int cus = 1;
+      st = device_cus(&cus);
+      if (st != EXATTN_OK) return st;
+      p.pair_tiles = pl.grid <= cus ? 1 : 0;
+    }
     p.scale_log2 = pl.scale_log2;
     p.cap_in = pl.cap_in;
     p.cap_out_log2 = pl.cap_out_log2;

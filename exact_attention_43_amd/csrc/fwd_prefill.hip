@@ -149,7 +149,7 @@ prefill_kernel(const FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;   // KV-block group
-  const int wg = wave & 3;     // wave within the group: query rows 32 wg .. 32 wg + 31
+  const int wg = wave & 3;     // wave within the group
   const int gtid = tid & 255;  // thread index within the group
   const int hsel = lane >> 5;  // which 32-lane half
   const int l32 = lane & 31;
@@ -194,8 +194,22 @@ prefill_kernel(const FwdParams p) {
     voff = (int64_t)b * p.v_sb;
     lseoff = (int64_t)b * p.lse_sb;
   }
-  const int q0 = qt * kBM;
-  if (q0 >= sq) return;  // uniform across the work group
+  // ---- the work group's 128 rows are two 64-row tiles: 2 qt and 2 qt + 1,
+  // or, when pairing (two groups), tiles j and n64 - 1 - j, a light and a heavy
+  // one under a causal mask, so every work group carries about the same work.
+  // Paired, group 0's waves 0-1 and group 1's waves 2-3 take tile j and the
+  // others tile n64 - 1 - j, so each SIMD (waves w and w + 4) holds one wave of
+  // each tile; otherwise waves 0-1 of each group take the first tile.
+  const int n64 = (sq + 63) / 64;
+  if (2 * qt >= n64) return;  // uniform across the work group
+  const bool paired = NG > 1 && p.pair_tiles != 0;
+  const int tile_a = paired ? qt : 2 * qt;
+  const int tile_b = paired ? n64 - 1 - qt : 2 * qt + 1;
+  const bool b_valid = tile_b > tile_a && tile_b < n64;  // an odd tile count leaves one alone
+  const bool my_a = paired ? (wg >> 1) == grp : wg < 2;
+  const bool my_valid = my_a || b_valid;
+  const int q0 = 64 * (my_a ? tile_a : tile_b);   // first row of this wave's tile
+  const int q_last = min(q0 + 64, sq) - 1;
 
   const uint16_t* qg = p.q + qoff + (int64_t)h * p.q_sh;
   const uint16_t* kg = p.k + koff + (int64_t)hk * p.k_sh;
@@ -203,22 +217,36 @@ prefill_kernel(const FwdParams p) {
   uint16_t* og = p.o + ooff + (int64_t)h * p.o_sh;
   float* lseg = p.lse != nullptr ? p.lse + lseoff + (int64_t)h * p.lse_sh : nullptr;
 
-  // ---- visible key range of the whole tile (bottom-right aligned).
+  // ---- visible key blocks [lo, hi) of a 64-row tile (bottom-right aligned);
+  // the groups walk the union over both tiles, a wave computes its own tile's.
   const int off = sk - sq;
-  const int q_last = min(q0 + kBM, sq) - 1;
-  int kmin = 0, kmax = sk - 1;
-  if (p.wl >= 0) kmin = max(0, q0 + off - p.wl);
-  if (p.wr >= 0) kmax = min(kmax, q_last + off + p.wr);
-  int n_lo = 0, n_hi = 0;
-  if (kmax >= kmin) {
-    n_lo = kmin / BN;
-    n_hi = kmax / BN + 1;
+  auto block_range = [&](int tile, int& lo, int& hi) {
+    const int t0 = 64 * tile, t1 = min(t0 + 64, sq) - 1;
+    int kmin = 0, kmax = sk - 1;
+    if (p.wl >= 0) kmin = max(0, t0 + off - p.wl);
+    if (p.wr >= 0) kmax = min(kmax, t1 + off + p.wr);
+    lo = 0;
+    hi = 0;
+    if (kmax >= kmin) {
+      lo = kmin / BN;
+      hi = kmax / BN + 1;
+    }
+  };
+  int a_lo, a_hi, b_lo = 0, b_hi = 0;
+  block_range(tile_a, a_lo, a_hi);
+  if (b_valid) block_range(tile_b, b_lo, b_hi);
+  int n_lo = a_lo, n_hi = a_hi;
+  if (b_valid && b_hi > b_lo) {
+    n_lo = a_hi > a_lo ? min(a_lo, b_lo) : b_lo;
+    n_hi = max(a_hi, b_hi);
   }
+  const int w_lo = my_a ? a_lo : b_lo;                    // this wave's blocks
+  const int w_hi = my_valid ? (my_a ? a_hi : b_hi) : 0;
 
   // ---- Q^T fragments: lane holds Q[row][16 ks + 8 hsel .. +7] for every ks.
-  const int qrow = q0 + wg * 32 + l32;
+  const int qrow = q0 + 32 * (wg & 1) + l32;
   u32x4_t qf[KS];
-  if (qrow < sq) {
+  if (my_valid && qrow < sq) {
     const uint16_t* qp = qg + (int64_t)qrow * p.q_ss + 8 * hsel;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
@@ -422,7 +450,7 @@ prefill_kernel(const FwdParams p) {
   auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                   uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
     if (n + NG < n_hi) issue(n + NG, kn, vn);
-    if (n < n_hi) block(n, kc, vc);
+    if (n >= w_lo && n < w_hi) block(n, kc, vc);  // uniform per wave
   };
   const int nblk = n_hi - n_lo;
   const int steps = (nblk + NG - 1) / NG;
@@ -451,13 +479,14 @@ prefill_kernel(const FwdParams p) {
     __syncthreads();  // tile buffers are free
     float* xm = reinterpret_cast<float*>(smem);  // [wave in group][2][lane]: m, l
     float* xo = xm + 2 * 4 * 64;                  // [wave in group][reg][lane]: O^T
-    if (grp == 1) {
-      xm[(wg * 2 + 0) * 64 + lane] = m_ref;
-      xm[(wg * 2 + 1) * 64 + lane] = l_tot;
+    if (grp == 1) {  // group 0's wave `slot` holds the same rows
+      const int slot = paired ? wg ^ 2 : wg;
+      xm[(slot * 2 + 0) * 64 + lane] = m_ref;
+      xm[(slot * 2 + 1) * 64 + lane] = l_tot;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[((wg * DT + dt) * 16 + r) * 64 + lane] = oacc[dt][r];
+        for (int r = 0; r < 16; ++r) xo[((slot * DT + dt) * 16 + r) * 64 + lane] = oacc[dt][r];
     }
     __syncthreads();
     if (grp != 0) return;
@@ -478,7 +507,7 @@ prefill_kernel(const FwdParams p) {
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; empty rows: 0 and -inf.
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < sq) {
+  if (my_valid && qrow < sq) {
     uint16_t* op = og + (int64_t)qrow * p.o_ss;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)

@@ -25,6 +25,7 @@ struct FwdParams {
   int32_t h_q, h_kv, group;
   int32_t n_qt;        // query tiles per (batch, head)
   int32_t xcd_group;   // 1: co-locate the query heads of one KV head on one XCD
+  int32_t pair_tiles;  // 1: a work group takes 64-row tiles j and n - 1 - j (about one work group per CU)
   float scale_log2;    // softmax_scale * log2(e)
   float cap_in;        // softmax_scale / softcap
   float cap_out_log2;  // softcap * log2(e)
