@@ -84,18 +84,18 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     p.group = pl.group;
     p.n_qt = pl.n_qt;
     p.xcd_group = pl.xcd_group;
-    // When the key range depends on the row (causal or windowed) and the grid
-    // is about one work group per CU, the launch lasts as long as its heaviest
-    // work group, so light and heavy tiles are paired; with more work groups
-    // the dispatch order already balances the CUs and pairing would only idle
-    // waves.
-    p.pair_tiles = 0;
-    if (pl.head_dim <= 128 && (pl.wr >= 0 || pl.wl >= 0)) {
-      int cus = 1;
-      st = device_cus(&cus);
-      if (st != EXATTN_OK) return st;
-      p.pair_tiles = pl.grid <= cus ? 1 : 0;
-    }
+    // Launch shape.  With at least two work groups per CU, one-group work
+    // groups (two per CU, unsynchronised) are faster; with fewer, two groups
+    // split each tile's KV blocks.  When the key range depends on the row
+    // (causal or windowed) and the grid is about one work group per CU, the
+    // launch lasts as long as its heaviest work group, so light and heavy tiles
+    // are paired; with more work groups the dispatch order already balances the
+    // CUs and pairing would only idle waves.
+    int cus = 1;
+    st = device_cus(&cus);
+    if (st != EXATTN_OK) return st;
+    const int groups = pl.head_dim == 256 || pl.grid >= 2 * cus ? 1 : 2;
+    p.pair_tiles = groups == 2 && (pl.wr >= 0 || pl.wl >= 0) && pl.grid <= cus ? 1 : 0;
     p.scale_log2 = pl.scale_log2;
     p.cap_in = pl.cap_in;
     p.cap_out_log2 = pl.cap_out_log2;
@@ -104,11 +104,11 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     p.q_sign = pl.q_sign;
     char buf[256];
     snprintf(buf, sizeof buf,
-             "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d x256",
+             "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d groups=%d pair=%d",
              pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, (int)pl.varlen, a->batch,
-             pl.s_q, pl.s_k, a->heads_q, a->heads_kv, pl.wl, pl.wr, pl.grid);
+             pl.s_q, pl.s_k, a->heads_q, a->heads_kv, pl.wl, pl.wr, pl.grid, groups, p.pair_tiles);
     debug_once(buf, buf);
-    hipError_t e = launch_prefill(p, pl.bf16, pl.head_dim, pl.softcap, pl.grid,
+    hipError_t e = launch_prefill(p, pl.bf16, pl.head_dim, pl.softcap, pl.grid, groups,
                                   static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
     return EXATTN_OK;

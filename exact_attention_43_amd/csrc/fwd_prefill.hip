@@ -54,12 +54,13 @@ constexpr int kBM = 128;          // query rows per work group
 constexpr float kLazyTau = 8.0f;  // rescale only when the row max grows by > 2^8
 constexpr float kSumCap = 256.0f;  // 2^tau: a block sum below it means every p <= 2^tau
 
-// Groups per work group and keys per KV block for a head dimension (LDS: NG
-// groups x 2 stages x (K + V^T) tiles of BN x D bf16 = NG * 4 * BN * D bytes).
-template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int NG = 2, BN = 64; };
-template <> struct Cfg<128> { static constexpr int NG = 2, BN = 64; };
-template <> struct Cfg<256> { static constexpr int NG = 1, BN = 64; };
+// Keys per KV block.  The number of groups per work group (NG, a template
+// parameter) is chosen per launch: two groups (8 waves, 128 KiB of LDS, one
+// work group per CU) split one tile's KV blocks when the grid is small; one
+// group (4 waves, 64 KiB, two work groups per CU) when there are at least two
+// work groups per CU, which then run unsynchronised (measured faster there).
+// d = 256 always takes one group (its tiles need 128 KiB).
+template <int D> struct Cfg { static constexpr int BN = 64; };
 
 // K tile: row `key` is D*2 bytes; 16-byte chunk c is stored at c ^ kswz(key).
 // ds_read_b128 serves 16 lanes per clock (256 bytes over the 64 banks), and the
@@ -123,11 +124,10 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t rs, uint
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <bool BF16, int D, bool SOFTCAP>
-__global__ void __launch_bounds__(256 * Cfg<D>::NG)
+template <bool BF16, int D, bool SOFTCAP, int NG>
+__global__ void __launch_bounds__(256 * NG)
 prefill_kernel(const FwdParams p) {
   using E = Elem<BF16>;
-  constexpr int NG = Cfg<D>::NG;
   constexpr int BN = Cfg<D>::BN;
   constexpr int NT2 = BN / 32;                 // 32-key MFMA tiles per KV block
   constexpr int DCH = D / 8;                   // 16-byte chunks per row
@@ -523,22 +523,27 @@ prefill_kernel(const FwdParams p) {
   }
 }
 
-template <bool BF16, int D>
-hipError_t launch_d(const FwdParams& p, bool softcap, int grid, hipStream_t stream) {
-  const dim3 block(256 * Cfg<D>::NG);
+template <bool BF16, int D, int NG>
+hipError_t launch_g(const FwdParams& p, bool softcap, int grid, hipStream_t stream) {
+  const dim3 block(256 * NG);
   if (softcap)
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, true>), dim3(grid), block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<BF16, D, true, NG>), dim3(grid), block, 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, false>), dim3(grid), block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<BF16, D, false, NG>), dim3(grid), block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <bool BF16>
-hipError_t launch_t(const FwdParams& p, int head_dim, bool softcap, int grid, hipStream_t stream) {
+hipError_t launch_t(const FwdParams& p, int head_dim, bool softcap, int grid, int groups,
+                    hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<BF16, 64>(p, softcap, grid, stream);
-    case 128: return launch_d<BF16, 128>(p, softcap, grid, stream);
-    case 256: return launch_d<BF16, 256>(p, softcap, grid, stream);
+    case 64:
+      return groups == 1 ? launch_g<BF16, 64, 1>(p, softcap, grid, stream)
+                         : launch_g<BF16, 64, 2>(p, softcap, grid, stream);
+    case 128:
+      return groups == 1 ? launch_g<BF16, 128, 1>(p, softcap, grid, stream)
+                         : launch_g<BF16, 128, 2>(p, softcap, grid, stream);
+    case 256: return launch_g<BF16, 256, 1>(p, softcap, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -548,9 +553,9 @@ hipError_t launch_t(const FwdParams& p, int head_dim, bool softcap, int grid, hi
 int prefill_rows_per_tile() { return kBM; }
 
 hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,
-                          hipStream_t stream) {
-  return bf16 ? launch_t<true>(p, head_dim, softcap, grid, stream)
-              : launch_t<false>(p, head_dim, softcap, grid, stream);
+                          int groups, hipStream_t stream) {
+  return bf16 ? launch_t<true>(p, head_dim, softcap, grid, groups, stream)
+              : launch_t<false>(p, head_dim, softcap, grid, groups, stream);
 }
 
 }  // namespace exattn

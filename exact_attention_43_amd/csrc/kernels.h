@@ -25,7 +25,7 @@ struct FwdParams {
   int32_t h_q, h_kv, group;
   int32_t n_qt;        // query tiles per (batch, head)
   int32_t xcd_group;   // 1: co-locate the query heads of one KV head on one XCD
-  int32_t pair_tiles;  // 1: a work group takes 64-row tiles j and n - 1 - j (about one work group per CU)
+  int32_t pair_tiles;  // 1: a two-group work group takes 64-row tiles j and n - 1 - j
   float scale_log2;    // softmax_scale * log2(e)
   float cap_in;        // softmax_scale / softcap
   float cap_out_log2;  // softcap * log2(e)
@@ -54,8 +54,9 @@ struct DecParams {
 };
 
 int prefill_rows_per_tile();
+// groups: 1 or 2 groups of 4 waves per work group (d = 256 always uses 1).
 hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,
-                          hipStream_t stream);
+                          int groups, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softcap,
                          hipStream_t stream);
 
