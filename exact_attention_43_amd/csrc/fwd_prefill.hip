@@ -258,11 +258,6 @@ prefill_kernel(const FwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] ^= u32x4_t{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
   }
-  // Consume Q here: the compiler then waits for these loads before the loop.
-  // Otherwise it cannot tell that the loop's own waits covered them and waits
-  // inside every step for all newer loads, the next block's prefetch included.
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
 
   // ---- loop-invariant LDS addresses.
   // K operand: tile t2 row key = 32 t2 + row_key(l32); chunk 2 ks + hsel lives
@@ -454,7 +449,19 @@ prefill_kernel(const FwdParams p) {
   };
   const int nblk = n_hi - n_lo;
   const int steps = (nblk + NG - 1) / NG;
-  if (n_lo + grp < n_hi) issue(n_lo + grp, k0, v0);
+  // Consume Q after the first block's DMA is on its way (in each branch, so
+  // that each path waits only for the Q loads): the compiler then waits for
+  // them before the loop.  Otherwise it cannot tell that the loop's own waits
+  // covered them and waits inside every step for all newer loads, the next
+  // block's prefetch included.
+  if (n_lo + grp < n_hi) {
+    issue(n_lo + grp, k0, v0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
   // Unrolled by two so each call sees fixed stages.  Before each step: block
   // n has landed in LDS and every wave is done with the previous step.
   int i = 0;
