@@ -122,6 +122,19 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t rs, uint
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, 0));
 }
 
+// Scores of keys outside [lo, hi] (relative to the block's first key plus
+// 8 hsel) -> -inf.  Register r of tile t2 holds key 32 t2 + 16 (r / 8) + r % 8.
+template <int NT2>
+__device__ __forceinline__ void mask_keys(f32x16_t (&s)[NT2], int hi, int lo) {
+#pragma unroll
+  for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 32 * t2 + 16 * (r >> 3) + (r & 7);
+      if (kk > hi || kk < lo) s[t2][r] = kNegInf;
+    }
+}
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <bool BF16, int D, bool SOFTCAP, int NG>
@@ -140,8 +153,6 @@ prefill_kernel(const FwdParams p) {
   constexpr int KINST = KTILE / 4096;          // direct loads per wave per K tile
   static_assert(KINST >= 1 && KTILE % 4096 == 0, "tile/thread mismatch");
   static_assert(NG * GROUP_LDS <= 160 * 1024, "LDS budget");
-  // the end-of-loop merge reuses the tile buffers: 4 waves x (16 DT + 2) floats per lane
-  static_assert(NG == 1 || NG * GROUP_LDS >= 4 * 64 * (16 * DT + 2) * 4, "merge buffer");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NG * GROUP_LDS];
 
@@ -302,11 +313,13 @@ prefill_kernel(const FwdParams p) {
     kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
     vofs_ld[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ vswz<D>(row))) * 2u;
   }
-  auto issue = [&](int n, uint8_t* kdst, uint8_t* vdst) {
+  auto issue_k = [&](int n, uint8_t* kdst) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
 #pragma unroll
     for (int i = 0; i < KINST; ++i) buffer_load_lds16(rk, kdst + (4 * i + wg) * 1024, kofs_ld[i]);
+  };
+  auto issue_v = [&](int n, uint8_t* vdst) {
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
 #pragma unroll
     for (int i = 0; i < KINST; ++i) buffer_load_lds16(rv, vdst + (4 * i + wg) * 1024, vofs_ld[i]);
   };
@@ -345,74 +358,62 @@ prefill_kernel(const FwdParams p) {
     return psum;
   };
 
-  // ---- one KV block: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
-  // The exponentials are taken against the current reference right away; the
-  // block's row max is needed only when a lane's block sum exceeds 2^tau (some
-  // p may exceed 2^tau, or overflowed) or a row has no reference yet.  Then the
-  // reference moves lazily (only when the block max exceeds it by more than
-  // 2^tau, never while the block is fully masked), O and l are rescaled and the
-  // exponentials recomputed.  Exact in all cases: O and l always share the
-  // reference, and every p stays <= 2^tau.
-  auto block = [&](int n, const uint8_t* __restrict__ ks_, const uint8_t* __restrict__ vs_) {
-    f32x16_t s[NT2];
+  // ---- the pieces of one KV block: S^T = K Q^T, the mask, the online softmax
+  // and O^T += V^T P^T.
+  // K operand of MFMA (ks, t2): keys 32 t2 + row_key(lane), head dims 16 ks + 8 hsel + 0..7.
+  auto k_operand = [&](const uint8_t* __restrict__ ks_, int ks, int t2) {
+    return *(const u32x4_t*)(ks_ + kaddr[ks % NKA] + 32 * NKA * (ks / NKA) + t2 * 32 * (D * 2));
+  };
+  auto qk = [&](const uint8_t* __restrict__ ks_, f32x16_t (&s)[NT2]) {
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2) s[t2] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int t2 = 0; t2 < NT2; ++t2) {
-        const u32x4_t a =
-            *(const u32x4_t*)(ks_ + kaddr[ks % NKA] + 32 * NKA * (ks / NKA) + t2 * 32 * (D * 2));
-        s[t2] = E::mfma32x32x16(a, qf[ks], s[t2]);
-      }
-
-    const int kb = n * BN;
-    const bool need_mask = (kb + BN > sk) || (p.wr >= 0 && kb + BN - 1 > q0 + off + p.wr) ||
-                           (p.wl >= 0 && kb < q_last + off - p.wl);
-    if (need_mask) {
-      const int hi = (p.wr >= 0 ? min(sk - 1, qrow + off + p.wr) : sk - 1) - kb - 8 * hsel;
-      const int lo = (p.wl >= 0 ? qrow + off - p.wl : -0x3fffffff) - kb - 8 * hsel;
+      for (int t2 = 0; t2 < NT2; ++t2) s[t2] = E::mfma32x32x16(k_operand(ks_, ks, t2), qf[ks], s[t2]);
+  };
+  // scores outside the causal / window bounds or past the last key -> -inf
+  // (only blocks that straddle a bound carry any)
+  // Keys <= full_r and >= full_l are visible to every row of the wave's tile,
+  // so only blocks that reach past them carry a mask; this lane's row sees
+  // keys mlo + 8 hsel .. mhi + 8 hsel.
+  const int full_r = p.wr >= 0 ? min(sk - 1, q0 + off + p.wr) : sk - 1;
+  const int full_l = p.wl >= 0 ? q_last + off - p.wl : -0x3fffffff;
+  const int mhi = (p.wr >= 0 ? min(sk - 1, qrow + off + p.wr) : sk - 1) - 8 * hsel;
+  const int mlo = (p.wl >= 0 ? qrow + off - p.wl : -0x3fffffff) - 8 * hsel;
+  // The exponentials are first taken against the current reference; the
+  // block's row max is needed only when a lane's block sum exceeds 2^tau (some
+  // p may exceed 2^tau, or overflowed) or a row has no reference yet (then the
+  // sum is inf or NaN).  Then the reference moves lazily (only when the block
+  // max exceeds it by more than 2^tau, never while the block is fully masked),
+  // O and l are rescaled and the exponentials recomputed.  Exact in all cases:
+  // O and l always share the reference, and every p stays <= 2^tau.
+  auto slow = [&](const f32x16_t (&s)[NT2], u32x4_t (&pf)[NT2][2]) {
+    float mraw = s[0][0];
 #pragma unroll
-      for (int t2 = 0; t2 < NT2; ++t2)
+    for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * t2 + 16 * (r >> 3) + (r & 7);  // key - kb - 8 hsel
-          if (kk > hi || kk < lo) s[t2][r] = kNegInf;
-        }
+      for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[t2][r]);
+    mraw = halves_max(mraw);
+    float m_blk;
+    if constexpr (SOFTCAP)
+      m_blk = mraw == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(mraw * p.cap_in);
+    else
+      m_blk = mraw * p.scale_log2;
+    const bool need = m_blk > m_ref + kLazyTau;
+    const float m_new = need ? m_blk : m_ref;
+    const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
+    if (__ballot(need && m_ref != kNegInf) != 0) {
+      // a row that already holds mass moves its reference
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
-    u32x4_t pf[NT2][2];
-    float psum = 0.f;
-    bool ok = false;
-    if (__ballot(m_ref == kNegInf) == 0) {
-      psum = exps(s, pf, m_ref);
-      ok = __ballot(!(psum <= kSumCap)) == 0;  // !(<=) also catches inf and NaN
-    }
-    if (!ok) {
-      float mraw = s[0][0];
-#pragma unroll
-      for (int t2 = 0; t2 < NT2; ++t2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[t2][r]);
-      mraw = halves_max(mraw);
-      float m_blk;
-      if constexpr (SOFTCAP)
-        m_blk = mraw == kNegInf ? kNegInf : p.cap_out_log2 * tanh_exp2(mraw * p.cap_in);
-      else
-        m_blk = mraw * p.scale_log2;
-      const bool need = m_blk > m_ref + kLazyTau;
-      const float m_new = need ? m_blk : m_ref;
-      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
-      if (__ballot(need && m_ref != kNegInf) != 0) {
-        // a row that already holds mass moves its reference
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      }
-      l_run *= alpha;
-      m_ref = m_new;
-      psum = exps(s, pf, m_ref == kNegInf ? 0.f : m_ref);
-    }
-    l_run += psum;
-
+    l_run *= alpha;
+    m_ref = m_new;
+    return exps(s, pf, m_ref == kNegInf ? 0.f : m_ref);
+  };
+  auto sum_too_big = [](float psum) { return __ballot(!(psum <= kSumCap)) != 0; };  // also inf, NaN
+  auto pv = [&](const uint8_t* __restrict__ vs_, const u32x4_t (&pf)[NT2][2]) {
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
@@ -430,103 +431,277 @@ prefill_kernel(const FwdParams p) {
           oacc[dt] = E::mfma32x32x16(a, pf[t2][c], oacc[dt]);
         }
   };
+  // softmax of a block's scores s into pf, then O^T += V^T P^T
+  auto softmax_pv = [&](const uint8_t* __restrict__ vs_, const f32x16_t (&s)[NT2]) {
+    u32x4_t pf[NT2][2];
+    float psum = 0.f;
+    bool ok = false;
+    if (__ballot(m_ref == kNegInf) == 0) {  // some row without a reference: straight to the max
+      psum = exps(s, pf, m_ref);
+      ok = !sum_too_big(psum);
+    }
+    if (!ok) psum = slow(s, pf);
+    l_run += psum;
+    pv(vs_, pf);
+  };
 
-  // ---- main loop: step i, group g works on block n_lo + NG i + g; every group
-  // runs the same number of steps so one work-group barrier per step suffices.
-  // K(n) and V(n) live in stage i & 1.  A step starts the DMA of the group's
-  // next block into the other stage and computes block n.  The stages never
-  // overlap; restrict tells the compiler so, which lets the operand reads of
-  // this step proceed while the DMA into the other stage is in flight (without
-  // it every LDS read waits for all outstanding DMA).
   uint8_t* const k0 = gsm;
   uint8_t* const k1 = gsm + KTILE;
   uint8_t* const v0 = gsm + 2 * KTILE;
   uint8_t* const v1 = gsm + 2 * KTILE + VTILE;
-  auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                  uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
-    if (n + NG < n_hi) issue(n + NG, kn, vn);
-    if (n >= w_lo && n < w_hi) block(n, kc, vc);  // uniform per wave
-  };
   const int nblk = n_hi - n_lo;
   const int steps = (nblk + NG - 1) / NG;
-  // Consume Q after the first block's DMA is on its way (in each branch, so
-  // that each path waits only for the Q loads): the compiler then waits for
-  // them before the loop.  Otherwise it cannot tell that the loop's own waits
-  // covered them and waits inside every step for all newer loads, the next
-  // block's prefetch included.
-  if (n_lo + grp < n_hi) {
-    issue(n_lo + grp, k0, v0);
+  // group g works on blocks b_i = n_lo + g + NG i, i < nb
+  const int nb = nblk > grp ? (nblk - grp + NG - 1) / NG : 0;
+  auto blk = [&](int i) { return n_lo + grp + NG * i; };
+  auto active = [&](int i) { return blk(i) >= w_lo && blk(i) < w_hi; };  // uniform per wave
+  // Consume Q after the first DMA is on its way (in each branch, so that each
+  // path waits only for the Q loads): the compiler then waits for them before
+  // the loop.  Otherwise it cannot tell that the loop's own waits covered them
+  // and waits inside every step for all newer loads, the next block's
+  // prefetch included.
+  auto pin_q = [&] {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
-  // Unrolled by two so each call sees fixed stages.  Before each step: block
-  // n has landed in LDS and every wave is done with the previous step.
-  int i = 0;
-  for (; i + 1 < steps; i += 2) {
-    const int n = n_lo + NG * i + grp;
-    wait_vmem_all();
-    __syncthreads();
-    step(k0, v0, k1, v1, n);
-    wait_vmem_all();
-    __syncthreads();
-    step(k1, v1, k0, v0, n + NG);
-  }
-  if (i < steps) {
-    wait_vmem_all();
-    __syncthreads();
-    step(k0, v0, k1, v1, n_lo + NG * i + grp);
-  }
+  };
 
-  // ---- merge the groups: group 1 hands (m, l, O) to group 0 through LDS.
-  float l_tot = halves_sum(l_run);
-  if constexpr (NG > 1) {
-    __syncthreads();  // tile buffers are free
-    float* xm = reinterpret_cast<float*>(smem);  // [wave in group][2][lane]: m, l
-    float* xo = xm + 2 * 4 * 64;                  // [wave in group][reg][lane]: O^T
-    if (grp == 1) {  // group 0's wave `slot` holds the same rows
-      const int slot = paired ? wg ^ 2 : wg;
-      xm[(slot * 2 + 0) * 64 + lane] = m_ref;
-      xm[(slot * 2 + 1) * 64 + lane] = l_tot;
+  if constexpr (NG == 1 && D == 128 && !SOFTCAP) {
+    // ---- software-pipelined loop (one group: large grids).  Step i computes
+    // S(b_i) = K(b_i) Q^T and, with the exponentials of S(b_{i-1}) issued
+    // between those MFMAs, the softmax and O += P V of b_{i-1}.  One SIMD
+    // overlaps MFMAs with VALU work only when the instruction streams it holds
+    // mix them finely; block-sized phases of MFMA and of VALU work, in step on
+    // every wave after the barrier, leave one of the two units idle.  K(b_i)
+    // lives in K stage i & 1, V(b_i) in V stage i & 1; step i loads K(b_{i+1})
+    // and V(b_i) (their stages were last read in step i - 1).  With two groups
+    // (small grids, few blocks per tile), and at d = 64 (twice the VALU work
+    // per MFMA), the extra step and the discarded work at each end cost more
+    // than the overlap gains (measured), so those take the plain loop; softcap
+    // needs more registers than two waves per SIMD leave.
+    constexpr int NA = KS * NT2;        // MFMAs of S^T = K Q^T per block
+    constexpr int EPM = 16 * NT2 / NA;  // exponentials per such MFMA
+    static_assert(EPM >= 2 && EPM % 2 == 0, "exponential pairs per MFMA");
+    constexpr int VPM = EPM / 2 * 7;  // VALU instructions per MFMA: 2 FMA, 2 exp, 1 pack, 2 add
+    // S(b_i) = K Q^T interleaved with the exponentials of S(b_{i-1}) = sc
+    // against the current reference, then the check, the softmax fix-up if
+    // needed and O += P(b_{i-1}) V(b_{i-1}).
+    auto fused = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vp,
+                     const f32x16_t (&sc)[NT2], f32x16_t (&sn)[NT2], bool ap) {
+      u32x4_t pf[NT2][2];
+      float psum = 0.f;
+      const float base = m_ref;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int t2 = 0; t2 < NT2; ++t2) sn[t2] = f32x16_t{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[((slot * DT + dt) * 16 + r) * 64 + lane] = oacc[dt][r];
-    }
-    __syncthreads();
-    if (grp != 0) return;
-    const float m1 = xm[(wg * 2 + 0) * 64 + lane];
-    const float l1 = xm[(wg * 2 + 1) * 64 + lane];
-    const float mm = fmaxf(m_ref, m1);
-    const float bm = mm == kNegInf ? 0.f : mm;
-    const float a0 = fast_exp2(m_ref - bm);  // 0 for an empty side
-    const float a1 = fast_exp2(m1 - bm);
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int t2 = 0; t2 < NT2; ++t2) {
+          const int mi = ks * NT2 + t2;
+          sn[t2] = E::mfma32x32x16(k_operand(kc, ks, t2), qf[ks], sn[t2]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        oacc[dt][r] = oacc[dt][r] * a0 + xo[((wg * DT + dt) * 16 + r) * 64 + lane] * a1;
-    l_tot = l_tot * a0 + l1 * a1;
-    m_ref = mm;
-  }
-
-  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; empty rows: 0 and -inf.
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_valid && qrow < sq) {
-    uint16_t* op = og + (int64_t)qrow * p.o_ss;
+          for (int u = 0; u < EPM; u += 2) {
+            const int e = mi * EPM + u, t = e >> 4, r = e & 15;
+            const float x0 = fast_exp2(__builtin_fmaf(sc[t][r], p.scale_log2, -base));
+            const float x1 = fast_exp2(__builtin_fmaf(sc[t][r + 1], p.scale_log2, -base));
+            pf[t][r >> 3][(r & 7) >> 1] = E::pack2(x0, x1);
+            psum += x0 + x1;
+          }
+        }
+      // order: two K operand reads ahead, then per MFMA one more read and its
+      // share of the exponentials
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        u32x2_t w;
-        w[0] = E::pack2(oacc[dt][4 * J] * inv, oacc[dt][4 * J + 1] * inv);
-        w[1] = E::pack2(oacc[dt][4 * J + 2] * inv, oacc[dt][4 * J + 3] * inv);
-        *(u32x2_t*)(op + 32 * dt + 8 * J + 4 * hsel) = w;
+      for (int mi = 0; mi < NA; ++mi) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (mi + 2 < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
       }
-    if (hsel == 0 && lseg != nullptr)
-      lseg[qrow] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+      // consume the exponentials here: LLVM would otherwise sink them below
+      // the branch that follows, out of the MFMA stream
+#pragma unroll
+      for (int t = 0; t < NT2; ++t) asm volatile("" ::"v"(pf[t][0]), "v"(pf[t][1]));
+      asm volatile("" ::"v"(psum));
+      if (ap) {
+        if (sum_too_big(psum)) psum = slow(sc, pf);
+        l_run += psum;
+        pv(vp, pf);
+      }
+    };
+    // kc: K(b_i); vp: V(b_{i-1}); kn: stage for K(b_{i+1}); vc: stage for V(b_i)
+    auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vp,
+                    uint8_t* __restrict__ kn, uint8_t* __restrict__ vc, int i,
+                    const f32x16_t (&sc)[NT2], f32x16_t (&sn)[NT2]) {
+      if (i + 1 < nb) issue_k(blk(i + 1), kn);
+      if (i < nb) issue_v(blk(i), vc);
+      const bool ai = i < nb && active(i);
+      const bool ap = i > 0 && i <= nb && active(i - 1);
+      // A wave's first block (no previous one) still runs the exponentials, on
+      // stale registers, and its last runs S = K Q^T on a stale stage: both
+      // results are discarded.  Branching around them instead costs registers.
+      if (ai || ap) fused(kc, vp, sc, sn, ap);
+      if (ai) {
+        const int kb = blk(i) * BN;
+        if (kb + BN - 1 > full_r || kb < full_l) mask_keys(sn, mhi - kb, mlo - kb);
+      }
+    };
+    if (nb > 0) {
+      issue_k(blk(0), k0);
+      pin_q();
+    } else {
+      pin_q();
+    }
+    f32x16_t sa[NT2], sb[NT2];
+    // Unrolled by two so each call sees fixed stages and score registers.
+    // Before each step: K(b_i) and V(b_{i-1}) have landed, and every wave is
+    // done with the previous step.
+    int i = 0;
+    for (; i + 1 <= steps; i += 2) {
+      wait_vmem_all();
+      __syncthreads();
+      step(k0, v1, k1, v0, i, sb, sa);
+      wait_vmem_all();
+      __syncthreads();
+      step(k1, v0, k0, v1, i + 1, sa, sb);
+    }
+    if (i <= steps) {
+      wait_vmem_all();
+      __syncthreads();
+      step(k0, v1, k1, v0, i, sb, sa);
+    }
+  } else {
+    // ---- plain loop: step i, group g works on block b_i; K(b_i) and V(b_i)
+    // live in stage i & 1.  A step starts the DMA of the group's next block
+    // into the other stage and computes block b_i.  The stages never overlap;
+    // restrict tells the compiler so, which lets the operand reads of this
+    // step proceed while the DMA into the other stage is in flight (without
+    // it every LDS read waits for all outstanding DMA).
+    auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                    uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
+      if (n + NG < n_hi) {
+        issue_k(n + NG, kn);
+        issue_v(n + NG, vn);
+      }
+      if (n >= w_lo && n < w_hi) {  // uniform per wave
+        f32x16_t s[NT2];
+        qk(kc, s);
+        const int kb = n * BN;
+        if (kb + BN - 1 > full_r || kb < full_l) mask_keys(s, mhi - kb, mlo - kb);
+        softmax_pv(vc, s);
+      }
+    };
+    if (n_lo + grp < n_hi) {
+      issue_k(n_lo + grp, k0);
+      issue_v(n_lo + grp, v0);
+      pin_q();
+    } else {
+      pin_q();
+    }
+    int i = 0;
+    for (; i + 1 < steps; i += 2) {
+      const int n = n_lo + NG * i + grp;
+      wait_vmem_all();
+      __syncthreads();
+      step(k0, v0, k1, v1, n);
+      wait_vmem_all();
+      __syncthreads();
+      step(k1, v1, k0, v0, n + NG);
+    }
+    if (i < steps) {
+      wait_vmem_all();
+      __syncthreads();
+      step(k0, v0, k1, v1, n_lo + NG * i + grp);
+    }
+  }
+
+  // ---- epilogue.  The tile buffers are free after the barrier.  With two
+  // groups, the two waves that hold the same 32 rows merge their (m, l, O)
+  // with the log-sum-exp merge, each finalizing half of the head dims from
+  // what its partner hands over through LDS.  Then O = O^T / l, rounded, goes
+  // through an LDS tile so that global stores cover whole rows (16 lanes x
+  // 16 bytes per row piece instead of 32 rows x 8 bytes per instruction), and
+  // LSE = (m + log2 l) ln 2.  Empty rows give 0 and -inf.
+  constexpr int DTH = DT / NG;                           // d tiles a wave finalizes
+  constexpr int XM_BYTES = NG > 1 ? 4 * NG * 2 * 64 * 4 : 0;          // m, l
+  constexpr int XO_BYTES = NG > 1 ? 4 * NG * DTH * 16 * 64 * 4 : 0;   // half of O^T
+  constexpr int OROW = D * 2;                            // bytes per row of the O tile
+  static_assert(XM_BYTES + XO_BYTES + kBM * OROW <= NG * GROUP_LDS, "epilogue buffers");
+  float* const xm = reinterpret_cast<float*>(smem);
+  float* const xo = reinterpret_cast<float*>(smem + XM_BYTES);
+  uint8_t* const otile = smem + XM_BYTES + XO_BYTES;
+  const int rs = (my_a ? 0 : 2) + (wg & 1);  // which 32 of the work group's 128 rows
+  const int orow = 32 * rs + l32;            // this lane's row in the O tile
+  float l_tot = halves_sum(l_run);
+  __syncthreads();
+  // rounds O^T tile dt (scaled by inv) into the O tile
+  auto put = [&](int dt, float inv) {
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      u32x2_t w;
+      w[0] = E::pack2(oacc[dt][4 * J] * inv, oacc[dt][4 * J + 1] * inv);
+      w[1] = E::pack2(oacc[dt][4 * J + 2] * inv, oacc[dt][4 * J + 3] * inv);
+      const int chunk = 4 * dt + J;
+      *(u32x2_t*)(otile + orow * OROW + 16 * (chunk ^ kswz<D>(orow)) + 8 * hsel) = w;
+    }
+  };
+  if constexpr (NG > 1) {
+    // half h of the head dims (d tiles h DTH ..) is finalized by group h
+    auto merge = [&](int h) {
+      const int ex = rs * NG + grp, pe = rs * NG + (1 - h);
+      xm[(ex * 2 + 0) * 64 + lane] = m_ref;
+      xm[(ex * 2 + 1) * 64 + lane] = l_tot;
+#pragma unroll
+      for (int j = 0; j < DTH; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          xo[((ex * DTH + j) * 16 + r) * 64 + lane] = oacc[(1 - h) * DTH + j][r];
+      __syncthreads();
+      const float m1 = xm[(pe * 2 + 0) * 64 + lane];
+      const float l1 = xm[(pe * 2 + 1) * 64 + lane];
+      const float mm = fmaxf(m_ref, m1);
+      const float bm = mm == kNegInf ? 0.f : mm;
+      const float a0 = fast_exp2(m_ref - bm);  // 0 for an empty side
+      const float a1 = fast_exp2(m1 - bm);
+#pragma unroll
+      for (int j = 0; j < DTH; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[h * DTH + j][r] =
+              oacc[h * DTH + j][r] * a0 + xo[((pe * DTH + j) * 16 + r) * 64 + lane] * a1;
+      // the same terms in both groups, so both get the same l and m
+      l_tot = l_tot * a0 + l1 * a1;
+      m_ref = mm;
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      if (my_valid) {
+#pragma unroll
+        for (int j = 0; j < DTH; ++j) put(h * DTH + j, inv);
+      }
+    };
+    if (grp == 0)
+      merge(0);
+    else
+      merge(1);
+  } else {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (my_valid) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) put(dt, inv);
+    }
+  }
+  if (grp == 0 && my_valid && qrow < sq && hsel == 0 && lseg != nullptr)
+    lseg[qrow] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+  __syncthreads();
+  // O tile -> global, 16 bytes per thread: rows 0-63 are tile_a, 64-127 tile_b
+  constexpr int NTH = 256 * NG;
+  static_assert(kBM * DCH % NTH == 0, "O tile copy");
+#pragma unroll
+  for (int it = 0; it < kBM * DCH / NTH; ++it) {
+    const int idx = it * NTH + tid;
+    const int row = idx / DCH, chunk = idx % DCH;
+    const int grow = 64 * (row < 64 ? tile_a : tile_b) + (row & 63);
+    if ((row < 64 || b_valid) && grow < sq) {
+      const u32x4_t v = *(const u32x4_t*)(otile + row * OROW + 16 * (chunk ^ kswz<D>(row)));
+      *(u32x4_t*)(og + (int64_t)grow * p.o_ss + 8 * chunk) = v;
+    }
   }
 }
 
