@@ -15,7 +15,9 @@
 //   runs two waves: one wave's softmax issues while the other's MFMAs run, and
 //   LDS reads reach about 200 B/clk/CU instead of about 120 with one wave per
 //   SIMD (measured).  The groups' partial (m, l, O) are merged through LDS at
-//   the end, the same log-sum-exp merge as between tiles;
+//   the end, the same log-sum-exp merge as between tiles, each group
+//   finalizing half of the head dims; O then leaves through an LDS tile so
+//   that global stores cover whole rows;
 // - the wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (bf16/f16, fp32
 //   accumulate): K is the A operand read from LDS, Q^T the B operand held in
 //   registers for the whole loop.  In the 32x32 accumulator layout every lane
@@ -24,13 +26,13 @@
 // - the A-operand row -> key map is permuted so that accumulator registers
 //   8c..8c+7 of lane half H are 8 consecutive keys (16c + 8H + 0..7); rounded
 //   to 16 bits they are directly the B operand (P^T) of O^T = V^T P^T;
-// - K tiles go from global memory straight into LDS (buffer_load ... lds, no
-//   staging registers); V tiles are staged in registers and written to LDS
-//   transposed, so the V^T operand is one ds_read_b128 per MFMA (the LDS
-//   transpose read delivers about half the bytes per clock, measured);
-// - 16-byte chunks are XOR-swizzled per row, which keeps every operand read
-//   and every V^T write free of bank conflicts and all LDS addresses
-//   loop-invariant;
+// - K and V tiles go from global memory straight into LDS (buffer_load ...
+//   lds, no staging registers).  V stays row-major: the V^T operand is two
+//   transposing LDS reads (ds_read_b64_tr_b16) per MFMA;
+// - 16-byte chunks are XOR-swizzled per row, which keeps the operand reads
+//   free of bank conflicts and all LDS addresses loop-invariant;
+// - with one group and d = 128 the loop is software-pipelined: the QK MFMAs of
+//   block i are interleaved with the exponentials of block i - 1;
 // - loads use per-block buffer descriptors whose range ends at the last key of
 //   the sequence: the hardware range check returns zeros past the end, so
 //   block tails need no extra code;
