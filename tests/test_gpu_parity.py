@@ -101,6 +101,66 @@ def test_varlen_gqa_window_softcap():
     assert_lse_close(lse, l_ref, "varlen")
 
 
+def _dense_grid(b, s_q, h_q):
+    """Work groups of a dense prefill launch: one per 128 query rows of a head."""
+    return b * h_q * math.ceil(s_q / 128)
+
+
+ONE_GROUP_CASES = [
+    # dtype, b, s_q, s_k, h_q, h_kv, d, causal, window, softcap
+    (torch.bfloat16, 4, 1061, 1061, 16, 4, 128, True, (-1, -1), 0.0),
+    (torch.float16, 4, 1061, 1300, 16, 16, 128, False, (100, 20), 0.0),
+    (torch.bfloat16, 4, 1061, 1061, 16, 8, 128, False, (-1, -1), 0.0),
+    (torch.float16, 4, 1061, 1061, 16, 2, 128, True, (-1, -1), 30.0),
+    (torch.bfloat16, 4, 1061, 900, 16, 8, 64, True, (-1, -1), 0.0),
+]
+
+
+@pytest.mark.parametrize("case", ONE_GROUP_CASES, ids=[f"o{i}" for i in range(len(ONE_GROUP_CASES))])
+def test_one_group_launches(case):
+    """Grids of at least two work groups per CU take 4-wave work groups, and for
+    d = 128 without softcap the software-pipelined loop: every mask rule, GQA and
+    a ragged tail there, three heads in full against the oracle."""
+    dt, b, sq, sk, hq, hkv, d, causal, window, cap = case
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert _dense_grid(b, sq, hq) >= 2 * cus, "shape too small for one-group work groups"
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=140 + ONE_GROUP_CASES.index(case), dtype=dt)
+    dq, dk, dv = _dev(q, k, v)
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((b, hq, sq))
+    ex.attn_func(dq, dk, dv, causal=causal, window_size=window, softcap=cap, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    heads = [0, hq // 2 + 1, hq - 1]
+    o_ref, l_ref = oracle.attention(q, k, v, causal=causal, window_size=window, softcap=cap,
+                                    heads=heads)
+    o_cpu, l_cpu = out.cpu(), lse.cpu()
+    for h in heads:
+        assert_o_close(o_cpu[:, :, h], o_ref[:, :, h], dt, f"one-group h{h}")
+        assert_lse_close(l_cpu[:, h], l_ref[:, h], f"one-group h{h}")
+
+
+def test_one_group_varlen():
+    """Varlen with enough sequences for one-group work groups (d = 128, pipelined
+    loop), ragged and empty sequences, causal then a window."""
+    lens_q = [1100, 37, 640, 1025, 300, 0, 777, 129]
+    lens_k = [1100, 50, 640, 1000, 301, 9, 777, 129]
+    hq, hkv = 8, 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert len(lens_q) * hq * math.ceil(max(lens_q) / 128) >= 2 * cus
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, hq, hkv, 128, seed=150)
+    dq, dk, dv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    for causal, window in [(True, (-1, -1)), (False, (70, 5))]:
+        out = _poison_out(q.shape, q.dtype)
+        lse = _poison_lse((hq, q.shape[0]))
+        ex.attn_varlen_func(dq, dk, dv, dcq, dck, max(lens_q), max(lens_k), causal=causal,
+                            window_size=window, out=out, lse=lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal=causal, window_size=window)
+        assert_o_close(out, o_ref, q.dtype, f"one-group varlen {causal} {window}")
+        assert_lse_close(lse, l_ref, f"one-group varlen {causal} {window}")
+
+
 def test_cross_attention():
     w = W.WORKLOADS["cross"]
     q, k, v = W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
