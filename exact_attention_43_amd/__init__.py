@@ -67,6 +67,14 @@ class DecodeArgs(C.Structure):
     ]
 
 
+class KvNew(C.Structure):
+    """Mirror of exattn_kv_new."""
+    _fields_ = [
+        ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("seqlen_new", C.c_int32),
+        ("k_new_stride", C.c_int64 * 3), ("v_new_stride", C.c_int64 * 3),
+    ]
+
+
 _lib_handle = None
 _lib_lock = threading.Lock()
 
@@ -93,6 +101,9 @@ def lib():
             L.exattn_decode_plan.restype = C.c_int
             L.exattn_decode.argtypes = [C.POINTER(DecodeArgs), C.c_void_p, C.c_size_t, C.c_void_p]
             L.exattn_decode.restype = C.c_int
+            L.exattn_decode_append.argtypes = [C.POINTER(DecodeArgs), C.POINTER(KvNew), C.c_void_p,
+                                               C.c_size_t, C.c_void_p]
+            L.exattn_decode_append.restype = C.c_int
             L.exattn_decode_auto_splits.argtypes = [C.c_int32] * 6
             L.exattn_decode_auto_splits.restype = C.c_int32
             L.exattn_args_size.argtypes = [C.c_int32]
@@ -103,7 +114,8 @@ def lib():
             L.exattn_last_error.restype = C.c_char_p
             L.exattn_abi_version.argtypes = []
             L.exattn_abi_version.restype = C.c_int32
-            if L.exattn_args_size(0) != C.sizeof(FwdArgs) or L.exattn_args_size(1) != C.sizeof(DecodeArgs):
+            if (L.exattn_args_size(0) != C.sizeof(FwdArgs) or L.exattn_args_size(1) != C.sizeof(DecodeArgs)
+                    or L.exattn_args_size(2) != C.sizeof(KvNew)):
                 raise RuntimeError("libexattn.so struct layout does not match this binding; rebuild it")
             _lib_handle = L
     return _lib_handle
@@ -325,13 +337,16 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     """KV-cache decode with one query token (FAQ Q17).
 
     q (b, 1, h_q, d); k_cache, v_cache (b, s_cache, h_kv, d); cache_seqlens an
-    int32 GPU tensor (b,), an int, or None for the full cache.  The call never
-    changes cache_seqlens (the caller advances it).  num_splits = 0 picks the
-    split count automatically (FAQ Q14).  Appending k/v into the cache is not
-    provided by this forward.
+    int32 GPU tensor (b,), an int, or None for the full cache.  With k, v
+    (b, s_new, h_kv, d) the new tokens are first written to cache rows
+    cache_seqlens[b] .. cache_seqlens[b] + s_new - 1 (k_cache and v_cache are
+    updated in place) and the query attends to cache_seqlens[b] + s_new rows;
+    cache_seqlens is required then.  The call never changes cache_seqlens (the
+    caller advances it by s_new).  num_splits = 0 picks the split count
+    automatically (FAQ Q14).
     """
-    if k is not None or v is not None:
-        raise NotImplementedError("appending k/v to the cache is not provided; pass k=None, v=None")
+    if (k is None) != (v is None):
+        raise ValueError("pass both k and v to append, or neither")
     if q.dim() != 4 or q.shape[1] != 1:
         raise ValueError("q must be (batch, 1, heads_q, head_dim)")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -339,9 +354,22 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share one dtype")
     _on_gpu(q, k_cache, v_cache, out, lse, cache_seqlens if torch.is_tensor(cache_seqlens) else None,
-            workspace)
+            workspace, k, v)
     _check_last_dim(q, k_cache, v_cache)
     b, _, h_q, d = q.shape
+    kv = None
+    if k is not None:
+        if k.dim() != 4 or v.shape != k.shape or k.shape[0] != b or k.shape[2:] != k_cache.shape[2:]:
+            raise ValueError("k and v must be (batch, seqlen_new, heads_kv, head_dim) like the cache")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("k and v must share the cache dtype")
+        if cache_seqlens is None:
+            raise ValueError("appending k/v needs cache_seqlens")
+        _check_last_dim(k, v)
+        kv = KvNew()
+        kv.k_new, kv.v_new, kv.seqlen_new = k.data_ptr(), v.data_ptr(), k.shape[1]
+        kv.k_new_stride[:] = list(k.stride()[:3])
+        kv.v_new_stride[:] = list(v.stride()[:3])
     if isinstance(cache_seqlens, int):
         cache_seqlens = torch.full((b,), cache_seqlens, dtype=torch.int32, device=q.device)
     if cache_seqlens is not None:
@@ -364,9 +392,13 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
             if workspace is None:
                 workspace = _workspace(q.device, wb.value)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        st = L.exattn_decode(C.byref(a), C.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes,
-                             C.c_void_p(_stream(q.device)))
-    _raise_for(st, "exattn_decode")
+        ws = C.c_void_p(ws_ptr) if ws_ptr else None
+        strm = C.c_void_p(_stream(q.device))
+        if kv is None:
+            st = L.exattn_decode(C.byref(a), ws, ws_bytes, strm)
+        else:
+            st = L.exattn_decode_append(C.byref(a), C.byref(kv), ws, ws_bytes, strm)
+    _raise_for(st, "exattn_decode" if kv is None else "exattn_decode_append")
     return out, lse
 
 

@@ -139,13 +139,25 @@ exattn_status exattn_decode_plan(const exattn_decode_args* a, int32_t* num_split
   }
 }
 
-exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode behind exattn_decode and exattn_decode_append: kv_new (or NULL)
+// is written into the cache first, and the attended length per batch entry is
+// cache_seqlens[b] + its seqlen_new.
+exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_new, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   try {
     clear_error();
     DecodePlan pl;
     exattn_status st = plan_decode(a, 1, &pl);
     if (st != EXATTN_OK) return st;
+    if (kv_new != nullptr) {
+      st = check_append(a, kv_new);
+      if (st != EXATTN_OK) return st;
+    }
+    const int32_t s_new = kv_new != nullptr && a->batch > 0 ? kv_new->seqlen_new : 0;
     if (a->num_splits == 0) {
       int cus = 1;
       st = device_cus(&cus);
@@ -162,7 +174,29 @@ exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(EXATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
     }
+    if (s_new > 0) {
+      AppendParams ap{};
+      ap.k_new = static_cast<const uint16_t*>(kv_new->k_new);
+      ap.v_new = static_cast<const uint16_t*>(kv_new->v_new);
+      ap.k = static_cast<uint16_t*>(const_cast<void*>(a->k_cache));
+      ap.v = static_cast<uint16_t*>(const_cast<void*>(a->v_cache));
+      ap.kn_sb = kv_new->k_new_stride[0], ap.kn_ss = kv_new->k_new_stride[1];
+      ap.kn_sh = kv_new->k_new_stride[2];
+      ap.vn_sb = kv_new->v_new_stride[0], ap.vn_ss = kv_new->v_new_stride[1];
+      ap.vn_sh = kv_new->v_new_stride[2];
+      ap.k_sb = a->k_stride[0], ap.k_ss = a->k_stride[1], ap.k_sh = a->k_stride[2];
+      ap.v_sb = a->v_stride[0], ap.v_ss = a->v_stride[1], ap.v_sh = a->v_stride[2];
+      ap.cache_seqlens = a->cache_seqlens;
+      ap.batch = a->batch;
+      ap.s_new = s_new;
+      ap.h_kv = a->heads_kv;
+      ap.head_dim = a->head_dim;
+      ap.s_cache = a->seqlen_cache;
+      hipError_t e = launch_append(ap, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("append launch: ") + hipGetErrorString(e));
+    }
     DecParams p{};
+    p.seq_add = s_new;
     p.q = static_cast<const uint16_t*>(a->q);
     p.k = static_cast<const uint16_t*>(a->k_cache);
     p.v = static_cast<const uint16_t*>(a->v_cache);
@@ -202,13 +236,34 @@ exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t
   }
 }
 
+}  // namespace
+
+extern "C" {
+
+exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return run_decode(a, nullptr, workspace, workspace_bytes, stream);
+}
+
+exattn_status exattn_decode_append(const exattn_decode_args* a, const exattn_kv_new* kv_new,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_new == nullptr) {
+    clear_error();
+    return fail(EXATTN_E_INVALID, "kv_new is NULL");
+  }
+  return run_decode(a, kv_new, workspace, workspace_bytes, stream);
+}
+
 int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv,
                                   int32_t seqlen_k, int32_t head_dim, int32_t num_cus) {
   return auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus);
 }
 
 size_t exattn_args_size(int32_t which) {
-  return which == 0 ? sizeof(exattn_fwd_args) : which == 1 ? sizeof(exattn_decode_args) : 0;
+  return which == 0   ? sizeof(exattn_fwd_args)
+         : which == 1 ? sizeof(exattn_decode_args)
+         : which == 2 ? sizeof(exattn_kv_new)
+                      : 0;
 }
 
 const char* exattn_status_string(int32_t status) {

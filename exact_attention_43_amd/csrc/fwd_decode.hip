@@ -108,7 +108,8 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
 
   // cache_seqlens[b] is clamped to [0, s_cache] so a bad entry cannot address
   // memory outside the cache.
-  const int nk = p.cache_seqlens != nullptr ? min(max(p.cache_seqlens[b], 0), p.s_cache) : p.s_cache;
+  const int nk = p.cache_seqlens != nullptr ? min(max(p.cache_seqlens[b] + p.seq_add, 0), p.s_cache)
+                                            : p.s_cache;
   // The query sits at position nk - 1; only the left window edge removes keys.
   const int kb = p.wl >= 0 ? max(0, nk - 1 - p.wl) : 0;
   const int nsteps = nk > kb ? (nk - kb + KSTEP - 1) / KSTEP : 0;
@@ -409,6 +410,37 @@ hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softc
                          hipStream_t stream) {
   return bf16 ? launch_t<true>(p, head_dim, softcap, stream)
               : launch_t<false>(p, head_dim, softcap, stream);
+}
+
+namespace {
+
+// One work group per (new token t, batch entry b): its threads copy the
+// token's K and V rows of every KV head, 16 bytes each, to cache row
+// cache_seqlens[b] + t (FAQ Q17: the new tokens are appended, then attended).
+__global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
+  const int t = blockIdx.x;
+  const int b = blockIdx.y;
+  const int pos = p.cache_seqlens[b] + t;
+  if (pos < 0 || pos >= p.s_cache) return;  // outside the cache: not written
+  const int cpr = p.head_dim / 8;  // 16-byte chunks per head row
+  const int n = p.h_kv * cpr;
+  for (int c = threadIdx.x; c < 2 * n; c += blockDim.x) {
+    const bool is_v = c >= n;
+    const int cc = is_v ? c - n : c;
+    const int h = cc / cpr, j = cc % cpr;
+    const uint16_t* src = is_v ? p.v_new + (int64_t)b * p.vn_sb + (int64_t)t * p.vn_ss + (int64_t)h * p.vn_sh
+                               : p.k_new + (int64_t)b * p.kn_sb + (int64_t)t * p.kn_ss + (int64_t)h * p.kn_sh;
+    uint16_t* dst = is_v ? p.v + (int64_t)b * p.v_sb + (int64_t)pos * p.v_ss + (int64_t)h * p.v_sh
+                         : p.k + (int64_t)b * p.k_sb + (int64_t)pos * p.k_ss + (int64_t)h * p.k_sh;
+    *(u32x4_t*)(dst + 8 * j) = *(const u32x4_t*)(src + 8 * j);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(p.s_new, p.batch), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace exattn

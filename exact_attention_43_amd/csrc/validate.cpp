@@ -208,4 +208,21 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
   return EXATTN_OK;
 }
 
+exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n) {
+  if (n == nullptr) return fail(EXATTN_E_INVALID, "kv_new is NULL");
+  if (n->seqlen_new < 0) return fail(EXATTN_E_INVALID, "seqlen_new is negative");
+  if (n->seqlen_new == 0 || a->batch == 0) return EXATTN_OK;
+  if (a->cache_seqlens == nullptr)
+    return fail(EXATTN_E_INVALID, "appending needs cache_seqlens (the rows to write at)");
+  if (n->seqlen_new > a->seqlen_cache)
+    return fail(EXATTN_E_INVALID, "seqlen_new exceeds seqlen_cache");
+  if (n->k_new == nullptr || n->v_new == nullptr) return fail(EXATTN_E_INVALID, "k_new or v_new is NULL");
+  if (!aligned16(n->k_new) || !aligned16(n->v_new))
+    return fail(EXATTN_E_INVALID, "k_new and v_new must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (!stride_ok(n->k_new_stride[i]) || !stride_ok(n->v_new_stride[i]))
+      return fail(EXATTN_E_INVALID, "k_new/v_new strides must be non-negative multiples of 8 elements");
+  return EXATTN_OK;
+}
+
 }  // namespace exattn

@@ -57,6 +57,10 @@ struct DecodePlan {
 // Check `a` and fill `plan` for a device with `num_cus` compute units.
 exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* plan);
 
+// Checks the new tokens of exattn_decode_append against the decode arguments
+// (which plan_decode has accepted).
+exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n);
+
 
 // Adjacent KV heads one decode work group covers: enough for a 2 KiB piece of
 // every key row (16 at d = 64, 8 at d = 128, 4 at d = 256), rounded down to a

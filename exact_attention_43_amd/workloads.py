@@ -80,6 +80,14 @@ def kvcache(b, s_cache, h_q, h_kv, d, seed, dtype=torch.bfloat16):
     return q, kc, vc
 
 
+def kv_new(b, s_new, h_kv, d, seed, dtype=torch.bfloat16):
+    """New tokens for a cache append: one (b, s_new, 2, h_kv, d) draw, returned as
+    the strided views k_new = [:, :, 0] and v_new = [:, :, 1]."""
+    g = torch.Generator().manual_seed(int(seed))
+    kv = randn((b, s_new, 2, h_kv, d), dtype=dtype, generator=g)
+    return kv[:, :, 0], kv[:, :, 1]
+
+
 @dataclass(frozen=True)
 class Workload:
     """A named attention shape.  ``kind`` is 'dense', 'qkvpacked', 'varlen' or 'decode'."""

@@ -156,6 +156,35 @@ exattn_status exattn_decode_plan(const exattn_decode_args *args, int32_t *num_sp
 exattn_status exattn_decode(const exattn_decode_args *args, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/*
+ * New tokens for exattn_decode_append: flash_attn_with_kvcache called with
+ * k=k_new, v=v_new (FAQ Q17).  k_new and v_new are (batch, seqlen_new,
+ * heads_kv, head_dim) in the cache's dtype, addressed by k_new_stride /
+ * v_new_stride (elements: batch, token, head; last dimension contiguous),
+ * 16-byte aligned, strides multiples of 8 elements.
+ */
+typedef struct {
+  const void *k_new, *v_new;
+  int32_t seqlen_new;
+  int64_t k_new_stride[3], v_new_stride[3];
+} exattn_kv_new;
+
+/* KV-cache decode with an append (FAQ Q17): for every batch entry b, new
+ * token t is first written to cache row cache_seqlens[b] + t of k_cache and
+ * v_cache, then the query attends to the first cache_seqlens[b] + seqlen_new
+ * rows exactly as exattn_decode does (the query sits at the last of them).
+ * cache_seqlens must not be NULL, and, as in the FAQ, the call does not
+ * advance it: the caller adds seqlen_new afterwards.  Precondition:
+ * 0 <= cache_seqlens[b] and cache_seqlens[b] + seqlen_new <= seqlen_cache;
+ * new rows that would fall outside [0, seqlen_cache) are not written and the
+ * attended length is clamped to seqlen_cache, so a violated precondition
+ * gives wrong values but no out-of-bounds access.  Cache rows other than the
+ * new ones are left unchanged.  workspace as for exattn_decode (the same
+ * plan applies: exattn_decode_plan on args).  seqlen_new = 0 is exattn_decode.
+ * The write and the attention are two kernels in order on the stream. */
+exattn_status exattn_decode_append(const exattn_decode_args *args, const exattn_kv_new *kv_new,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* The automatic split count, as a pure function (no device query).  One work
  * group covers up to 1024/head_dim adjacent KV heads (16 at d = 64, 8 at
  * d = 128, 4 at d = 256; a power of two no larger than heads_kv) and 16 of
@@ -166,7 +195,8 @@ int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_
                                   int32_t seqlen_k, int32_t head_dim, int32_t num_cus);
 
 /* sizeof(exattn_fwd_args) for which = 0, sizeof(exattn_decode_args) for which = 1,
- * 0 otherwise: lets a binding check its mirror of the structs. */
+ * sizeof(exattn_kv_new) for which = 2, 0 otherwise: lets a binding check its
+ * mirror of the structs. */
 size_t exattn_args_size(int32_t which);
 
 const char *exattn_status_string(int32_t status);

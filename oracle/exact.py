@@ -31,7 +31,10 @@ Semantics, each from the pages, with the readings taken where they are silent:
 - variable length: sequences packed end to end and addressed by int32 prefix
   sums cu_seqlens (FAQ Q8); every sequence is attended on its own;
 - KV-cache decode: the query attends to the first cache_seqlens[b] cache rows
-  (FAQ Q17), with the bottom-right offset s_k - 1.
+  (FAQ Q17), with the bottom-right offset s_k - 1; with new tokens k, v the
+  rows are first written at cache_seqlens[b] + t and the query attends to
+  cache_seqlens[b] + s_new rows (reading: append, then attend, as the FAQ's
+  example and its manual cache_seqlens update imply).
 """
 from __future__ import annotations
 
@@ -216,6 +219,41 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens=None, *, softmax_scale=
         os_.append(ob)
         ls_.append(lb)
     return np.concatenate(os_, axis=0), np.concatenate(ls_, axis=0)
+
+
+def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new):
+    """The cache update of flash_attn_with_kvcache(q, k_cache, v_cache, k=k_new,
+    v=v_new, cache_seqlens=...) (FAQ Q17): token t of k_new / v_new
+    (b, s_new, h_kv, d) becomes cache row cache_seqlens[b] + t.
+
+    Works on copies, in the caches' own storage type (a plain copy of the
+    rows, no arithmetic), and returns (k_cache', v_cache').  Rows that would
+    land outside the cache are dropped.
+    """
+    lens = [int(x) for x in np.asarray(cache_seqlens).tolist()]
+    kc = k_cache.clone() if hasattr(k_cache, "clone") else np.array(k_cache, copy=True)
+    vc = v_cache.clone() if hasattr(v_cache, "clone") else np.array(v_cache, copy=True)
+    s_cache, s_new = kc.shape[1], k_new.shape[1]
+    for bi, n in enumerate(lens):
+        for t in range(s_new):
+            if 0 <= n + t < s_cache:
+                kc[bi, n + t] = k_new[bi, t]
+                vc[bi, n + t] = v_new[bi, t]
+    return kc, vc
+
+
+def attention_kvcache_append(q, k_cache, v_cache, k_new, v_new, cache_seqlens, *, softmax_scale=None,
+                             causal=False, window_size=(-1, -1), softcap=0.0, heads=None):
+    """Decode with an append (FAQ Q17): the new tokens are written into the
+    cache first, then q attends to the first cache_seqlens[b] + s_new rows.
+
+    Returns O, LSE and the updated caches (k_cache', v_cache').
+    """
+    kc, vc = kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new)
+    lens = [int(x) + k_new.shape[1] for x in np.asarray(cache_seqlens).tolist()]
+    o, lse = attention_kvcache(q, kc, vc, lens, softmax_scale=softmax_scale, causal=causal,
+                               window_size=window_size, softcap=softcap, heads=heads)
+    return o, lse, kc, vc
 
 
 def merge_partials(o_parts, lse_parts):

@@ -39,6 +39,7 @@ def test_exports_every_declared_symbol(L):
 def test_struct_layout_and_version(L):
     assert L.exattn_args_size(0) == C.sizeof(ex.FwdArgs)
     assert L.exattn_args_size(1) == C.sizeof(ex.DecodeArgs)
+    assert L.exattn_args_size(2) == C.sizeof(ex.KvNew)
     assert L.exattn_args_size(7) == 0
     assert L.exattn_abi_version() == 1
     assert L.exattn_status_string(0) == b"EXATTN_OK"
@@ -136,6 +137,46 @@ def test_decode_rejects(L, name, kw, status):
     a = _dec(**kw)
     assert L.exattn_decode_plan(C.byref(a), None, None) == status, L.exattn_last_error()
     assert L.exattn_decode(C.byref(a), None, 0, None) == status, L.exattn_last_error()
+
+
+def _kvn(**kw):
+    n = ex.KvNew()
+    n.k_new = n.v_new = FAKE
+    n.seqlen_new = 2
+    n.k_new_stride[:] = [2 * 8 * 128, 8 * 128, 128]
+    n.v_new_stride[:] = [2 * 8 * 128, 8 * 128, 128]
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(n, key)[:] = val
+        else:
+            setattr(n, key, val)
+    return n
+
+
+BAD_APPEND = [
+    ("no cache_seqlens", dict(), dict(), ex.EXATTN_E_INVALID),
+    ("negative seqlen_new", dict(cache_seqlens=FAKE), dict(seqlen_new=-1), ex.EXATTN_E_INVALID),
+    ("longer than the cache", dict(cache_seqlens=FAKE, seqlen_cache=1), dict(), ex.EXATTN_E_INVALID),
+    ("null k_new", dict(cache_seqlens=FAKE), dict(k_new=None), ex.EXATTN_E_INVALID),
+    ("misaligned v_new", dict(cache_seqlens=FAKE), dict(v_new=FAKE + 8), ex.EXATTN_E_INVALID),
+    ("odd stride", dict(cache_seqlens=FAKE), dict(k_new_stride=[2048, 1028, 128]), ex.EXATTN_E_INVALID),
+    ("bad decode args", dict(cache_seqlens=FAKE, head_dim=80), dict(), ex.EXATTN_E_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,dkw,nkw,status", BAD_APPEND, ids=[c[0] for c in BAD_APPEND])
+def test_decode_append_rejects(L, name, dkw, nkw, status):
+    a, n = _dec(**dkw), _kvn(**nkw)
+    assert L.exattn_decode_append(C.byref(a), C.byref(n), C.c_void_p(FAKE), 1 << 30, None) == status, \
+        L.exattn_last_error()
+
+
+def test_decode_append_null_and_empty(L):
+    a = _dec(cache_seqlens=FAKE)
+    assert L.exattn_decode_append(C.byref(a), None, None, 0, None) == ex.EXATTN_E_INVALID
+    # nothing to attend: batch 0 launches nothing, whatever kv_new holds
+    assert L.exattn_decode_append(C.byref(_dec(batch=0)), C.byref(_kvn(seqlen_new=3)), None, 0,
+                                  None) == ex.EXATTN_OK
 
 
 def test_decode_workspace_checks(L):

@@ -206,6 +206,65 @@ def test_decode_kvcache():
     assert_lse_close(lse, l_ref, "decode")
 
 
+APPEND_CASES = [
+    # b, s_cache, h_q, h_kv, d, dtype, lens, s_new, window, softcap, splits, seed
+    (4, 2048, 32, 8, 128, torch.bfloat16, [0, 5, 1000, 2045], 3, (-1, -1), 0.0, 0, 160),
+    (3, 777, 16, 2, 64, torch.float16, [1, 300, 770], 7, (100, -1), 30.0, 0, 161),
+    (2, 4096, 8, 8, 256, torch.bfloat16, [4000, 17], 1, (-1, -1), 0.0, 5, 162),
+    (2, 1000, 16, 4, 128, torch.float16, [999, 0], 1, (-1, -1), 0.0, 1, 163),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"a{c[-1]}" for c in APPEND_CASES])
+def test_decode_append(case):
+    """k/v appended at cache_seqlens[b] (FAQ Q17), then attended: O and LSE against
+    the oracle, the new cache rows bit-exact, every other row untouched, and
+    cache_seqlens unchanged."""
+    b, s_cache, hq, hkv, d, dt, lens, s_new, window, cap, splits, seed = case
+    q, kc, vc = W.kvcache(b, s_cache, hq, hkv, d, seed=seed, dtype=dt)
+    kn, vn = W.kv_new(b, s_new, hkv, d, seed=seed + 1000, dtype=dt)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens_t)
+    dkv = torch.stack([kn, vn], dim=2).to(DEV)  # the packed (b, s_new, 2, h_kv, d) draw
+    dkn, dvn = dkv[:, :, 0], dkv[:, :, 1]
+    assert dkn.stride(1) == 2 * hkv * d  # strided views
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((b, hq, 1))
+    ex.attn_with_kvcache(dq, dkc, dvc, k=dkn, v=dvn, cache_seqlens=dl, causal=True, window_size=window,
+                         softcap=cap, num_splits=splits, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref, kc_ref, vc_ref = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens_t, causal=True,
+                                                                   window_size=window, softcap=cap)
+    assert_o_close(out, o_ref, dt, "append")
+    assert_lse_close(lse, l_ref, "append")
+    assert torch.equal(dkc.cpu(), kc_ref) and torch.equal(dvc.cpu(), vc_ref)
+    assert torch.equal(dl.cpu(), lens_t)
+
+
+def test_decode_append_steps():
+    """Token-by-token decoding as in FAQ Q17: append one token, attend, then the
+    caller advances cache_seqlens; four steps against the oracle."""
+    b, s_cache, hq, hkv, d = 3, 600, 16, 4, 128
+    q, kc, vc = W.kvcache(b, s_cache, hq, hkv, d, seed=170)
+    dkc, dvc = _dev(kc, vc)
+    lens = torch.tensor([0, 100, 590], dtype=torch.int32)
+    dl = lens.to(DEV)
+    kc_ref, vc_ref = kc.clone(), vc.clone()
+    for step in range(4):
+        kn, vn = W.kv_new(b, 1, hkv, d, seed=171 + step)
+        qs = W.kvcache(b, 1, hq, hkv, d, seed=180 + step)[0]
+        out, lse = ex.attn_with_kvcache(qs.to(DEV), dkc, dvc, k=kn.to(DEV), v=vn.to(DEV), cache_seqlens=dl,
+                                        causal=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref, kc_ref, vc_ref = oracle.attention_kvcache_append(qs, kc_ref, vc_ref, kn, vn, lens,
+                                                                       causal=True)
+        assert_o_close(out, o_ref, qs.dtype, f"append step {step}")
+        assert_lse_close(lse, l_ref, f"append step {step}")
+        dl += 1
+        lens += 1
+    assert torch.equal(dkc.cpu(), kc_ref) and torch.equal(dvc.cpu(), vc_ref)
+
+
 # --------------------------------------------------------------------------
 # masks, tails and degenerate cases
 # --------------------------------------------------------------------------

@@ -347,6 +347,42 @@ def pin_decode():
         assert abs(lse[bi, 0, 0] - math.log(n - lo)) < 1e-13
 
 
+def pin_decode_append():
+    """Append then attend (FAQ Q17), pinned from the inputs themselves: with
+    Q = 0 every visible score is 0, so O is the mean of the old rows
+    0..n-1 and the new rows, LSE = ln(n + s_new); the cache copy keeps every
+    other row; with an empty cache and one new token O = v_new, LSE = scale q.k_new."""
+    r = _rng(22)
+    b, s_cache, h_q, h_kv, d, s_new = 3, 40, 4, 2, 8, 3
+    kc = r.standard_normal((b, s_cache, h_kv, d))
+    vc = r.standard_normal((b, s_cache, h_kv, d))
+    kn = r.standard_normal((b, s_new, h_kv, d))
+    vn = r.standard_normal((b, s_new, h_kv, d))
+    lens = [0, 5, 30]
+    q = np.zeros((b, 1, h_q, d))
+    o, lse, kc2, vc2 = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens, causal=True)
+    for bi, n in enumerate(lens):
+        for h in range(h_q):
+            hk = h // 2
+            assert abs(lse[bi, h, 0] - math.log(n + s_new)) < 1e-13
+            mean = (vc[bi, :n, hk].sum(axis=0) + vn[bi, :, hk].sum(axis=0)) / (n + s_new)
+            assert np.allclose(o[bi, 0, h], mean, atol=1e-13)
+        keep = [j for j in range(s_cache) if not n <= j < n + s_new]
+        assert np.array_equal(kc2[bi, keep], kc[bi, keep]) and np.array_equal(vc2[bi, keep], vc[bi, keep])
+        assert np.array_equal(kc2[bi, n:n + s_new], kn[bi]) and np.array_equal(vc2[bi, n:n + s_new], vn[bi])
+    assert np.array_equal(kc[1, 5], kc[1, 5])  # inputs untouched (copies)
+    # empty cache, one new token
+    q1 = r.standard_normal((1, 1, 1, d))
+    o1, l1, _, _ = oracle.attention_kvcache_append(q1, kc[:1, :, :1], vc[:1, :, :1], kn[:1, :1, :1],
+                                                   vn[:1, :1, :1], [0])
+    assert np.allclose(o1[0, 0, 0], vn[0, 0, 0], atol=1e-14)
+    assert abs(l1[0, 0, 0] - float(q1[0, 0, 0] @ kn[0, 0, 0]) / math.sqrt(d)) < 1e-12
+    # rows past the capacity are dropped
+    _, _, kc3, _ = oracle.attention_kvcache_append(q[:1], kc[:1], vc[:1], kn[:1], vn[:1], [s_cache - 2])
+    assert np.array_equal(kc3[0, s_cache - 2:], kn[0, :2]) and np.array_equal(kc3[0, :s_cache - 2],
+                                                                                kc[0, :s_cache - 2])
+
+
 def pin_softcap():
     r = _rng(19)
     q = r.standard_normal((1, 6, 2, 16)) * 4
@@ -388,7 +424,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_softcap,
         pin_default_scale]
 
 
@@ -442,8 +478,14 @@ def _bad_kv_head_modulo(h, h_q, h_kv):
     return h % h_kv
 
 
+def _bad_append_offset(k_cache, v_cache, cache_seqlens, k_new, v_new):
+    return OA_append(k_cache, v_cache, [max(0, int(n) - 1) for n in np.asarray(cache_seqlens)], k_new,
+                     v_new)
+
+
 OA_visible = OA.visible
 OA_softmax = OA.softmax_rows
+OA_append = OA.kvcache_append
 
 MUTATIONS = [
     ("scores", _bad_scores_noscale),
@@ -456,6 +498,7 @@ MUTATIONS = [
     ("softmax_rows", _bad_softmax_lse_nomax),
     ("softmax_rows", _bad_softmax_sign),
     ("_kv_head", _bad_kv_head_modulo),
+    ("kvcache_append", _bad_append_offset),
 ]
 
 
