@@ -200,6 +200,27 @@ def run_decode(ex, W, args):
     nbytes = W.algorithmic_bytes(w)
     gbs = nbytes / (ms_avg * 1e-3) / 1e9
     traffic = measured_traffic("decode_b8_h32x8_d128_cache16384", DECODE_SOURCES)
+
+    # The same step with a one-token append (FAQ Q17): each batch entry's new K/V row is written
+    # at cache_seqlens[b] = 16383 and the query attends to all 16384 rows, as above.
+    kn, vn = W.kv_new(w.batch, 1, w.heads_kv, w.head_dim, seed=w.seed + 1)
+    kn, vn = kn.cuda(), vn.cuda()
+    lens_app = lens - 1
+
+    def step_app():
+        ex.attn_with_kvcache(q, kc, vc, k=kn, v=vn, cache_seqlens=lens_app, out=out, lse=lse,
+                             workspace=ws)
+
+    ta = time_steps(step_app, steps, max(2, args.warmup // 4), between)
+    new_bytes = 2 * 2 * kn.numel() * kn.element_size()  # read k_new, v_new and write them into the cache
+    gbs_app = (nbytes + new_bytes) / (ta["pair_avg"] * 1e-3) / 1e9
+    append = {
+        "workload": "the same decode with a one-token k/v append at cache_seqlens = 16383",
+        "value": round(gbs_app, 2), "unit": "GB/s", "ms_per_call_avg": round(ta["pair_avg"], 5),
+        "ms_per_call_median": round(ta["pair_median"], 5), "ms_per_call_min": round(ta["pair_min"], 5),
+        "calls": steps, "algorithmic_bytes": nbytes + new_bytes,
+        "frac": round(gbs_app / PEAK_HBM_GBS, 4),
+    }
     return {
         "workload": "kvcache decode b8 s_q1 cache16384 h_q32 h_kv8 d128 bf16",
         "num_splits": ns, "value": round(gbs, 2), "unit": "GB/s",
@@ -209,6 +230,7 @@ def run_decode(ex, W, args):
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": nbytes},
         "cache_flush": "1 GiB read of another buffer between calls (outside the event pairs)",
+        "append": append,
     }
 
 

@@ -174,29 +174,16 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(EXATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
     }
-    if (s_new > 0) {
-      AppendParams ap{};
-      ap.k_new = static_cast<const uint16_t*>(kv_new->k_new);
-      ap.v_new = static_cast<const uint16_t*>(kv_new->v_new);
-      ap.k = static_cast<uint16_t*>(const_cast<void*>(a->k_cache));
-      ap.v = static_cast<uint16_t*>(const_cast<void*>(a->v_cache));
-      ap.kn_sb = kv_new->k_new_stride[0], ap.kn_ss = kv_new->k_new_stride[1];
-      ap.kn_sh = kv_new->k_new_stride[2];
-      ap.vn_sb = kv_new->v_new_stride[0], ap.vn_ss = kv_new->v_new_stride[1];
-      ap.vn_sh = kv_new->v_new_stride[2];
-      ap.k_sb = a->k_stride[0], ap.k_ss = a->k_stride[1], ap.k_sh = a->k_stride[2];
-      ap.v_sb = a->v_stride[0], ap.v_ss = a->v_stride[1], ap.v_sh = a->v_stride[2];
-      ap.cache_seqlens = a->cache_seqlens;
-      ap.batch = a->batch;
-      ap.s_new = s_new;
-      ap.h_kv = a->heads_kv;
-      ap.head_dim = a->head_dim;
-      ap.s_cache = a->seqlen_cache;
-      hipError_t e = launch_append(ap, static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("append launch: ") + hipGetErrorString(e));
-    }
     DecParams p{};
     p.seq_add = s_new;
+    if (s_new > 0) {
+      p.k_new = static_cast<const uint16_t*>(kv_new->k_new);
+      p.v_new = static_cast<const uint16_t*>(kv_new->v_new);
+      p.kn_sb = kv_new->k_new_stride[0], p.kn_ss = kv_new->k_new_stride[1];
+      p.kn_sh = kv_new->k_new_stride[2];
+      p.vn_sb = kv_new->v_new_stride[0], p.vn_ss = kv_new->v_new_stride[1];
+      p.vn_sh = kv_new->v_new_stride[2];
+    }
     p.q = static_cast<const uint16_t*>(a->q);
     p.k = static_cast<const uint16_t*>(a->k_cache);
     p.v = static_cast<const uint16_t*>(a->v_cache);

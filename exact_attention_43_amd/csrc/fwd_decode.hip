@@ -234,6 +234,42 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     }
   };
 
+  // ---- append (FAQ Q17): the new tokens go to cache rows cache_seqlens[b] + t
+  // before they are attended.  Each work group writes the new rows of its own
+  // KV heads that fall in its own key range (split 0 also those left of the
+  // window), so every row is read only by work groups that wrote it
+  // themselves: a wait for the stores and the barrier order them before the
+  // DMA.  Work groups for other query heads of the same KV heads write the
+  // same bytes.
+  if (p.seq_add > 0) {  // uniform
+    const int base = p.cache_seqlens[b];
+    const int lo = kb + s_lo * KSTEP, hi = kb + s_hi * KSTEP;
+    constexpr int CPR = D / 8;  // 16-byte chunks per head row
+    const int n = nh_valid * CPR;
+    uint16_t* kw = const_cast<uint16_t*>(kg);
+    uint16_t* vw = const_cast<uint16_t*>(vg);
+    for (int idx = tid; idx < p.seq_add * 2 * n; idx += NW * 64) {
+      const int t = idx / (2 * n);
+      const int c = idx - t * 2 * n;
+      const int pos = base + t;
+      const bool mine =
+          pos >= 0 && pos < p.s_cache && ((pos >= lo && pos < hi) || (split == 0 && pos < kb));
+      if (!mine) continue;
+      const bool is_v = c >= n;
+      const int cc = is_v ? c - n : c;
+      const int hh = cc / CPR, j = cc - hh * CPR;
+      const int64_t hd = (int64_t)(hk0 + hh);
+      const uint16_t* src =
+          is_v ? p.v_new + (int64_t)b * p.vn_sb + (int64_t)t * p.vn_ss + hd * p.vn_sh
+               : p.k_new + (int64_t)b * p.kn_sb + (int64_t)t * p.kn_ss + hd * p.kn_sh;
+      uint16_t* dst = is_v ? vw + (int64_t)pos * p.v_ss + (int64_t)hh * p.v_sh
+                           : kw + (int64_t)pos * p.k_ss + (int64_t)hh * p.k_sh;
+      *(u32x4_t*)(dst + 8 * j) = *(const u32x4_t*)(src + 8 * j);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
   if (s_lo < s_hi) issue(s_lo, smem);
   for (int st = s_lo; st < s_hi; ++st) {
     // this work group's loads of step st have landed, and every wave is done
@@ -410,37 +446,6 @@ hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softc
                          hipStream_t stream) {
   return bf16 ? launch_t<true>(p, head_dim, softcap, stream)
               : launch_t<false>(p, head_dim, softcap, stream);
-}
-
-namespace {
-
-// One work group per (new token t, batch entry b): its threads copy the
-// token's K and V rows of every KV head, 16 bytes each, to cache row
-// cache_seqlens[b] + t (FAQ Q17: the new tokens are appended, then attended).
-__global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
-  const int t = blockIdx.x;
-  const int b = blockIdx.y;
-  const int pos = p.cache_seqlens[b] + t;
-  if (pos < 0 || pos >= p.s_cache) return;  // outside the cache: not written
-  const int cpr = p.head_dim / 8;  // 16-byte chunks per head row
-  const int n = p.h_kv * cpr;
-  for (int c = threadIdx.x; c < 2 * n; c += blockDim.x) {
-    const bool is_v = c >= n;
-    const int cc = is_v ? c - n : c;
-    const int h = cc / cpr, j = cc % cpr;
-    const uint16_t* src = is_v ? p.v_new + (int64_t)b * p.vn_sb + (int64_t)t * p.vn_ss + (int64_t)h * p.vn_sh
-                               : p.k_new + (int64_t)b * p.kn_sb + (int64_t)t * p.kn_ss + (int64_t)h * p.kn_sh;
-    uint16_t* dst = is_v ? p.v + (int64_t)b * p.v_sb + (int64_t)pos * p.v_ss + (int64_t)h * p.v_sh
-                         : p.k + (int64_t)b * p.k_sb + (int64_t)pos * p.k_ss + (int64_t)h * p.k_sh;
-    *(u32x4_t*)(dst + 8 * j) = *(const u32x4_t*)(src + 8 * j);
-  }
-}
-
-}  // namespace
-
-hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(append_kernel, dim3(p.s_new, p.batch), dim3(256), 0, stream, p);
-  return hipGetLastError();
 }
 
 }  // namespace exattn

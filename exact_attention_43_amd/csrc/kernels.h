@@ -51,20 +51,13 @@ struct DecParams {
   int32_t hpw;            // adjacent KV heads per work group (a power of two)
   float scale_log2, cap_in, cap_out_log2;
   int32_t wl;
-  int32_t seq_add;  // keys per batch entry = cache_seqlens[b] + seq_add (new tokens appended)
-};
-
-// Writes new tokens into the KV cache: row cache_seqlens[b] + t of k/v gets
-// token t of k_new/v_new (rows outside [0, s_cache) are skipped).
-struct AppendParams {
+  // Append: seq_add new tokens (k_new / v_new, (batch, seq_add, h_kv, d) by
+  // the kn_* / vn_* strides) are written to cache rows cache_seqlens[b] + t
+  // and attended with the rest: keys per batch entry = cache_seqlens[b] + seq_add.
+  int32_t seq_add;
   const uint16_t* k_new;
   const uint16_t* v_new;
-  uint16_t* k;
-  uint16_t* v;
   int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;
-  int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
-  const int32_t* cache_seqlens;
-  int32_t batch, s_new, h_kv, head_dim, s_cache;
 };
 
 int prefill_rows_per_tile();
@@ -73,6 +66,5 @@ hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool soft
                           int groups, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softcap,
                          hipStream_t stream);
-hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 
 }  // namespace exattn

@@ -181,7 +181,8 @@ typedef struct {
  * gives wrong values but no out-of-bounds access.  Cache rows other than the
  * new ones are left unchanged.  workspace as for exattn_decode (the same
  * plan applies: exattn_decode_plan on args).  seqlen_new = 0 is exattn_decode.
- * The write and the attention are two kernels in order on the stream. */
+ * The rows are written by the decode kernel itself, each by the work groups
+ * that read them, before they read them. */
 exattn_status exattn_decode_append(const exattn_decode_args *args, const exattn_kv_new *kv_new,
                                    void *workspace, size_t workspace_bytes, void *stream);
 

@@ -212,6 +212,8 @@ APPEND_CASES = [
     (3, 777, 16, 2, 64, torch.float16, [1, 300, 770], 7, (100, -1), 30.0, 0, 161),
     (2, 4096, 8, 8, 256, torch.bfloat16, [4000, 17], 1, (-1, -1), 0.0, 5, 162),
     (2, 1000, 16, 4, 128, torch.float16, [999, 0], 1, (-1, -1), 0.0, 1, 163),
+    (2, 500, 8, 2, 128, torch.bfloat16, [10, 200], 7, (3, -1), 0.0, 4, 164),   # new rows left of the window
+    (2, 300, 12, 6, 128, torch.float16, [0, 250], 2, (-1, -1), 0.0, 0, 165),   # a partial KV-head group
 ]
 
 
