@@ -221,6 +221,29 @@ def run_decode(ex, W, args):
         "calls": steps, "algorithmic_bytes": nbytes + new_bytes,
         "frac": round(gbs_app / PEAK_HBM_GBS, 4),
     }
+    # The same decode over a paged cache (FAQ Q18): 256-token pages of the same K/V, placed at a
+    # seeded random permutation of the pool's page slots.
+    page = 256
+    per_seq = w.seqlen_k // page
+    perm = torch.randperm(w.batch * per_seq, generator=torch.Generator().manual_seed(w.seed + 2))
+    bt = perm.to(torch.int32).reshape(w.batch, per_seq).cuda()
+    kpool = torch.empty((w.batch * per_seq, page, w.heads_kv, w.head_dim), dtype=kc.dtype, device="cuda")
+    vpool = torch.empty_like(kpool)
+    kpool[perm.cuda()] = kc.reshape(w.batch * per_seq, page, w.heads_kv, w.head_dim)
+    vpool[perm.cuda()] = vc.reshape(w.batch * per_seq, page, w.heads_kv, w.head_dim)
+
+    def step_paged():
+        ex.attn_with_kvcache(q, kpool, vpool, cache_seqlens=lens, out=out, lse=lse, workspace=ws,
+                             block_table=bt)
+
+    tp = time_steps(step_paged, steps, max(2, args.warmup // 4), between)
+    gbs_pg = nbytes / (tp["pair_avg"] * 1e-3) / 1e9
+    paged = {
+        "workload": "the same decode over a paged cache: 256-token pages in a random pool order",
+        "value": round(gbs_pg, 2), "unit": "GB/s", "ms_per_call_avg": round(tp["pair_avg"], 5),
+        "ms_per_call_median": round(tp["pair_median"], 5), "ms_per_call_min": round(tp["pair_min"], 5),
+        "calls": steps, "algorithmic_bytes": nbytes, "frac": round(gbs_pg / PEAK_HBM_GBS, 4),
+    }
     return {
         "workload": "kvcache decode b8 s_q1 cache16384 h_q32 h_kv8 d128 bf16",
         "num_splits": ns, "value": round(gbs, 2), "unit": "GB/s",
@@ -231,6 +254,7 @@ def run_decode(ex, W, args):
                      "algorithmic_bytes": nbytes},
         "cache_flush": "1 GiB read of another buffer between calls (outside the event pairs)",
         "append": append,
+        "paged": paged,
     }
 
 

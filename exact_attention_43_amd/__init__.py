@@ -75,6 +75,14 @@ class KvNew(C.Structure):
     ]
 
 
+class PagedKv(C.Structure):
+    """Mirror of exattn_paged_kv."""
+    _fields_ = [
+        ("block_table", C.c_void_p), ("block_table_stride", C.c_int32), ("page_size", C.c_int32),
+        ("num_pages", C.c_int32), ("k_page_stride", C.c_int64), ("v_page_stride", C.c_int64),
+    ]
+
+
 _lib_handle = None
 _lib_lock = threading.Lock()
 
@@ -104,6 +112,9 @@ def lib():
             L.exattn_decode_append.argtypes = [C.POINTER(DecodeArgs), C.POINTER(KvNew), C.c_void_p,
                                                C.c_size_t, C.c_void_p]
             L.exattn_decode_append.restype = C.c_int
+            L.exattn_decode_paged.argtypes = [C.POINTER(DecodeArgs), C.POINTER(PagedKv), C.POINTER(KvNew),
+                                              C.c_void_p, C.c_size_t, C.c_void_p]
+            L.exattn_decode_paged.restype = C.c_int
             L.exattn_decode_auto_splits.argtypes = [C.c_int32] * 6
             L.exattn_decode_auto_splits.restype = C.c_int32
             L.exattn_args_size.argtypes = [C.c_int32]
@@ -115,7 +126,7 @@ def lib():
             L.exattn_abi_version.argtypes = []
             L.exattn_abi_version.restype = C.c_int32
             if (L.exattn_args_size(0) != C.sizeof(FwdArgs) or L.exattn_args_size(1) != C.sizeof(DecodeArgs)
-                    or L.exattn_args_size(2) != C.sizeof(KvNew)):
+                    or L.exattn_args_size(2) != C.sizeof(KvNew) or L.exattn_args_size(3) != C.sizeof(PagedKv)):
                 raise RuntimeError("libexattn.so struct layout does not match this binding; rebuild it")
             _lib_handle = L
     return _lib_handle
@@ -297,9 +308,11 @@ def _workspace(dev, nbytes):
 
 
 def _decode_args(q, k_cache, v_cache, out, lse, cache_seqlens, softmax_scale, causal, window_size,
-                 softcap, num_splits):
+                 softcap, num_splits, block_table=None):
     b, h_q, d = q.shape[0], q.shape[-2], q.shape[-1]
     s_cache, h_kv = k_cache.shape[1], k_cache.shape[2]
+    if block_table is not None:  # pools of pages: capacity = pages per sequence x page size
+        s_cache = block_table.shape[1] * k_cache.shape[1]
     a = DecodeArgs()
     a.dtype = _dtype_code(q)
     a.batch, a.heads_q, a.heads_kv, a.head_dim, a.seqlen_cache = b, h_q, h_kv, d, s_cache
@@ -309,6 +322,9 @@ def _decode_args(q, k_cache, v_cache, out, lse, cache_seqlens, softmax_scale, ca
     a.o_stride[:] = [out.stride(0), out.stride(-2)]
     a.k_stride[:] = list(k_cache.stride()[:3])
     a.v_stride[:] = list(v_cache.stride()[:3])
+    if block_table is not None:  # the batch stride is replaced by the page table
+        a.k_stride[0] = 0
+        a.v_stride[0] = 0
     a.cache_seqlens = cache_seqlens.data_ptr() if cache_seqlens is not None else None
     a.softmax_scale = _scale(softmax_scale)
     a.softcap = float(softcap or 0.0)
@@ -319,10 +335,10 @@ def _decode_args(q, k_cache, v_cache, out, lse, cache_seqlens, softmax_scale, ca
 
 
 def decode_plan(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, causal=False,
-                window_size=(-1, -1), softcap=0.0, num_splits=0):
+                window_size=(-1, -1), softcap=0.0, num_splits=0, block_table=None):
     """(num_splits, workspace_bytes) the library would use for this decode call."""
     a = _decode_args(q, k_cache, v_cache, q, None, cache_seqlens, softmax_scale, causal, window_size,
-                     softcap, num_splits)
+                     softcap, num_splits, block_table)
     ns = C.c_int32(0)
     wb = C.c_size_t(0)
     with torch.cuda.device(q.device):
@@ -333,7 +349,7 @@ def decode_plan(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, cau
 
 def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, softmax_scale=None,
                       causal=False, window_size=(-1, -1), softcap=0.0, num_splits=0, out=None, lse=None,
-                      workspace=None):
+                      workspace=None, block_table=None):
     """KV-cache decode with one query token (FAQ Q17).
 
     q (b, 1, h_q, d); k_cache, v_cache (b, s_cache, h_kv, d); cache_seqlens an
@@ -343,7 +359,9 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     updated in place) and the query attends to cache_seqlens[b] + s_new rows;
     cache_seqlens is required then.  The call never changes cache_seqlens (the
     caller advances it by s_new).  num_splits = 0 picks the split count
-    automatically (FAQ Q14).
+    automatically (FAQ Q14).  With block_table (b, pages per sequence) int32 the
+    caches are page pools (num_pages, page_size, h_kv, d) (FAQ Q18): token j of
+    batch entry b is row j % page_size of page block_table[b, j // page_size].
     """
     if (k is None) != (v is None):
         raise ValueError("pass both k and v to append, or neither")
@@ -354,7 +372,17 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share one dtype")
     _on_gpu(q, k_cache, v_cache, out, lse, cache_seqlens if torch.is_tensor(cache_seqlens) else None,
-            workspace, k, v)
+            workspace, k, v, block_table)
+    pg = None
+    if block_table is not None:
+        if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != q.shape[0]
+                or block_table.stride(1) != 1):
+            raise ValueError("block_table must be an int32 (batch, pages per sequence) tensor, rows contiguous")
+        pg = PagedKv()
+        pg.block_table = block_table.data_ptr()
+        pg.block_table_stride = block_table.stride(0)
+        pg.page_size, pg.num_pages = k_cache.shape[1], k_cache.shape[0]
+        pg.k_page_stride, pg.v_page_stride = k_cache.stride(0), v_cache.stride(0)
     _check_last_dim(q, k_cache, v_cache)
     b, _, h_q, d = q.shape
     kv = None
@@ -380,7 +408,7 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     if lse is None:
         lse = torch.empty((b, h_q, 1), dtype=torch.float32, device=q.device)
     a = _decode_args(q[:, 0], k_cache, v_cache, out[:, 0], lse, cache_seqlens, softmax_scale, causal,
-                     window_size, softcap, num_splits)
+                     window_size, softcap, num_splits, block_table)
     L = lib()
     with torch.cuda.device(q.device):
         ns = C.c_int32(0)
@@ -394,11 +422,15 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
         ws = C.c_void_p(ws_ptr) if ws_ptr else None
         strm = C.c_void_p(_stream(q.device))
-        if kv is None:
-            st = L.exattn_decode(C.byref(a), ws, ws_bytes, strm)
+        if pg is not None:
+            st = L.exattn_decode_paged(C.byref(a), C.byref(pg), C.byref(kv) if kv is not None else None, ws,
+                                       ws_bytes, strm)
+            what = "exattn_decode_paged"
+        elif kv is None:
+            st, what = L.exattn_decode(C.byref(a), ws, ws_bytes, strm), "exattn_decode"
         else:
-            st = L.exattn_decode_append(C.byref(a), C.byref(kv), ws, ws_bytes, strm)
-    _raise_for(st, "exattn_decode" if kv is None else "exattn_decode_append")
+            st, what = L.exattn_decode_append(C.byref(a), C.byref(kv), ws, ws_bytes, strm), "exattn_decode_append"
+    _raise_for(st, what)
     return out, lse
 
 

@@ -146,8 +146,9 @@ namespace {
 // The decode behind exattn_decode and exattn_decode_append: kv_new (or NULL)
 // is written into the cache first, and the attended length per batch entry is
 // cache_seqlens[b] + its seqlen_new.
-exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_new, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_new,
+                         const exattn_paged_kv* paged, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   try {
     clear_error();
     DecodePlan pl;
@@ -155,6 +156,10 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
     if (st != EXATTN_OK) return st;
     if (kv_new != nullptr) {
       st = check_append(a, kv_new);
+      if (st != EXATTN_OK) return st;
+    }
+    if (paged != nullptr) {
+      st = check_paged(a, pl, paged);
       if (st != EXATTN_OK) return st;
     }
     const int32_t s_new = kv_new != nullptr && a->batch > 0 ? kv_new->seqlen_new : 0;
@@ -175,6 +180,14 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
         return fail(EXATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
     }
     DecParams p{};
+    if (paged != nullptr) {
+      p.block_table = paged->block_table;
+      p.bt_stride = paged->block_table_stride;
+      p.page_size = paged->page_size;
+      p.num_pages = paged->num_pages;
+      p.k_sp = paged->k_page_stride;
+      p.v_sp = paged->v_page_stride;
+    }
     p.seq_add = s_new;
     if (s_new > 0) {
       p.k_new = static_cast<const uint16_t*>(kv_new->k_new);
@@ -229,7 +242,7 @@ extern "C" {
 
 exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  return run_decode(a, nullptr, workspace, workspace_bytes, stream);
+  return run_decode(a, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 exattn_status exattn_decode_append(const exattn_decode_args* a, const exattn_kv_new* kv_new,
@@ -238,7 +251,17 @@ exattn_status exattn_decode_append(const exattn_decode_args* a, const exattn_kv_
     clear_error();
     return fail(EXATTN_E_INVALID, "kv_new is NULL");
   }
-  return run_decode(a, kv_new, workspace, workspace_bytes, stream);
+  return run_decode(a, kv_new, nullptr, workspace, workspace_bytes, stream);
+}
+
+exattn_status exattn_decode_paged(const exattn_decode_args* a, const exattn_paged_kv* paged,
+                                  const exattn_kv_new* kv_new, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (paged == nullptr) {
+    clear_error();
+    return fail(EXATTN_E_INVALID, "paged is NULL");
+  }
+  return run_decode(a, kv_new, paged, workspace, workspace_bytes, stream);
 }
 
 int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv,
@@ -250,6 +273,7 @@ size_t exattn_args_size(int32_t which) {
   return which == 0   ? sizeof(exattn_fwd_args)
          : which == 1 ? sizeof(exattn_decode_args)
          : which == 2 ? sizeof(exattn_kv_new)
+         : which == 3 ? sizeof(exattn_paged_kv)
                       : 0;
 }
 

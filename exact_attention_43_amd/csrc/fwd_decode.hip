@@ -56,11 +56,10 @@ __device__ __forceinline__ int vswz(int key) { return D >= 128 ? 2 * (key & 7) :
 // last valid element return zeros (per-dword range check of raw buffer loads).
 // Word 3 is the gfx9 default.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* g, int64_t ss, int64_t sh,
-                                                            int kbase, int nk, int nh, int rows) {
-  const int64_t last = (int64_t)min(nk - 1 - kbase, rows - 1) * ss + (int64_t)(nh - 1) * sh + D;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)kbase * ss), 0, (int)(last * 2),
-                                           0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* row0, int64_t ss, int64_t sh,
+                                                            int nrows, int nh) {
+  const int64_t last = (int64_t)(nrows - 1) * ss + (int64_t)(nh - 1) * sh + D;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)row0, 0, (int)(last * 2), 0x00020000);
 }
 
 // 16 bytes per lane from a buffer into LDS at lds + 16 * lane (lds must be
@@ -71,7 +70,7 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, uin
                                            0, 0, 0);
 }
 
-template <bool BF16, int D, bool SOFTCAP, int HPWV>
+template <bool BF16, int D, bool SOFTCAP, int HPWV, bool PAGED>
 __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecParams p) {
   using E = Elem<BF16>;
   constexpr int NW = DecCfg<D>::NW;
@@ -111,7 +110,11 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   const int nk = p.cache_seqlens != nullptr ? min(max(p.cache_seqlens[b] + p.seq_add, 0), p.s_cache)
                                             : p.s_cache;
   // The query sits at position nk - 1; only the left window edge removes keys.
-  const int kb = p.wl >= 0 ? max(0, nk - 1 - p.wl) : 0;
+  // A paged cache starts the steps on a multiple of the step size, so that a
+  // step never straddles a page, and masks the keys before kb_w.
+  constexpr bool paged = PAGED;  // p.block_table != nullptr
+  const int kb_w = p.wl >= 0 ? max(0, nk - 1 - p.wl) : 0;
+  const int kb = paged ? kb_w - kb_w % KSTEP : kb_w;
   const int nsteps = nk > kb ? (nk - kb + KSTEP - 1) / KSTEP : 0;
   const int per = (nsteps + p.n_split - 1) / p.n_split;
   const int s_lo = split * per;
@@ -133,11 +136,29 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     kofs[t] = (uint32_t)((key * p.k_ss + head * p.k_sh) * 2 + 16 * (pos ^ kswz(key)));
     vofs[t] = (uint32_t)((key * p.v_ss + head * p.v_sh) * 2 + 16 * (pos ^ vswz<D>(key)));
   }
-  // DMA of step st's K and V tiles into the stage at dst.
-  auto issue = [&](int st, uint8_t* dst) {
+  // Page of the cache row `key` (paged cache), clamped to the pool.  The table
+  // is read through the constant address space: a scalar load, whose wait is
+  // separate from the DMA's (a vector load would need the DMA count drained
+  // before its value could move to a scalar register).
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)p.block_table;
+  auto page_of = [&](int key) {
+    const int pg = bt[(int64_t)b * p.bt_stride + key / p.page_size];
+    return min(max(pg, 0), p.num_pages - 1);
+  };
+  // DMA of step st's K and V tiles into the stage at dst; pg: its page if paged.
+  auto issue = [&](int st, uint8_t* dst, int pg) {
     const int kbase = kb + st * KSTEP;
-    const __amdgpu_buffer_rsrc_t rk = rows_rsrc<D>(kg, p.k_ss, p.k_sh, kbase, nk, nh_valid, KSTEP);
-    const __amdgpu_buffer_rsrc_t rv = rows_rsrc<D>(vg, p.v_ss, p.v_sh, kbase, nk, nh_valid, KSTEP);
+    const int nrows = min(nk - kbase, KSTEP);
+    const uint16_t* k0 = kg + (int64_t)kbase * p.k_ss;
+    const uint16_t* v0 = vg + (int64_t)kbase * p.v_ss;
+    if (paged) {
+      const int64_t r = kbase % p.page_size;
+      k0 = p.k + (int64_t)pg * p.k_sp + r * p.k_ss + (int64_t)hk0 * p.k_sh;
+      v0 = p.v + (int64_t)pg * p.v_sp + r * p.v_ss + (int64_t)hk0 * p.v_sh;
+    }
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc<D>(k0, p.k_ss, p.k_sh, nrows, nh_valid);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc<D>(v0, p.v_ss, p.v_sh, nrows, nh_valid);
 #pragma unroll
     for (int t = 0; t < KI; ++t) buffer_load_lds16(rk, dst + (wave + NW * t) * 1024, kofs[t]);
 #pragma unroll
@@ -188,8 +209,13 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   // from stage cur.  The two stages never overlap; restrict tells the compiler
   // so, which lets the operand reads of cur proceed while the DMA into nxt is
   // in flight (without it every LDS read waits for all outstanding DMA).
+  // pg_next: the page of the next step to issue, read one step ahead.
+  int pg_next = 0;
   auto step = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int st) {
-    if (st + 1 < s_hi) issue(st + 1, nxt);
+    if (st + 1 < s_hi) {
+      issue(st + 1, nxt, pg_next);
+      if (paged && st + 2 < s_hi) pg_next = page_of(kb + (st + 2) * KSTEP);
+    }
     const uint8_t* kt = cur;
     const uint8_t* vt = cur + KTILE;
     const int key0 = kb + st * KSTEP + 16 * sub;  // first key of this wave's sub-block
@@ -211,7 +237,8 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
           x[r] = p.cap_out_log2 * tanh_exp2(s[r] * p.cap_in);
         else
           x[r] = s[r] * p.scale_log2;
-        if (key0 + 4 * g16 + r >= nk) x[r] = kNegInf;
+        const int key = key0 + 4 * g16 + r;
+        if (key >= nk || key < kb_w) x[r] = kNegInf;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = fmaxf(mx, xor16(mx));
@@ -248,6 +275,17 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     const int n = nh_valid * CPR;
     uint16_t* kw = const_cast<uint16_t*>(kg);
     uint16_t* vw = const_cast<uint16_t*>(vg);
+    // K / V row `pos` of this work group's first head
+    auto row_k = [&](int pos) {
+      if (!paged) return kw + (int64_t)pos * p.k_ss;
+      return const_cast<uint16_t*>(p.k) + (int64_t)page_of(pos) * p.k_sp +
+             (int64_t)(pos % p.page_size) * p.k_ss + (int64_t)hk0 * p.k_sh;
+    };
+    auto row_v = [&](int pos) {
+      if (!paged) return vw + (int64_t)pos * p.v_ss;
+      return const_cast<uint16_t*>(p.v) + (int64_t)page_of(pos) * p.v_sp +
+             (int64_t)(pos % p.page_size) * p.v_ss + (int64_t)hk0 * p.v_sh;
+    };
     for (int idx = tid; idx < p.seq_add * 2 * n; idx += NW * 64) {
       const int t = idx / (2 * n);
       const int c = idx - t * 2 * n;
@@ -262,15 +300,17 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
       const uint16_t* src =
           is_v ? p.v_new + (int64_t)b * p.vn_sb + (int64_t)t * p.vn_ss + hd * p.vn_sh
                : p.k_new + (int64_t)b * p.kn_sb + (int64_t)t * p.kn_ss + hd * p.kn_sh;
-      uint16_t* dst = is_v ? vw + (int64_t)pos * p.v_ss + (int64_t)hh * p.v_sh
-                           : kw + (int64_t)pos * p.k_ss + (int64_t)hh * p.k_sh;
+      uint16_t* dst = is_v ? row_v(pos) + (int64_t)hh * p.v_sh : row_k(pos) + (int64_t)hh * p.k_sh;
       *(u32x4_t*)(dst + 8 * j) = *(const u32x4_t*)(src + 8 * j);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  if (s_lo < s_hi) issue(s_lo, smem);
+  if (s_lo < s_hi) {
+    issue(s_lo, smem, paged ? page_of(kb + s_lo * KSTEP) : 0);
+    if (paged && s_lo + 1 < s_hi) pg_next = page_of(kb + (s_lo + 1) * KSTEP);
+  }
   for (int st = s_lo; st < s_hi; ++st) {
     // this work group's loads of step st have landed, and every wave is done
     // with step st - 1, whose stage the next loads refill
@@ -408,10 +448,15 @@ template <bool BF16, int D, int HPWV>
 hipError_t launch_h(const DecParams& p, bool softcap, hipStream_t stream) {
   const dim3 grid(p.n_split, ((p.h_kv + p.hpw - 1) / p.hpw) * p.n_hg, p.batch);
   const dim3 block(DecCfg<D>::NW * 64);
-  if (softcap)
-    hipLaunchKernelGGL((decode_kernel<BF16, D, true, HPWV>), grid, block, 0, stream, p);
+  const bool paged = p.block_table != nullptr;
+  if (softcap && paged)
+    hipLaunchKernelGGL((decode_kernel<BF16, D, true, HPWV, true>), grid, block, 0, stream, p);
+  else if (softcap)
+    hipLaunchKernelGGL((decode_kernel<BF16, D, true, HPWV, false>), grid, block, 0, stream, p);
+  else if (paged)
+    hipLaunchKernelGGL((decode_kernel<BF16, D, false, HPWV, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<BF16, D, false, HPWV>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<BF16, D, false, HPWV, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -58,6 +58,14 @@ struct DecParams {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;
+  // Paged cache (block_table != nullptr): k and v point to pools of num_pages
+  // pages of page_size tokens (page strides k_sp / v_sp elements; k_ss, k_sh
+  // within a page); token j of batch entry b lives in page
+  // block_table[b * bt_stride + j / page_size], row j % page_size.
+  // page_size is a multiple of the kernel's keys per step.
+  const int32_t* block_table;
+  int32_t bt_stride, page_size, num_pages;
+  int64_t k_sp, v_sp;
 };
 
 int prefill_rows_per_tile();

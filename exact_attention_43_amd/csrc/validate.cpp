@@ -225,4 +225,28 @@ exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n) 
   return EXATTN_OK;
 }
 
+int decode_keys_per_step(int head_dim, int hpw) {
+  const int nw = head_dim == 256 ? 4 : 8;                 // waves per work group
+  const int hpwv = head_dim == 64 && hpw == 16 ? 2 : 1;    // heads per wave
+  return 16 * (nw * hpwv / hpw);
+}
+
+exattn_status check_paged(const exattn_decode_args* a, const DecodePlan& pl, const exattn_paged_kv* pg) {
+  if (pg == nullptr) return fail(EXATTN_E_INVALID, "paged is NULL");
+  if (pg->page_size <= 0) return fail(EXATTN_E_INVALID, "page_size must be positive");
+  const int kstep = decode_keys_per_step(a->head_dim, pl.hpw);
+  if (pg->page_size % kstep != 0)
+    return fail(EXATTN_E_UNSUPPORTED, "page_size must be a multiple of " + std::to_string(kstep) +
+                                          " for this head_dim and heads_kv");
+  if (a->batch == 0 || a->seqlen_cache == 0) return EXATTN_OK;
+  if (pg->block_table == nullptr) return fail(EXATTN_E_INVALID, "block_table is NULL");
+  if (pg->num_pages <= 0) return fail(EXATTN_E_INVALID, "num_pages must be positive");
+  const int64_t need = ((int64_t)a->seqlen_cache + pg->page_size - 1) / pg->page_size;
+  if (pg->block_table_stride < need)
+    return fail(EXATTN_E_INVALID, "block_table_stride is smaller than ceil(seqlen_cache / page_size)");
+  if (!stride_ok(pg->k_page_stride) || !stride_ok(pg->v_page_stride))
+    return fail(EXATTN_E_INVALID, "page strides must be non-negative multiples of 8 elements");
+  return EXATTN_OK;
+}
+
 }  // namespace exattn

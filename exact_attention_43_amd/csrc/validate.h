@@ -61,6 +61,14 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
 // (which plan_decode has accepted).
 exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n);
 
+// Keys per step of the decode kernel for this head_dim and heads per work
+// group: 16 times the waves that share one head slot (the kernel derives the
+// same from its wave count and head slots).
+int decode_keys_per_step(int head_dim, int hpw);
+
+// Checks a paged-cache description against accepted decode arguments.
+exattn_status check_paged(const exattn_decode_args* a, const DecodePlan& pl, const exattn_paged_kv* pg);
+
 
 // Adjacent KV heads one decode work group covers: enough for a 2 KiB piece of
 // every key row (16 at d = 64, 8 at d = 128, 4 at d = 256), rounded down to a

@@ -186,6 +186,34 @@ typedef struct {
 exattn_status exattn_decode_append(const exattn_decode_args *args, const exattn_kv_new *kv_new,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Paged KV cache (FAQ Q18): k_cache and v_cache of exattn_decode_args point to
+ * pools of num_pages pages, each page_size tokens of (heads_kv, head_dim);
+ * k_page_stride / v_page_stride are the page strides and k_stride[1..2] /
+ * v_stride[1..2] the token and head strides inside a page (k_stride[0] and
+ * v_stride[0] are ignored).  Token j of batch entry b lives in page
+ * block_table[b * block_table_stride + j / page_size], row j % page_size.
+ * block_table: device int32, at least ceil(seqlen_cache / page_size) entries
+ * per batch entry; seqlen_cache is the capacity of one sequence.
+ * page_size must be a multiple of the decode kernel's keys per step (16 for
+ * head_dim 128 with 8 or more KV heads; always satisfied by multiples of 128);
+ * other sizes are rejected with EXATTN_E_UNSUPPORTED.  Page indices outside
+ * [0, num_pages) are clamped (a precondition violation, memory-safe).
+ */
+typedef struct {
+  const int32_t *block_table;
+  int32_t block_table_stride; /* entries per batch entry */
+  int32_t page_size, num_pages;
+  int64_t k_page_stride, v_page_stride; /* elements */
+} exattn_paged_kv;
+
+/* exattn_decode (kv_new NULL) or exattn_decode_append over a paged cache: the
+ * same computation, the new rows written into their pages.  The plan and the
+ * workspace are those of exattn_decode_plan on args. */
+exattn_status exattn_decode_paged(const exattn_decode_args *args, const exattn_paged_kv *paged,
+                                  const exattn_kv_new *kv_new, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* The automatic split count, as a pure function (no device query).  One work
  * group covers up to 1024/head_dim adjacent KV heads (16 at d = 64, 8 at
  * d = 128, 4 at d = 256; a power of two no larger than heads_kv) and 16 of
@@ -196,8 +224,8 @@ int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_
                                   int32_t seqlen_k, int32_t head_dim, int32_t num_cus);
 
 /* sizeof(exattn_fwd_args) for which = 0, sizeof(exattn_decode_args) for which = 1,
- * sizeof(exattn_kv_new) for which = 2, 0 otherwise: lets a binding check its
- * mirror of the structs. */
+ * sizeof(exattn_kv_new) for which = 2, sizeof(exattn_paged_kv) for which = 3, 0
+ * otherwise: lets a binding check its mirror of the structs. */
 size_t exattn_args_size(int32_t which);
 
 const char *exattn_status_string(int32_t status);

@@ -256,6 +256,24 @@ def attention_kvcache_append(q, k_cache, v_cache, k_new, v_new, cache_seqlens, *
     return o, lse, kc, vc
 
 
+def paged_to_contiguous(pool, block_table, seqlen_cache):
+    """A paged KV cache (FAQ Q18) as a contiguous one: pool (num_pages,
+    page_size, h_kv, d); token j of batch entry b is row j % page_size of page
+    block_table[b, j // page_size].  Returns (b, seqlen_cache, h_kv, d) in the
+    pool's storage type (a gather of rows, no arithmetic)."""
+    bt = np.asarray(block_table)
+    page_size = pool.shape[1]
+    rows = []
+    for bi in range(bt.shape[0]):
+        idx = [int(bt[bi, j // page_size]) for j in range(seqlen_cache)]
+        off = [j % page_size for j in range(seqlen_cache)]
+        rows.append(pool[idx, off])
+    if hasattr(pool, "clone"):
+        import torch  # the pool's own type; the gather above is torch/numpy agnostic
+        return torch.stack(rows, 0)
+    return np.stack(rows, 0)
+
+
 def merge_partials(o_parts, lse_parts):
     """Combine attention results over disjoint key sets by their log-sum-exp.
 

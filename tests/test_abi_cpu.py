@@ -40,6 +40,7 @@ def test_struct_layout_and_version(L):
     assert L.exattn_args_size(0) == C.sizeof(ex.FwdArgs)
     assert L.exattn_args_size(1) == C.sizeof(ex.DecodeArgs)
     assert L.exattn_args_size(2) == C.sizeof(ex.KvNew)
+    assert L.exattn_args_size(3) == C.sizeof(ex.PagedKv)
     assert L.exattn_args_size(7) == 0
     assert L.exattn_abi_version() == 1
     assert L.exattn_status_string(0) == b"EXATTN_OK"
@@ -177,6 +178,39 @@ def test_decode_append_null_and_empty(L):
     # nothing to attend: batch 0 launches nothing, whatever kv_new holds
     assert L.exattn_decode_append(C.byref(_dec(batch=0)), C.byref(_kvn(seqlen_new=3)), None, 0,
                                   None) == ex.EXATTN_OK
+
+
+def _pg(**kw):
+    g = ex.PagedKv()
+    g.block_table = FAKE
+    g.block_table_stride = 64
+    g.page_size, g.num_pages = 256, 1000
+    g.k_page_stride = g.v_page_stride = 256 * 8 * 128
+    for key, val in kw.items():
+        setattr(g, key, val)
+    return g
+
+
+BAD_PAGED = [
+    ("zero page size", dict(page_size=0), ex.EXATTN_E_INVALID),
+    ("page size not a step multiple", dict(page_size=24), ex.EXATTN_E_UNSUPPORTED),
+    ("null block table", dict(block_table=None), ex.EXATTN_E_INVALID),
+    ("short block table rows", dict(block_table_stride=63), ex.EXATTN_E_INVALID),
+    ("no pages", dict(num_pages=0), ex.EXATTN_E_INVALID),
+    ("odd page stride", dict(k_page_stride=256 * 8 * 128 + 4), ex.EXATTN_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_PAGED, ids=[c[0] for c in BAD_PAGED])
+def test_decode_paged_rejects(L, name, kw, status):
+    a = _dec(cache_seqlens=FAKE)  # 16384 tokens per sequence: 64 pages of 256
+    assert L.exattn_decode_paged(C.byref(a), C.byref(_pg(**kw)), None, C.c_void_p(FAKE), 1 << 30,
+                                 None) == status, L.exattn_last_error()
+
+
+def test_decode_paged_null(L):
+    a = _dec(cache_seqlens=FAKE)
+    assert L.exattn_decode_paged(C.byref(a), None, None, None, 0, None) == ex.EXATTN_E_INVALID
 
 
 def test_decode_workspace_checks(L):

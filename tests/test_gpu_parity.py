@@ -267,6 +267,88 @@ def test_decode_append_steps():
     assert torch.equal(dkc.cpu(), kc_ref) and torch.equal(dvc.cpu(), vc_ref)
 
 
+def _to_pages(cache, page, spare, gen):
+    """Scatter a contiguous cache (b, s, h, d) into a pool of pages at a random
+    permutation of page slots; returns (pool, block_table)."""
+    b, s_cache = cache.shape[:2]
+    per_seq = -(-s_cache // page)
+    n_pages = b * per_seq + spare
+    perm = torch.randperm(n_pages, generator=gen)
+    pool = torch.zeros((n_pages, page) + tuple(cache.shape[2:]), dtype=cache.dtype)
+    bt = torch.zeros((b, per_seq), dtype=torch.int32)
+    for bi in range(b):
+        for i in range(per_seq):
+            slot = int(perm[bi * per_seq + i])
+            bt[bi, i] = slot
+            rows = cache[bi, i * page:(i + 1) * page]
+            pool[slot, :rows.shape[0]] = rows
+    return pool, bt
+
+
+PAGED_CASES = [
+    # b, pages per seq, page, h_q, h_kv, d, dtype, lens, window, softcap, splits, s_new, seed
+    (3, 8, 256, 32, 8, 128, torch.bfloat16, [2048, 1, 1000], (-1, -1), 0.0, 0, 0, 190),
+    (2, 64, 16, 16, 8, 128, torch.float16, [1024, 77], (-1, -1), 0.0, 6, 0, 191),
+    (2, 8, 64, 16, 16, 64, torch.bfloat16, [500, 13], (40, -1), 20.0, 0, 0, 192),
+    (2, 4, 128, 8, 4, 256, torch.float16, [512, 300], (-1, -1), 0.0, 3, 0, 193),
+    (3, 16, 16, 16, 8, 128, torch.bfloat16, [0, 100, 250], (-1, -1), 0.0, 0, 5, 194),  # append
+    (2, 8, 64, 8, 8, 128, torch.bfloat16, [300, 10], (2, -1), 0.0, 2, 7, 195),         # append, window
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[f"p{c[-1]}" for c in PAGED_CASES])
+def test_decode_paged(case):
+    """Paged KV cache (FAQ Q18): O and LSE against the oracle on the same cache
+    laid out contiguously; without a window and append, bitwise equal to the
+    contiguous decode with the same split count; appended rows land in their
+    pages and nothing else in the pool changes."""
+    b, per_seq, page, hq, hkv, d, dt, lens, window, cap, splits, s_new, seed = case
+    s_cache = per_seq * page
+    q, kc, vc = W.kvcache(b, s_cache, hq, hkv, d, seed=seed, dtype=dt)
+    gen = torch.Generator().manual_seed(seed)
+    kpool, bt = _to_pages(kc, page, 3, gen)
+    vpool, _ = _to_pages(vc, page, 3, torch.Generator().manual_seed(seed))  # same permutation
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    dq, dkp, dvp, dbt, dl = _dev(q, kpool, vpool, bt, lens_t)
+    kw = {}
+    if s_new:
+        kn, vn = W.kv_new(b, s_new, hkv, d, seed=seed + 1000, dtype=dt)
+        kw = dict(k=kn.to(DEV), v=vn.to(DEV))
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((b, hq, 1))
+    ex.attn_with_kvcache(dq, dkp, dvp, cache_seqlens=dl, causal=True, window_size=window, softcap=cap,
+                         num_splits=splits, out=out, lse=lse, block_table=dbt, **kw)
+    torch.cuda.synchronize()
+    if s_new:
+        o_ref, l_ref, kc_ref, vc_ref = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens_t, causal=True,
+                                                                       window_size=window, softcap=cap)
+        assert torch.equal(oracle.paged_to_contiguous(dkp.cpu(), bt, s_cache), kc_ref)
+        assert torch.equal(oracle.paged_to_contiguous(dvp.cpu(), bt, s_cache), vc_ref)
+        used = set(bt.flatten().tolist())
+        spare = [i for i in range(kpool.shape[0]) if i not in used]
+        assert torch.equal(dkp.cpu()[spare], kpool[spare]) and torch.equal(dvp.cpu()[spare], vpool[spare])
+    else:
+        o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens_t, causal=True, window_size=window, softcap=cap)
+    assert_o_close(out, o_ref, dt, "paged")
+    assert_lse_close(lse, l_ref, "paged")
+    if not s_new and window == (-1, -1):
+        dkc, dvc = _dev(kc, vc)
+        o2, l2 = ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, causal=True, softcap=cap,
+                                      num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+def test_decode_paged_rejects_small_pages():
+    """With two KV heads a step covers 64 keys at d = 128: 16-token pages are refused."""
+    q, kc, vc = W.kvcache(1, 256, 4, 2, 128, seed=196)
+    kpool, bt = _to_pages(kc, 16, 0, torch.Generator().manual_seed(1))
+    dq, dkp, dbt = _dev(q, kpool, bt)
+    with pytest.raises(NotImplementedError, match="multiple of 64"):
+        ex.attn_with_kvcache(dq, dkp, dkp, cache_seqlens=torch.tensor([256], dtype=torch.int32, device=DEV),
+                             block_table=dbt)
+
+
 # --------------------------------------------------------------------------
 # masks, tails and degenerate cases
 # --------------------------------------------------------------------------

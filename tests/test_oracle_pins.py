@@ -383,6 +383,29 @@ def pin_decode_append():
                                                                                 kc[0, :s_cache - 2])
 
 
+def pin_paged():
+    """A paged cache (FAQ Q18) read back as contiguous: the pool is built here by
+    scattering the pages of a contiguous cache to a random permutation of page
+    slots; the gather must return the cache exactly, for any page size."""
+    r = _rng(23)
+    b, s_cache, h, d = 3, 48, 2, 4
+    cache = r.standard_normal((b, s_cache, h, d))
+    for page in (16, 12, 48):
+        per_seq = -(-s_cache // page)
+        n_pages = b * per_seq + 2
+        perm = r.permutation(n_pages)
+        pool = np.full((n_pages, page, h, d), np.nan)
+        bt = np.zeros((b, per_seq), dtype=np.int32)
+        for bi in range(b):
+            for i in range(per_seq):
+                slot = perm[bi * per_seq + i]
+                bt[bi, i] = slot
+                rows = cache[bi, i * page:(i + 1) * page]
+                pool[slot, :rows.shape[0]] = rows
+        got = OA.paged_to_contiguous(pool, bt, s_cache)
+        assert np.array_equal(got, cache), page
+
+
 def pin_softcap():
     r = _rng(19)
     q = r.standard_normal((1, 6, 2, 16)) * 4
@@ -424,7 +447,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_softcap,
         pin_default_scale]
 
 
@@ -483,6 +506,14 @@ def _bad_append_offset(k_cache, v_cache, cache_seqlens, k_new, v_new):
                      v_new)
 
 
+def _bad_paged_row(pool, block_table, seqlen_cache):
+    bt = np.asarray(block_table)
+    page = pool.shape[1]
+    rows = [pool[[int(bt[bi, j // page]) for j in range(seqlen_cache)], [j // page for j in range(seqlen_cache)]]
+            for bi in range(bt.shape[0])]
+    return np.stack(rows, 0)
+
+
 OA_visible = OA.visible
 OA_softmax = OA.softmax_rows
 OA_append = OA.kvcache_append
@@ -499,6 +530,7 @@ MUTATIONS = [
     ("softmax_rows", _bad_softmax_sign),
     ("_kv_head", _bad_kv_head_modulo),
     ("kvcache_append", _bad_append_offset),
+    ("paged_to_contiguous", _bad_paged_row),
 ]
 
 
