@@ -221,6 +221,47 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens=None, *, softmax_scale=
     return np.concatenate(os_, axis=0), np.concatenate(ls_, axis=0)
 
 
+def attention_backward(q, k, v, do, *, softmax_scale=None, causal=False, window_size=(-1, -1),
+                       softcap=0.0):
+    """Gradients of the dense forward (same arguments as ``attention``) for the
+    upstream gradient dO (b, s_q, h_q, d): returns dQ, dK, dV (float64, shaped
+    like q, k, v).
+
+    The backward of "FlashAttention完整说明" section 二.2 recomputes S and P from
+    Q, K and the kept statistics; what it computes is the chain rule through
+    the definition, written out here per head with P materialised:
+    dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(P * dP)); through the
+    softcap dS_raw = dS * (1 - tanh^2(s_raw / c)); dQ = scale dS_raw K and
+    dK = scale dS_raw^T Q.  Masked entries have P = 0 and contribute nothing.
+    A KV head's dK and dV sum over the query heads that read it (FAQ Q15).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    b, s_q, h_q, d = q.shape
+    s_k, h_kv = k.shape[1], k.shape[2]
+    scale = default_scale(d) if softmax_scale is None else float(softmax_scale)
+    wl, wr = window_size
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for bi in range(b):
+        for h in range(h_q):
+            hk = _kv_head(h, h_q, h_kv)
+            q2, k2, v2, do2 = q[bi, :, h], k[bi, :, hk], v[bi, :, hk], do[bi, :, h]
+            if s_k == 0 or s_q == 0:
+                continue
+            _, _, p = attend_head(q2, k2, v2, scale=scale, causal=causal, window_left=wl,
+                                  window_right=wr, softcap=softcap, return_probs=True)
+            dv[bi, :, hk] += p.T @ do2
+            dp = do2 @ v2.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            if softcap is not None and softcap > 0.0:
+                t = np.tanh(scores(q2, k2, scale) / softcap)
+                ds = ds * (1.0 - t * t)
+            dq[bi, :, h] = scale * (ds @ k2)
+            dk[bi, :, hk] += scale * (ds.T @ q2)
+    return dq, dk, dv
+
+
 def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new):
     """The cache update of flash_attn_with_kvcache(q, k_cache, v_cache, k=k_new,
     v=v_new, cache_seqlens=...) (FAQ Q17): token t of k_new / v_new

@@ -406,6 +406,80 @@ def pin_paged():
         assert np.array_equal(got, cache), page
 
 
+def _sdpa_autograd(q, k, v, do, scale, causal, wl, wr, softcap):
+    """dQ, dK, dV by torch autograd (float64, CPU) of a plain masked attention with
+    its own bottom-right mask; empty rows are multiplied out instead of NaN."""
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    b, s_q, h_q, d = q.shape
+    s_k, h_kv = k.shape[1], k.shape[2]
+    g = h_q // h_kv
+    ke = kt.repeat_interleave(g, dim=2)
+    ve = vt.repeat_interleave(g, dim=2)
+    s = torch.einsum("bqhd,bkhd->bhqk", qt, ke) * scale
+    if softcap > 0:
+        s = softcap * torch.tanh(s / softcap)
+    i = torch.arange(s_q)[:, None]
+    j = torch.arange(s_k)[None, :]
+    off = s_k - s_q
+    vis = torch.ones(s_q, s_k, dtype=torch.bool)
+    right = 0 if causal else wr
+    if right >= 0:
+        vis &= j <= i + off + right
+    if wl >= 0:
+        vis &= j >= i + off - wl
+    s = s.masked_fill(~vis, -1e30)
+    p = torch.softmax(s, dim=-1) * vis.any(dim=1)[:, None].to(torch.float64)
+    o = torch.einsum("bhqk,bkhd->bqhd", p, ve)
+    (o * torch.tensor(do)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_backward():
+    """The oracle's gradients against autograd of a plain masked attention, against
+    central differences, and two closed forms: without softcap each head's dK
+    sums to 0 over the keys (every row of dS sums to 0), and dV summed over the
+    keys is the sum of dO over the rows that see any key."""
+    r = _rng(24)
+    cases = [  # s_q, s_k, h_q, h_kv, causal, window, softcap
+        (5, 7, 2, 1, True, (-1, -1), 0.0),
+        (6, 6, 4, 2, False, (2, 1), 0.0),
+        (8, 4, 2, 2, True, (-1, -1), 0.0),   # rows 0-3 see nothing
+        (4, 9, 2, 1, False, (-1, -1), 1.5),  # saturating softcap
+    ]
+    for s_q, s_k, h_q, h_kv, causal, (wl, wr), cap in cases:
+        d = 4
+        q = r.standard_normal((2, s_q, h_q, d)) * 2
+        k = r.standard_normal((2, s_k, h_kv, d)) * 2
+        v = r.standard_normal((2, s_k, h_kv, d))
+        do = r.standard_normal((2, s_q, h_q, d))
+        scale = 0.7
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, softmax_scale=scale, causal=causal,
+                                               window_size=(wl, wr), softcap=cap)
+        gq, gk, gv = _sdpa_autograd(q, k, v, do, scale, causal, wl, wr, cap)
+        assert np.allclose(dq, gq, atol=1e-10) and np.allclose(dk, gk, atol=1e-10)
+        assert np.allclose(dv, gv, atol=1e-10)
+        if cap == 0:  # with a softcap dS is reweighted by 1 - tanh^2 and its rows no longer sum to 0
+            assert np.abs(dk.sum(axis=1)).max() < 1e-10
+        vis_rows = [i for i in range(s_q) if _visible_count(i, s_q, s_k, causal, wl, wr)[0] > 0]
+        want = do[:, vis_rows].reshape(2, len(vis_rows), h_kv, h_q // h_kv, d).sum(axis=(1, 3))
+        assert np.allclose(dv.sum(axis=1), want, atol=1e-10)
+        # central differences of L = sum(dO * O) for a few entries
+        def loss(qq, kk, vv):
+            o, _ = oracle.attention(qq, kk, vv, softmax_scale=scale, causal=causal,
+                                    window_size=(wl, wr), softcap=cap)
+            return float((np.nan_to_num(o) * do).sum())
+        eps = 1e-6
+        for arr, grad in ((q, dq), (k, dk), (v, dv)):
+            idx = tuple(int(x) for x in r.integers(0, arr.shape))
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args_p = [plus if a is arr else a for a in (q, k, v)]
+            args_m = [minus if a is arr else a for a in (q, k, v)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6, (idx, fd, grad[idx])
+
+
 def pin_softcap():
     r = _rng(19)
     q = r.standard_normal((1, 6, 2, 16)) * 4
@@ -447,7 +521,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_backward, pin_softcap,
         pin_default_scale]
 
 
