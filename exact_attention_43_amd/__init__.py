@@ -83,6 +83,21 @@ class PagedKv(C.Structure):
     ]
 
 
+class BwdArgs(C.Structure):
+    """Mirror of exattn_bwd_args."""
+    _fields_ = [
+        ("dtype", C.c_int32), ("batch", C.c_int32), ("seqlen_q", C.c_int32), ("seqlen_k", C.c_int32),
+        ("heads_q", C.c_int32), ("heads_kv", C.c_int32), ("head_dim", C.c_int32),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p), ("o", C.c_void_p), ("dout", C.c_void_p),
+        ("lse", C.c_void_p), ("dq", C.c_void_p), ("dk", C.c_void_p), ("dv", C.c_void_p),
+        ("q_stride", C.c_int64 * 3), ("k_stride", C.c_int64 * 3), ("v_stride", C.c_int64 * 3),
+        ("o_stride", C.c_int64 * 3), ("dout_stride", C.c_int64 * 3), ("dq_stride", C.c_int64 * 3),
+        ("dk_stride", C.c_int64 * 3), ("dv_stride", C.c_int64 * 3), ("lse_stride", C.c_int64 * 2),
+        ("softmax_scale", C.c_float), ("softcap", C.c_float), ("causal", C.c_int32),
+        ("window_left", C.c_int32), ("window_right", C.c_int32),
+    ]
+
+
 _lib_handle = None
 _lib_lock = threading.Lock()
 
@@ -115,6 +130,10 @@ def lib():
             L.exattn_decode_paged.argtypes = [C.POINTER(DecodeArgs), C.POINTER(PagedKv), C.POINTER(KvNew),
                                               C.c_void_p, C.c_size_t, C.c_void_p]
             L.exattn_decode_paged.restype = C.c_int
+            L.exattn_bwd_plan.argtypes = [C.POINTER(BwdArgs), C.POINTER(C.c_size_t)]
+            L.exattn_bwd_plan.restype = C.c_int
+            L.exattn_bwd.argtypes = [C.POINTER(BwdArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+            L.exattn_bwd.restype = C.c_int
             L.exattn_decode_auto_splits.argtypes = [C.c_int32] * 6
             L.exattn_decode_auto_splits.restype = C.c_int32
             L.exattn_args_size.argtypes = [C.c_int32]
@@ -126,7 +145,8 @@ def lib():
             L.exattn_abi_version.argtypes = []
             L.exattn_abi_version.restype = C.c_int32
             if (L.exattn_args_size(0) != C.sizeof(FwdArgs) or L.exattn_args_size(1) != C.sizeof(DecodeArgs)
-                    or L.exattn_args_size(2) != C.sizeof(KvNew) or L.exattn_args_size(3) != C.sizeof(PagedKv)):
+                    or L.exattn_args_size(2) != C.sizeof(KvNew) or L.exattn_args_size(3) != C.sizeof(PagedKv)
+                    or L.exattn_args_size(4) != C.sizeof(BwdArgs)):
                 raise RuntimeError("libexattn.so struct layout does not match this binding; rebuild it")
             _lib_handle = L
     return _lib_handle
@@ -434,10 +454,72 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     return out, lse
 
 
+def attn_backward(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
+                  softcap=0.0, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of attn_func: (dq, dk, dv) for the upstream gradient dout.
+
+    q, out, dout (b, s_q, h_q, d); k, v (b, s_k, h_kv, d); lse (b, h_q, s_q) fp32
+    as attn_func returns it; the same scale, causal and window as the forward
+    call.  A KV head's dk and dv sum over the query heads that read it.
+    head_dim 64 or 128, no softcap, fixed lengths.  Deterministic.
+    """
+    if softcap not in (0, 0.0, None):
+        raise NotImplementedError("the backward does not provide softcap")
+    for name, t in (("q", q), ("out", out), ("dout", dout)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be (batch, seqlen, heads, head_dim)")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have the shape of q")
+    if k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be (batch, seqlen_k, heads_kv, head_dim)")
+    if len({q.dtype, k.dtype, v.dtype, out.dtype, dout.dtype}) != 1:
+        raise ValueError("q, k, v, out and dout must share one dtype")
+    b, s_q, h_q, d = q.shape
+    s_k, h_kv = k.shape[1], k.shape[2]
+    if lse.dtype != torch.float32 or lse.shape != (b, h_q, s_q):
+        raise ValueError("lse must be fp32 (batch, heads_q, seqlen_q)")
+    _on_gpu(dout, q, k, v, out, lse, dq, dk, dv, workspace)
+    _check_last_dim(dout, q, k, v, out, dq, dk, dv)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk and dv must have the shapes of q, k and v")
+    if len({q.dtype, dq.dtype, dk.dtype, dv.dtype}) != 1:
+        raise ValueError("dq, dk and dv must have the dtype of q")
+    a = BwdArgs()
+    a.dtype = _dtype_code(q)
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = b, s_q, s_k, h_q, h_kv, d
+    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr()
+    a.lse = lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        getattr(a, f"{name}_stride")[:] = list(t.stride()[:3])
+    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    a.softmax_scale = _scale(softmax_scale)
+    a.softcap = 0.0
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = _window(window_size)
+    L = lib()
+    with torch.cuda.device(q.device):
+        wb = C.c_size_t(0)
+        _raise_for(L.exattn_bwd_plan(C.byref(a), C.byref(wb)), "exattn_bwd_plan")
+        ws_ptr, ws_bytes = None, 0
+        if wb.value > 0:
+            if workspace is None:
+                workspace = _workspace(q.device, wb.value)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = L.exattn_bwd(C.byref(a), C.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes,
+                          C.c_void_p(_stream(q.device)))
+    _raise_for(st, "exattn_bwd")
+    return dq, dk, dv
+
+
 def auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus):
     """The library's automatic split count for a device with num_cus compute units."""
     return int(lib().exattn_decode_auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus))
 
 
 __all__ = ["attn_func", "attn_qkvpacked_func", "attn_kvpacked_func", "attn_varlen_func",
-           "attn_with_kvcache", "decode_plan", "auto_splits", "lib", "library_path"]
+           "attn_with_kvcache", "attn_backward", "decode_plan", "auto_splits", "lib", "library_path"]

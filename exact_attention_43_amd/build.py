@@ -3,8 +3,10 @@
 Every HIP source is compiled with packed-fp32 instruction selection switched
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass of
 hipcc warns that it does not know that feature, which is harmless.  MFMA
-accumulators are kept in architectural VGPRs (``-amdgpu-mfma-vgpr-form``), so
-the softmax and the rare O rescale touch them without AGPR copies.
+accumulators of the forward kernels are kept in architectural VGPRs
+(``-amdgpu-mfma-vgpr-form``), so the softmax and the rare O rescale touch them
+without AGPR copies; the backward (``bwd.hip``) holds dK and dV accumulators
+beside K and V and lets the compiler place accumulators in AGPRs.
 
     python -m exact_attention_43_amd.build          # build
     python -m exact_attention_43_amd.build --check  # also build the host-only checker
@@ -25,7 +27,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libexattn.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "exattn_api.cpp"]
+HIP_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "exattn_api.cpp"]
+AGPR_SOURCES = {"bwd.hip"}  # compiled without -amdgpu-mfma-vgpr-form
 HOST_SOURCES = ["validate.cpp"]
 
 
@@ -55,7 +58,8 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         jobs.append([hipcc, f"--offload-arch={ARCH}", *common, "-Xclang", "-target-feature",
-                     "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", *lang, "-c",
+                     "-Xclang", "-packed-fp32-ops",
+                     *([] if src in AGPR_SOURCES else ["-mllvm", "-amdgpu-mfma-vgpr-form"]), *lang, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")

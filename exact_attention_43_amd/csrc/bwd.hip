@@ -1,0 +1,490 @@
+// Backward of exact attention: dQ, dK, dV from Q, K, V, O, dO and the forward's
+// LSE, by recomputing S and P tile by tile ("FlashAttention完整说明", section
+// 二.2: the forward keeps only O and the softmax statistics, the backward
+// recomputes the rest).  With P = exp(S - LSE) and D_i = dO_i . O_i:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
+//   dK = scale dS^T Q;
+// a KV head's dK and dV sum over the query heads that read it.
+//
+// gfx950 design, deterministic (no atomics):
+// - bwd_prep_kernel: D_i = dO_i . O_i and LSE in the log2 domain per row;
+// - bwd_dkdv_kernel: a work group owns 128 keys (32 per wave) of one KV head and
+//   walks the query blocks (32 rows) of every query head in its group.  K and V
+//   of its keys stay in registers; Q, dO and the rows' statistics stream
+//   through double-buffered LDS by DMA.  Per block a wave computes S = Q K^T and
+//   dP = dO V^T (queries x keys, Q and dO the A operands with the row
+//   permutation that makes 8 consecutive accumulator registers 8 consecutive
+//   queries), then dV^T += dO^T P and dK^T += Q^T dS with P and dS rounded in
+//   place as the B operand and dO^T / Q^T read transposed from LDS;
+// - bwd_dq_kernel: a work group owns 128 query rows (32 per wave) of one query
+//   head and walks its KV blocks (64 keys) like the forward: S^T = K Q^T and
+//   dP^T = V dO^T with Q^T and dO^T in registers, dS^T rounded in place as the
+//   B operand of dQ^T += K^T dS^T, K^T read transposed from LDS.
+// The row statistics make P exact without a running max: LSE is final.
+#include "device_common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+namespace exattn {
+namespace {
+
+constexpr int kBwdRows = 32;   // query rows per block of the dK/dV kernel
+constexpr int kBwdKeys = 128;  // keys per work group of the dK/dV kernel
+constexpr int kDqRows = 128;   // query rows per work group of the dQ kernel
+constexpr int kDqKeys = 64;    // keys per block of the dQ kernel
+
+// Is key j visible from query row i (bottom-right offset off = s_k - s_q)?
+__device__ __forceinline__ bool visible_key(int i, int j, int sq, int sk, int off, int wl, int wr) {
+  return i < sq && j < sk && (wr < 0 || j <= i + off + wr) && (wl < 0 || j >= i + off - wl);
+}
+
+// The two 16-bit values of a 32-bit word as floats.
+template <bool BF16>
+__device__ __forceinline__ float lo_f32(uint32_t w) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(float, w << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <bool BF16>
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+  else
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// D_i = dO_i . O_i (fp32) and LSE_i log2 e, or +inf for a row without keys
+// (then exp2(s - lse2) = 0 everywhere).  One thread per (batch, row, head).
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
+  const int64_t rows = (int64_t)p.batch * p.s_q * p.h_q;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows) return;
+  const int h = (int)(t % p.h_q);
+  const int i = (int)((t / p.h_q) % p.s_q);
+  const int b = (int)(t / ((int64_t)p.h_q * p.s_q));
+  const uint16_t* o = p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
+  const uint16_t* d = p.dout + (int64_t)b * p.do_sb + (int64_t)i * p.do_ss + (int64_t)h * p.do_sh;
+  float acc = 0.f;
+#pragma unroll 2
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4_t a = *(const u32x4_t*)(o + 8 * c);
+    const u32x4_t g = *(const u32x4_t*)(d + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = __builtin_fmaf(lo_f32<BF16>(a[e]), lo_f32<BF16>(g[e]), acc);
+      acc = __builtin_fmaf(hi_f32<BF16>(a[e]), hi_f32<BF16>(g[e]), acc);
+    }
+  }
+  const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i];
+  const int64_t w = ((int64_t)b * p.h_q + h) * p.s_q + i;
+  p.ws_d[w] = acc;
+  p.ws_lse2[w] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+}
+
+// dK, dV for 128 keys of one KV head (4 waves x 32 keys).
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
+  using E = Elem<BF16>;
+  constexpr int KS = D / 16;                   // k-steps over head_dim
+  constexpr int DT = D / 32;                   // 32-wide head_dim tiles
+  constexpr int DCH = D / 8;                   // 16-byte chunks per row
+  constexpr int TILE = kBwdRows * D * 2;       // bytes of a Q (or dO) tile
+  constexpr int ROWS_PER_KB = 1024 / (D * 2);  // rows per 1 KiB DMA slice
+  constexpr int SLICES = TILE / 1024;          // DMA slices per tile
+  constexpr int STAGE = 2 * TILE + 2 * 128;    // Q, dO, lse2[32], D[32]
+  static_assert(SLICES >= 4 && SLICES % 4 == 0, "slices per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hsel = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int n_kt = (p.s_k + kBwdKeys - 1) / kBwdKeys;
+  const int kt = blockIdx.x % n_kt;
+  const int hk = (blockIdx.x / n_kt) % p.h_kv;
+  const int b = blockIdx.x / (n_kt * p.h_kv);
+  const int sq = p.s_q, sk = p.s_k, off = sk - sq;
+  const int k0 = kt * kBwdKeys;
+  const int kcol = k0 + 32 * wave + l32;  // this lane's key
+
+  // ---- K and V of this lane's key as B operands: K[kcol][16 ks + 8 hsel .. +7].
+  u32x4_t kf[KS], vf[KS];
+  {
+    const uint16_t* kp = p.k + (int64_t)b * p.k_sb + (int64_t)kcol * p.k_ss + (int64_t)hk * p.k_sh + 8 * hsel;
+    const uint16_t* vp = p.v + (int64_t)b * p.v_sb + (int64_t)kcol * p.v_ss + (int64_t)hk * p.v_sh + 8 * hsel;
+    const bool in = kcol < sk;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = in ? *(const u32x4_t*)(kp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+      vf[ks] = in ? *(const u32x4_t*)(vp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  // ---- query rows that see any of keys k0 .. k0 + 127 (per head the same).
+  const int k1 = min(k0 + kBwdKeys, sk) - 1;
+  const int wr = p.wr;
+  int i_lo = 0, i_hi = sq - 1;
+  if (wr >= 0) i_lo = max(0, k0 - off - wr);
+  if (p.wl >= 0) i_hi = min(sq - 1, k1 - off + p.wl);
+  const int qb_lo = i_lo / kBwdRows;
+  const int qb_hi = i_hi >= i_lo ? i_hi / kBwdRows + 1 : qb_lo;  // exclusive
+  const int nqb = qb_hi - qb_lo;
+  const int g = p.group;
+  const int steps = nqb * g;  // (head, query block) pairs
+
+  // ---- DMA: tile row r, stored chunk (lane % DCH) at r * D * 2 + 16 * ((lane % DCH) ^ kswz(r)).
+  uint32_t q_ofs[SLICES / 4], d_ofs[SLICES / 4];
+#pragma unroll
+  for (int i = 0; i < SLICES / 4; ++i) {
+    const int row = (4 * i + wave) * ROWS_PER_KB + lane / DCH;
+    q_ofs[i] = (uint32_t)(row * p.q_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    d_ofs[i] = (uint32_t)(row * p.do_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+  }
+  auto issue = [&](int st, uint8_t* dst) {
+    const int h = hk * g + st / nqb;
+    const int q0 = (qb_lo + st % nqb) * kBwdRows;
+    const uint16_t* qg = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    const uint16_t* dg = p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qg, p.q_ss, q0, sq, kBwdRows);
+    const __amdgpu_buffer_rsrc_t rd = block_rsrc<D>(dg, p.do_ss, q0, sq, kBwdRows);
+#pragma unroll
+    for (int i = 0; i < SLICES / 4; ++i) {
+      buffer_load_lds16(rq, dst + (4 * i + wave) * 1024, q_ofs[i]);
+      buffer_load_lds16(rd, dst + TILE + (4 * i + wave) * 1024, d_ofs[i]);
+    }
+    // the rows' statistics: 32 floats each, by lanes 0-7 of waves 0 and 1
+    if (wave < 2 && lane < 8) {
+      const float* src = (wave == 0 ? p.ws_lse2 : p.ws_d) + ((int64_t)b * p.h_q + h) * sq;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(src + q0), 0, (int)(4 * max(0, min(kBwdRows, sq - q0))), 0x00020000);
+      buffer_load_lds16(rs, dst + 2 * TILE + 128 * wave, 16u * lane);
+    }
+  };
+
+  // ---- loop-invariant LDS addresses.
+  // A operand of S = Q K^T (and dP = dO V^T): row m = l32 is query row_key(l32)
+  // of the block, chunk 2 ks + hsel.
+  const int arow = row_key(l32);
+  int aaddr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aaddr[ks] = arow * (D * 2) + 16 * ((2 * ks + hsel) ^ kswz<D>(arow));
+  // Transposed A operands (dO^T, Q^T; rows = head dims, k = 8 consecutive
+  // queries per lane half) for MFMA (c, dt): two transposing reads of 4 rows.
+  const int gi = lane >> 4, li = lane & 15;
+  int tr[2][DT];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int row = 8 * (gi >> 1) + 4 * half + (li >> 2);
+      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
+      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ kswz<D>(row)) + 2 * (dcol & 7);
+    }
+
+  f32x16_t dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16_t{};
+
+  auto block = [&](int st, const uint8_t* __restrict__ stg) {
+    const uint8_t* qt = stg;
+    const uint8_t* dt_ = stg + TILE;
+    const float* lse2 = reinterpret_cast<const float*>(stg + 2 * TILE);
+    const float* dd = lse2 + 32;
+    const int q0 = (qb_lo + st % nqb) * kBwdRows;
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = E::mfma32x32x16(*(const u32x4_t*)(qt + aaddr[ks]), kf[ks], s);
+      dp = E::mfma32x32x16(*(const u32x4_t*)(dt_ + aaddr[ks]), vf[ks], dp);
+    }
+    // register 8c + u of lane half H holds query q0 + 16 c + 8 H + u
+    u32x4_t pb[2], sb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int qi = 16 * c + 8 * hsel;
+      const u32x4_t l0 = *(const u32x4_t*)(lse2 + qi), l1 = *(const u32x4_t*)(lse2 + qi + 4);
+      const u32x4_t d0 = *(const u32x4_t*)(dd + qi), d1 = *(const u32x4_t*)(dd + qi + 4);
+      float pv[8], sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float l = __builtin_bit_cast(float, u < 4 ? l0[u] : l1[u - 4]);
+        const float di = __builtin_bit_cast(float, u < 4 ? d0[u] : d1[u - 4]);
+        const bool vis = visible_key(q0 + qi + u, kcol, sq, sk, off, p.wl, wr);
+        const float pr = vis ? fast_exp2(__builtin_fmaf(s[8 * c + u], p.scale_log2, -l)) : 0.f;
+        pv[u] = pr;
+        sv[u] = pr * (dp[8 * c + u] - di);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[c][e] = E::pack2(pv[2 * e], pv[2 * e + 1]);
+        sb[c][e] = E::pack2(sv[2 * e], sv[2 * e + 1]);
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS: k = queries 16 c + 8 H + 0..7
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int rows = 16 * c * (D * 2);
+        u32x4_t ad, aq;
+        const u32x2_t d0 = lds_read_tr16(dt_ + tr[0][dt] + rows), d1 = lds_read_tr16(dt_ + tr[1][dt] + rows);
+        const u32x2_t q0v = lds_read_tr16(qt + tr[0][dt] + rows), q1v = lds_read_tr16(qt + tr[1][dt] + rows);
+        ad[0] = d0[0], ad[1] = d0[1], ad[2] = d1[0], ad[3] = d1[1];
+        aq[0] = q0v[0], aq[1] = q0v[1], aq[2] = q1v[0], aq[3] = q1v[1];
+        dv[dt] = E::mfma32x32x16(ad, pb[c], dv[dt]);
+        dk[dt] = E::mfma32x32x16(aq, sb[c], dk[dt]);
+      }
+  };
+
+  uint8_t* const st0 = smem;
+  uint8_t* const st1 = smem + STAGE;
+  auto step = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int st) {
+    if (st + 1 < steps) issue(st + 1, nxt);
+    block(st, cur);
+  };
+  if (steps > 0) issue(0, st0);
+  for (int st = 0; st < steps; st += 2) {
+    wait_vmem_all();
+    __syncthreads();
+    step(st0, st1, st);
+    if (st + 1 < steps) {
+      wait_vmem_all();
+      __syncthreads();
+      step(st1, st0, st + 1);
+    }
+  }
+
+  // ---- dK = scale (dK^T)^T, dV = (dV^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3.
+  if (kcol < sk) {
+    uint16_t* kq = p.dk + (int64_t)b * p.dk_sb + (int64_t)kcol * p.dk_ss + (int64_t)hk * p.dk_sh;
+    uint16_t* vq = p.dv + (int64_t)b * p.dv_sb + (int64_t)kcol * p.dv_ss + (int64_t)hk * p.dv_sh;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        u32x2_t wk, wv;
+        wk[0] = E::pack2(dk[dt][4 * J] * p.scale, dk[dt][4 * J + 1] * p.scale);
+        wk[1] = E::pack2(dk[dt][4 * J + 2] * p.scale, dk[dt][4 * J + 3] * p.scale);
+        wv[0] = E::pack2(dv[dt][4 * J], dv[dt][4 * J + 1]);
+        wv[1] = E::pack2(dv[dt][4 * J + 2], dv[dt][4 * J + 3]);
+        *(u32x2_t*)(kq + 32 * dt + 8 * J + 4 * hsel) = wk;
+        *(u32x2_t*)(vq + 32 * dt + 8 * J + 4 * hsel) = wv;
+      }
+  }
+}
+
+// dQ for 128 query rows of one query head (4 waves x 32 rows).
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
+  using E = Elem<BF16>;
+  constexpr int BN = kDqKeys;
+  constexpr int NT2 = BN / 32;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int DCH = D / 8;
+  constexpr int KTILE = BN * D * 2;
+  constexpr int ROWS_PER_KB = 1024 / (D * 2);
+  constexpr int KINST = KTILE / 4096;  // DMA instructions per wave per tile
+  static_assert(KINST >= 1, "tile / wave mismatch");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * KTILE];  // K, V double-buffered
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hsel = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int n_qt = (p.s_q + kDqRows - 1) / kDqRows;
+  const int units = p.batch * p.h_q;
+  const int qt = n_qt - 1 - (int)blockIdx.x / units;  // heaviest (last) tiles first
+  const int u = blockIdx.x % units;
+  const int b = u / p.h_q, h = u % p.h_q;
+  const int hk = h / p.group;
+  const int sq = p.s_q, sk = p.s_k, off = sk - sq;
+  const int q0 = qt * kDqRows;
+  const int qrow = q0 + 32 * wave + l32;
+
+  // ---- visible key blocks of the tile.
+  const int t1 = min(q0 + kDqRows, sq) - 1;
+  int kmin = 0, kmax = sk - 1;
+  if (p.wl >= 0) kmin = max(0, q0 + off - p.wl);
+  if (p.wr >= 0) kmax = min(kmax, t1 + off + p.wr);
+  const int n_lo = kmax >= kmin ? kmin / BN : 0;
+  const int n_hi = kmax >= kmin ? kmax / BN + 1 : 0;
+
+  // ---- Q^T and dO^T as B operands: lane holds row qrow, head dims 16 ks + 8 hsel .. +7.
+  u32x4_t qf[KS], df[KS];
+  {
+    const bool in = qrow < sq;
+    const uint16_t* qp = p.q + (int64_t)b * p.q_sb + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 8 * hsel;
+    const uint16_t* dp = p.dout + (int64_t)b * p.do_sb + (int64_t)qrow * p.do_ss + (int64_t)h * p.do_sh + 8 * hsel;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = in ? *(const u32x4_t*)(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+      df[ks] = in ? *(const u32x4_t*)(dp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+  const int64_t w = ((int64_t)b * p.h_q + h) * sq + qrow;
+  const float lse2 = qrow < sq ? p.ws_lse2[w] : __builtin_inff();
+  const float drow = qrow < sq ? p.ws_d[w] : 0.f;
+
+  const uint16_t* kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
+  const uint16_t* vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+  uint32_t kofs[KINST], vofs[KINST];
+#pragma unroll
+  for (int i = 0; i < KINST; ++i) {
+    const int row = (4 * i + wave) * ROWS_PER_KB + lane / DCH;
+    kofs[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    vofs[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+  }
+  auto issue = [&](int n, uint8_t* kdst, uint8_t* vdst) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
+#pragma unroll
+    for (int i = 0; i < KINST; ++i) {
+      buffer_load_lds16(rk, kdst + (4 * i + wave) * 1024, kofs[i]);
+      buffer_load_lds16(rv, vdst + (4 * i + wave) * 1024, vofs[i]);
+    }
+  };
+
+  // A operand of S^T = K Q^T and dP^T = V dO^T: tile t2 row m = l32 is key
+  // 32 t2 + row_key(l32), chunk 2 ks + hsel.
+  const int krow = row_key(l32);
+  int aaddr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aaddr[ks] = krow * (D * 2) + 16 * ((2 * ks + hsel) ^ kswz<D>(krow));
+  // K^T operand (rows = head dims, k = 8 consecutive keys per lane half).
+  const int gi = lane >> 4, li = lane & 15;
+  int tr[2][DT];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int row = 8 * (gi >> 1) + 4 * half + (li >> 2);
+      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
+      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ kswz<D>(row)) + 2 * (dcol & 7);
+    }
+
+  f32x16_t dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16_t{};
+
+  auto block = [&](int n, const uint8_t* __restrict__ kt, const uint8_t* __restrict__ vt) {
+    f32x16_t s[NT2], dp[NT2];
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2) s[t2] = dp[t2] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2) {
+        const int o = aaddr[ks] + t2 * 32 * (D * 2);
+        s[t2] = E::mfma32x32x16(*(const u32x4_t*)(kt + o), qf[ks], s[t2]);
+        dp[t2] = E::mfma32x32x16(*(const u32x4_t*)(vt + o), df[ks], dp[t2]);
+      }
+    // register 8c + u of lane half H in tile t2 holds key n BN + 32 t2 + 16 c + 8 H + u
+    u32x4_t sb[NT2][2];
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float sv[8];
+#pragma unroll
+        for (int uu = 0; uu < 8; ++uu) {
+          const int key = n * BN + 32 * t2 + 16 * c + 8 * hsel + uu;
+          const bool vis = visible_key(qrow, key, sq, sk, off, p.wl, p.wr);
+          const float pr = vis ? fast_exp2(__builtin_fmaf(s[t2][8 * c + uu], p.scale_log2, -lse2)) : 0.f;
+          sv[uu] = pr * (dp[t2][8 * c + uu] - drow);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sb[t2][c][e] = E::pack2(sv[2 * e], sv[2 * e + 1]);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rows = (32 * t2 + 16 * c) * (D * 2);
+          const u32x2_t lo = lds_read_tr16(kt + tr[0][dt] + rows), hi = lds_read_tr16(kt + tr[1][dt] + rows);
+          u32x4_t a;
+          a[0] = lo[0], a[1] = lo[1], a[2] = hi[0], a[3] = hi[1];
+          dq[dt] = E::mfma32x32x16(a, sb[t2][c], dq[dt]);
+        }
+  };
+
+  uint8_t* const k0s = smem;
+  uint8_t* const k1s = smem + KTILE;
+  uint8_t* const v0s = smem + 2 * KTILE;
+  uint8_t* const v1s = smem + 3 * KTILE;
+  auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                  uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
+    if (n + 1 < n_hi) issue(n + 1, kn, vn);
+    block(n, kc, vc);
+  };
+  if (n_lo < n_hi) issue(n_lo, k0s, v0s);
+  for (int n = n_lo; n < n_hi; n += 2) {
+    wait_vmem_all();
+    __syncthreads();
+    step(k0s, v0s, k1s, v1s, n);
+    if (n + 1 < n_hi) {
+      wait_vmem_all();
+      __syncthreads();
+      step(k1s, v1s, k0s, v0s, n + 1);
+    }
+  }
+
+  // ---- dQ = scale (dQ^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3 of row qrow.
+  if (qrow < sq) {
+    uint16_t* op = p.dq + (int64_t)b * p.dq_sb + (int64_t)qrow * p.dq_ss + (int64_t)h * p.dq_sh;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        u32x2_t wq;
+        wq[0] = E::pack2(dq[dt][4 * J] * p.scale, dq[dt][4 * J + 1] * p.scale);
+        wq[1] = E::pack2(dq[dt][4 * J + 2] * p.scale, dq[dt][4 * J + 3] * p.scale);
+        *(u32x2_t*)(op + 32 * dt + 8 * J + 4 * hsel) = wq;
+      }
+  }
+}
+
+template <bool BF16, int D>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  // A kernel whose grid would be empty is skipped: with no query rows dK and dV
+  // are zero (the dK/dV kernel sees no query block), with no keys dQ is zero
+  // (the dQ kernel sees no key block).
+  const int64_t rows = (int64_t)p.batch * p.s_q * p.h_q;
+  hipError_t e = hipSuccess;
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_kt = (p.s_k + kBwdKeys - 1) / kBwdKeys;
+  if (n_kt > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(n_kt * p.h_kv * p.batch), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_qt = (p.s_q + kDqRows - 1) / kDqRows;
+  if (n_qt > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(n_qt * p.h_q * p.batch), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 64) return p.bf16 ? launch_bwd_t<true, 64>(p, stream) : launch_bwd_t<false, 64>(p, stream);
+  if (head_dim == 128) return p.bf16 ? launch_bwd_t<true, 128>(p, stream) : launch_bwd_t<false, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace exattn

@@ -240,6 +240,73 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
 
 extern "C" {
 
+exattn_status exattn_bwd_plan(const exattn_bwd_args* a, size_t* workspace_bytes_out) {
+  try {
+    clear_error();
+    BwdPlan pl;
+    exattn_status st = plan_bwd(a, &pl);
+    if (st != EXATTN_OK) return st;
+    if (workspace_bytes_out != nullptr) *workspace_bytes_out = pl.ws_bytes;
+    return EXATTN_OK;
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
+exattn_status exattn_bwd(const exattn_bwd_args* a, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  try {
+    clear_error();
+    BwdPlan pl;
+    exattn_status st = plan_bwd(a, &pl);
+    if (st != EXATTN_OK) return st;
+    if (pl.empty) return EXATTN_OK;
+    if (pl.ws_bytes > 0) {
+      if (workspace == nullptr || workspace_bytes < pl.ws_bytes)
+        return fail(EXATTN_E_WORKSPACE, "workspace of " + std::to_string(pl.ws_bytes) + " bytes required");
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(EXATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    BwdParams p{};
+    p.q = static_cast<const uint16_t*>(a->q);
+    p.k = static_cast<const uint16_t*>(a->k);
+    p.v = static_cast<const uint16_t*>(a->v);
+    p.o = static_cast<const uint16_t*>(a->o);
+    p.dout = static_cast<const uint16_t*>(a->dout);
+    p.lse = a->lse;
+    p.dq = static_cast<uint16_t*>(a->dq);
+    p.dk = static_cast<uint16_t*>(a->dk);
+    p.dv = static_cast<uint16_t*>(a->dv);
+    p.ws_d = static_cast<float*>(workspace);
+    p.ws_lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_lse2_offset);
+    p.q_sb = a->q_stride[0], p.q_ss = a->q_stride[1], p.q_sh = a->q_stride[2];
+    p.k_sb = a->k_stride[0], p.k_ss = a->k_stride[1], p.k_sh = a->k_stride[2];
+    p.v_sb = a->v_stride[0], p.v_ss = a->v_stride[1], p.v_sh = a->v_stride[2];
+    p.o_sb = a->o_stride[0], p.o_ss = a->o_stride[1], p.o_sh = a->o_stride[2];
+    p.do_sb = a->dout_stride[0], p.do_ss = a->dout_stride[1], p.do_sh = a->dout_stride[2];
+    p.dq_sb = a->dq_stride[0], p.dq_ss = a->dq_stride[1], p.dq_sh = a->dq_stride[2];
+    p.dk_sb = a->dk_stride[0], p.dk_ss = a->dk_stride[1], p.dk_sh = a->dk_stride[2];
+    p.dv_sb = a->dv_stride[0], p.dv_ss = a->dv_stride[1], p.dv_sh = a->dv_stride[2];
+    p.lse_sb = a->lse_stride[0], p.lse_sh = a->lse_stride[1];
+    p.batch = a->batch;
+    p.s_q = a->seqlen_q;
+    p.s_k = a->seqlen_k;
+    p.h_q = a->heads_q;
+    p.h_kv = a->heads_kv;
+    p.group = pl.group;
+    p.scale = pl.scale;
+    p.scale_log2 = pl.scale_log2;
+    p.wl = pl.wl;
+    p.wr = pl.wr;
+    p.bf16 = pl.bf16 ? 1 : 0;
+    hipError_t e = launch_bwd(p, pl.head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+    return EXATTN_OK;
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
 exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t workspace_bytes,
                             void* stream) {
   return run_decode(a, nullptr, nullptr, workspace, workspace_bytes, stream);
@@ -274,6 +341,7 @@ size_t exattn_args_size(int32_t which) {
          : which == 1 ? sizeof(exattn_decode_args)
          : which == 2 ? sizeof(exattn_kv_new)
          : which == 3 ? sizeof(exattn_paged_kv)
+         : which == 4 ? sizeof(exattn_bwd_args)
                       : 0;
 }
 

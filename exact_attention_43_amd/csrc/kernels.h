@@ -68,11 +68,35 @@ struct DecParams {
   int64_t k_sp, v_sp;
 };
 
+// Backward (dense layouts): dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* ws_d;     // [batch][h_q][s_q]: dO_i . O_i
+  float* ws_lse2;  // [batch][h_q][s_q]: LSE log2 e, +inf for rows without keys
+  int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh, do_sb, do_ss, do_sh;
+  int64_t dq_sb, dq_ss, dq_sh, dk_sb, dk_ss, dk_sh, dv_sb, dv_ss, dv_sh;
+  int64_t lse_sb, lse_sh;
+  int32_t batch, s_q, s_k, h_q, h_kv, group;
+  float scale, scale_log2;
+  int32_t wl, wr;  // wr = 0 for causal; < 0 unbounded
+  int32_t bf16;
+};
+
 int prefill_rows_per_tile();
 // groups: 1 or 2 groups of 4 waves per work group (d = 256 always uses 1).
 hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,
                           int groups, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softcap,
                          hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace exattn

@@ -225,6 +225,53 @@ exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n) 
   return EXATTN_OK;
 }
 
+exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
+  if (a == nullptr || pl == nullptr) return fail(EXATTN_E_INVALID, "args is NULL");
+  *pl = BwdPlan{};
+  exattn_status st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->batch);
+  if (st != EXATTN_OK) return st;
+  if (a->head_dim == 256)
+    return fail(EXATTN_E_UNSUPPORTED, "the backward provides head_dim 64 and 128");
+  if (a->seqlen_q < 0 || a->seqlen_k < 0) return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k is negative");
+  float scale_log2, cap_in, cap_out;
+  bool cap;
+  st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &scale_log2, &cap_in, &cap_out, &cap);
+  if (st != EXATTN_OK) return st;
+  if (cap) return fail(EXATTN_E_UNSUPPORTED, "the backward does not provide softcap");
+  pl->bf16 = a->dtype == EXATTN_BF16;
+  pl->head_dim = a->head_dim;
+  pl->group = a->heads_q / a->heads_kv;
+  pl->scale_log2 = scale_log2;
+  pl->scale = scale_log2 / kLog2eHost;
+  pl->wl = a->window_left < 0 ? -1 : a->window_left;
+  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)a->seqlen_q;
+  pl->ws_lse2_offset = (rows * 4 + 255) & ~(size_t)255;
+  pl->ws_bytes = rows > 0 ? pl->ws_lse2_offset + ((rows * 4 + 255) & ~(size_t)255) : 0;
+  pl->empty = a->batch == 0 || (a->seqlen_q == 0 && a->seqlen_k == 0);
+  if (pl->empty) return EXATTN_OK;
+  const void* ptrs[9] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse};
+  const bool need[9] = {a->seqlen_q > 0, a->seqlen_k > 0, a->seqlen_k > 0, a->seqlen_q > 0,
+                        a->seqlen_q > 0, a->seqlen_q > 0, a->seqlen_k > 0, a->seqlen_k > 0,
+                        a->seqlen_q > 0};
+  for (int i = 0; i < 9; ++i) {
+    if (need[i] && ptrs[i] == nullptr)
+      return fail(EXATTN_E_INVALID, "q, k, v, o, dout, lse, dq, dk and dv must not be NULL");
+    if (i < 8 && ptrs[i] != nullptr && !aligned16(ptrs[i]))
+      return fail(EXATTN_E_INVALID, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  }
+  if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
+  const int64_t* strides[8] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride,
+                               a->dout_stride, a->dq_stride, a->dk_stride, a->dv_stride};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (!stride_ok(strides[t][i]))
+        return fail(EXATTN_E_INVALID, "backward strides must be non-negative multiples of 8 elements");
+  if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides are negative");
+  if (rows > ((size_t)1 << 31) / 2) return fail(EXATTN_E_INVALID, "too many rows for one backward");
+  return EXATTN_OK;
+}
+
 int decode_keys_per_step(int head_dim, int hpw) {
   const int nw = head_dim == 256 ? 4 : 8;                 // waves per work group
   const int hpwv = head_dim == 64 && hpw == 16 ? 2 : 1;    // heads per wave

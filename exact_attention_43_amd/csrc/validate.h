@@ -61,6 +61,16 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
 // (which plan_decode has accepted).
 exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n);
 
+// Checked backward arguments, resolved for the launch.
+struct BwdPlan {
+  bool bf16 = false;
+  bool empty = false;  // nothing to compute (batch 0 or no query rows and no keys)
+  int head_dim = 0, group = 1, wl = -1, wr = -1;
+  float scale = 0.f, scale_log2 = 0.f;
+  size_t ws_bytes = 0, ws_lse2_offset = 0;
+};
+exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl);
+
 // Keys per step of the decode kernel for this head_dim and heads per work
 // group: 16 times the waves that share one head slot (the kernel derives the
 // same from its wave count and head slots).

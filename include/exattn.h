@@ -214,6 +214,41 @@ exattn_status exattn_decode_paged(const exattn_decode_args *args, const exattn_p
                                   const exattn_kv_new *kv_new, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/*
+ * Backward of the dense forward (the third "next" row): dQ, dK, dV from Q, K,
+ * V, the forward's O and LSE, and the upstream gradient dO, recomputing S and
+ * P ("FlashAttention完整说明", section 二.2: only O and the softmax statistics
+ * are kept).  Same layouts and masks as exattn_fwd for fixed lengths
+ * (element strides over batch, token, head; head_dim contiguous); dq like q,
+ * dk and dv like k and v; lse as exattn_fwd writes it (fp32, element (b, h, i)
+ * at lse[b * lse_stride[0] + h * lse_stride[1] + i]).  A KV head's dK and dV
+ * sum over the query heads that read it.  Deterministic (no atomics).
+ * Provided: head_dim 64 and 128, no softcap, fixed lengths; other cases return
+ * EXATTN_E_UNSUPPORTED.  workspace: 2 * batch * heads_q * seqlen_q * 4 bytes
+ * (exattn_bwd_plan), 256-byte aligned, scratch owned by the caller.
+ */
+typedef struct {
+  int32_t dtype; /* exattn_dtype */
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], dout_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  int64_t lse_stride[2];
+  float softmax_scale; /* 0 or NaN: 1/sqrt(head_dim) */
+  float softcap;       /* must be <= 0 (off) */
+  int32_t causal;
+  int32_t window_left, window_right;
+} exattn_bwd_args;
+
+/* Host-only: the workspace size (bytes) exattn_bwd needs for these arguments. */
+exattn_status exattn_bwd_plan(const exattn_bwd_args *args, size_t *workspace_bytes_out);
+
+/* Run the backward: three kernels in order on the stream. */
+exattn_status exattn_bwd(const exattn_bwd_args *args, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
 /* The automatic split count, as a pure function (no device query).  One work
  * group covers up to 1024/head_dim adjacent KV heads (16 at d = 64, 8 at
  * d = 128, 4 at d = 256; a power of two no larger than heads_kv) and 16 of
@@ -224,8 +259,9 @@ int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_
                                   int32_t seqlen_k, int32_t head_dim, int32_t num_cus);
 
 /* sizeof(exattn_fwd_args) for which = 0, sizeof(exattn_decode_args) for which = 1,
- * sizeof(exattn_kv_new) for which = 2, sizeof(exattn_paged_kv) for which = 3, 0
- * otherwise: lets a binding check its mirror of the structs. */
+ * sizeof(exattn_kv_new) for which = 2, sizeof(exattn_paged_kv) for which = 3,
+ * sizeof(exattn_bwd_args) for which = 4, 0 otherwise: lets a binding check its
+ * mirror of the structs. */
 size_t exattn_args_size(int32_t which);
 
 const char *exattn_status_string(int32_t status);

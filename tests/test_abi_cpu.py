@@ -41,6 +41,7 @@ def test_struct_layout_and_version(L):
     assert L.exattn_args_size(1) == C.sizeof(ex.DecodeArgs)
     assert L.exattn_args_size(2) == C.sizeof(ex.KvNew)
     assert L.exattn_args_size(3) == C.sizeof(ex.PagedKv)
+    assert L.exattn_args_size(4) == C.sizeof(ex.BwdArgs)
     assert L.exattn_args_size(7) == 0
     assert L.exattn_abi_version() == 1
     assert L.exattn_status_string(0) == b"EXATTN_OK"
@@ -233,6 +234,70 @@ def test_decode_workspace_checks(L):
     assert L.exattn_decode_plan(C.byref(a2), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
     assert ns.value == 4
     assert L.exattn_decode(C.byref(_dec(batch=0)), None, 0, None) == ex.EXATTN_OK
+
+
+def _bwd(**kw):
+    a = ex.BwdArgs()
+    a.dtype, a.batch, a.seqlen_q, a.seqlen_k = 1, 2, 64, 96
+    a.heads_q, a.heads_kv, a.head_dim = 4, 2, 128
+    a.q = a.k = a.v = a.o = a.dout = a.lse = a.dq = a.dk = a.dv = FAKE
+    for n in ("q", "o", "dout", "dq"):
+        getattr(a, n + "_stride")[:] = [64 * 4 * 128, 4 * 128, 128]
+    for n in ("k", "v", "dk", "dv"):
+        getattr(a, n + "_stride")[:] = [96 * 2 * 128, 2 * 128, 128]
+    a.lse_stride[:] = [4 * 64, 64]
+    a.window_left = a.window_right = -1
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(a, key)[:] = val
+        else:
+            setattr(a, key, val)
+    return a
+
+
+BAD_BWD = [
+    ("dtype", dict(dtype=3), ex.EXATTN_E_UNSUPPORTED),
+    ("head_dim 256", dict(head_dim=256), ex.EXATTN_E_UNSUPPORTED),
+    ("head_dim 80", dict(head_dim=80), ex.EXATTN_E_UNSUPPORTED),
+    ("softcap", dict(softcap=30.0), ex.EXATTN_E_UNSUPPORTED),
+    ("heads ratio", dict(heads_q=3), ex.EXATTN_E_INVALID),
+    ("negative seqlen", dict(seqlen_q=-1), ex.EXATTN_E_INVALID),
+    ("null dout", dict(dout=None), ex.EXATTN_E_INVALID),
+    ("null dk", dict(dk=None), ex.EXATTN_E_INVALID),
+    ("null lse", dict(lse=None), ex.EXATTN_E_INVALID),
+    ("misaligned dq", dict(dq=FAKE + 8), ex.EXATTN_E_INVALID),
+    ("misaligned lse", dict(lse=FAKE + 2), ex.EXATTN_E_INVALID),
+    ("odd stride", dict(dv_stride=[96 * 2 * 128, 2 * 128 + 2, 128]), ex.EXATTN_E_INVALID),
+    ("negative lse stride", dict(lse_stride=[-64, 64]), ex.EXATTN_E_INVALID),
+    ("inf scale", dict(softmax_scale=float("inf")), ex.EXATTN_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_BWD, ids=[c[0] for c in BAD_BWD])
+def test_bwd_rejects(L, name, kw, status):
+    a = _bwd(**kw)
+    assert L.exattn_bwd_plan(C.byref(a), None) == status, (name, L.exattn_last_error())
+    assert L.exattn_bwd(C.byref(a), C.c_void_p(FAKE), 1 << 30, None) == status, L.exattn_last_error()
+    assert L.exattn_last_error()
+
+
+def test_bwd_workspace_and_empty(L):
+    a = _bwd()
+    wb = C.c_size_t(0)
+    assert L.exattn_bwd_plan(C.byref(a), C.byref(wb)) == ex.EXATTN_OK
+    rows = 2 * 4 * 64
+    assert wb.value == 2 * ((rows * 4 + 255) // 256 * 256)
+    assert L.exattn_bwd(C.byref(a), None, 0, None) == ex.EXATTN_E_WORKSPACE
+    assert L.exattn_bwd(C.byref(a), C.c_void_p(FAKE), wb.value - 1, None) == ex.EXATTN_E_WORKSPACE
+    assert L.exattn_bwd(C.byref(a), C.c_void_p(FAKE + 16), wb.value, None) == ex.EXATTN_E_WORKSPACE
+    assert L.exattn_bwd(None, None, 0, None) == ex.EXATTN_E_INVALID
+    assert L.exattn_bwd_plan(None, None) == ex.EXATTN_E_INVALID
+    # nothing to compute: no launch, no pointer needed
+    assert L.exattn_bwd(C.byref(_bwd(batch=0, q=None, dq=None)), None, 0, None) == ex.EXATTN_OK
+    assert L.exattn_bwd(C.byref(_bwd(seqlen_q=0, seqlen_k=0, q=None, k=None)), None, 0, None) == ex.EXATTN_OK
+    # no query rows: no workspace, and q, o, dout, dq, lse may be NULL
+    z = _bwd(seqlen_q=0, q=None, o=None, dout=None, dq=None, lse=None)
+    assert L.exattn_bwd_plan(C.byref(z), C.byref(wb)) == ex.EXATTN_OK and wb.value == 0
 
 
 def test_auto_splits_rules(L):

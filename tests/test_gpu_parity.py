@@ -349,6 +349,81 @@ def test_decode_paged_rejects_small_pages():
                              block_table=dbt)
 
 
+# Gradient tolerance.  The pages give none for the backward.  The kernels round
+# P and dS to the input type before their MFMAs, form D = dO . O from the
+# output O rounded to the input type, and round dQ, dK, dV once more.  Each
+# gradient element is a sum of terms; rounding each term's factors by a unit
+# roundoff u moves the sum by at most about u times the sum of the terms'
+# absolute values (the oracle's term magnitudes), whatever the cancellation.
+# So per element |g - g_ref| <= 4 u (mag + |g_ref|), u = 2^-8 for bf16 and
+# 2^-11 for fp16: one u each for P or dS, D, the output rounding, and one in
+# reserve (the forward's own O and LSE errors).  Where mag and g_ref are both
+# 0 (a row or key that sees nothing) the gradient must be exactly 0.
+GRAD_U = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+
+
+def assert_grad_close(g, ref, mag, dtype, where):
+    g = g.detach().float().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, f"{where}: shape {g.shape} vs {ref.shape}"
+    assert np.isfinite(g).all(), f"{where}: non-finite gradient"
+    u = GRAD_U[dtype]
+    bound = 4 * u * (np.asarray(mag) + np.abs(ref))
+    err = np.abs(g - ref)
+    bad = err > bound
+    worst = float(np.max(np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), 0.0))) if err.size else 0.0
+    print(f"{where}: worst err / bound = {worst:.3f}")
+    assert not bad.any(), (f"{where}: {int(bad.sum())} of {bad.size} out of tolerance (max err {err.max():.3e}); "
+                           f"first at {np.argwhere(bad)[:3].tolist()}")
+
+
+BWD_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, dtype, causal, window, seed
+    (2, 200, 200, 4, 4, 128, torch.bfloat16, True, (-1, -1), 200),
+    (1, 130, 300, 8, 2, 64, torch.float16, False, (-1, -1), 201),
+    (2, 257, 100, 4, 1, 128, torch.float16, True, (-1, -1), 202),    # rows without keys
+    (1, 300, 300, 2, 2, 128, torch.bfloat16, False, (50, 10), 203),
+    (1, 64, 64, 2, 2, 64, torch.bfloat16, False, (-1, -1), 204),
+    (1, 1, 513, 4, 2, 128, torch.bfloat16, True, (-1, -1), 205),      # one row
+    (1, 77, 40, 4, 2, 64, torch.float16, False, (5, -1), 206),        # left window only
+    (2, 1024, 1024, 16, 16, 128, torch.bfloat16, True, (-1, -1), 207),  # the causal training shape
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"g{c[-1]}" for c in BWD_CASES])
+def test_backward(case):
+    """dQ, dK, dV from the GPU forward's O and LSE against the oracle's gradients;
+    two runs bitwise equal (no atomics)."""
+    b, sq, sk, hq, hkv, d, dt, causal, window, seed = case
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=seed, dtype=dt)
+    dout = W.qkv(b, sq, 1, hq, 1, d, seed=seed + 1000, dtype=dt)[0]
+    dq_, dk_, dv_, ddo = _dev(q, k, v, dout)
+    out, lse = ex.attn_func(dq_, dk_, dv_, causal=causal, window_size=window)
+    gq, gk, gv = ex.attn_backward(ddo, dq_, dk_, dv_, out, lse, causal=causal, window_size=window)
+    gq2, gk2, gv2 = ex.attn_backward(ddo, dq_, dk_, dv_, out, lse, causal=causal, window_size=window)
+    torch.cuda.synchronize()
+    assert torch.equal(gq, gq2) and torch.equal(gk, gk2) and torch.equal(gv, gv2)
+    rq, rk, rv = oracle.attention_backward(q, k, v, dout, causal=causal, window_size=window)
+    mq, mk, mv = oracle.attention_backward_magnitudes(q, k, v, dout, causal=causal, window_size=window)
+    assert_grad_close(gq, rq, mq, dt, "dq")
+    assert_grad_close(gk, rk, mk, dt, "dk")
+    assert_grad_close(gv, rv, mv, dt, "dv")
+
+
+@pytest.mark.parametrize("s_q,s_k", [(0, 50), (40, 0)])
+def test_backward_empty_side(s_q, s_k):
+    """No query rows: dK = dV = 0; no keys: dQ = 0 (the buffers start as NaN)."""
+    q, k, v = W.qkv(2, s_q, s_k, 4, 2, 128, seed=208, dtype=torch.bfloat16)
+    dout = W.qkv(2, s_q, 1, 4, 1, 128, seed=209, dtype=torch.bfloat16)[0]
+    dq_, dk_, dv_, ddo = _dev(q, k, v, dout)
+    out, lse = ex.attn_func(dq_, dk_, dv_, causal=False)
+    gq, gk, gv = (torch.full_like(t, float("nan")) for t in (dq_, dk_, dv_))
+    ex.attn_backward(ddo, dq_, dk_, dv_, out, lse, dq=gq, dk=gk, dv=gv)
+    torch.cuda.synchronize()
+    for t in (gq, gk, gv):
+        assert torch.equal(t, torch.zeros_like(t))
+
+
 # --------------------------------------------------------------------------
 # masks, tails and degenerate cases
 # --------------------------------------------------------------------------

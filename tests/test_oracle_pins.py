@@ -480,6 +480,55 @@ def pin_backward():
             assert abs(fd - grad[idx]) < 1e-6, (idx, fd, grad[idx])
 
 
+def pin_backward_magnitudes():
+    """The term magnitudes bound the gradients from above; dV's equals dV where
+    dO >= 0 (P >= 0); and on a tiny case they match the terms enumerated one by
+    one in scalar Python (probabilities from exp and fsum, every term of D, dP
+    and the three products listed and summed in absolute value)."""
+    r = _rng(25)
+    for s_q, s_k, h_q, h_kv, causal, win in ((7, 9, 4, 2, True, (-1, -1)), (6, 6, 2, 2, False, (2, 0))):
+        q = r.standard_normal((2, s_q, h_q, 8))
+        k = r.standard_normal((2, s_k, h_kv, 8))
+        v = r.standard_normal((2, s_k, h_kv, 8))
+        do = r.standard_normal((2, s_q, h_q, 8))
+        g = oracle.attention_backward(q, k, v, do, causal=causal, window_size=win)
+        m = oracle.attention_backward_magnitudes(q, k, v, do, causal=causal, window_size=win)
+        for gi, mi in zip(g, m):
+            assert np.all(mi >= np.abs(gi) - 1e-12)
+        _, _, dv = oracle.attention_backward(q, k, v, np.abs(do), causal=causal, window_size=win)
+        _, _, mv = oracle.attention_backward_magnitudes(q, k, v, np.abs(do), causal=causal, window_size=win)
+        assert np.allclose(mv, dv, atol=1e-12)
+    # scalar enumeration: s_q 3, s_k 4, two query heads on one KV head, causal, d 3
+    s_q, s_k, d, scale = 3, 4, 3, 0.6
+    q = r.standard_normal((1, s_q, 2, d))
+    k = r.standard_normal((1, s_k, 1, d))
+    v = r.standard_normal((1, s_k, 1, d))
+    do = r.standard_normal((1, s_q, 2, d))
+    mq, mk, mv = oracle.attention_backward_magnitudes(q, k, v, do, softmax_scale=scale, causal=True)
+    wq = np.zeros_like(mq)
+    wk = np.zeros_like(mk)
+    wv = np.zeros_like(mv)
+    for h in range(2):
+        for i in range(s_q):
+            keys = [j for j in range(s_k) if j <= i + s_k - s_q]
+            sc = {j: scale * math.fsum(q[0, i, h, t] * k[0, j, 0, t] for t in range(d)) for j in keys}
+            top = max(sc.values())
+            z = math.fsum(math.exp(sc[j] - top) for j in keys)
+            pr = {j: math.exp(sc[j] - top) / z for j in keys}
+            o = [math.fsum(pr[j] * v[0, j, 0, t] for j in keys) for t in range(d)]
+            dterms = math.fsum(abs(do[0, i, h, t] * o[t]) for t in range(d))
+            for j in keys:
+                dp = math.fsum(do[0, i, h, t] * v[0, j, 0, t] for t in range(d))
+                a = pr[j] * (abs(dp) + dterms)
+                for t in range(d):
+                    wq[0, i, h, t] += scale * a * abs(k[0, j, 0, t])
+                    wk[0, j, 0, t] += scale * a * abs(q[0, i, h, t])
+                    wv[0, j, 0, t] += pr[j] * abs(do[0, i, h, t])
+    assert np.allclose(mq, wq, rtol=1e-12, atol=1e-14)
+    assert np.allclose(mk, wk, rtol=1e-12, atol=1e-14)
+    assert np.allclose(mv, wv, rtol=1e-12, atol=1e-14)
+
+
 def pin_softcap():
     r = _rng(19)
     q = r.standard_normal((1, 6, 2, 16)) * 4
@@ -521,7 +570,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_backward, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_backward, pin_backward_magnitudes, pin_softcap,
         pin_default_scale]
 
 
