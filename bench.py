@@ -7,14 +7,16 @@ section 六.1).  Inputs are resident in device memory before the timed region.
 The FLOP count is the pages' 4*b*h*s_q*s_k*d halved for causal (Inference
 Cookbook FAQ Q16).  The KV-cache decode workload (batch 8, 16384 cached
 tokens, 32 query / 8 KV heads, d 128, bf16, automatic num_splits) is timed in
-the same run and reported as HBM GB/s under "decode".
+the same run and reported as HBM GB/s under "decode", and the backward of the
+prefill workload (dQ, dK, dV from O, LSE and dO) as TFLOPS under "backward".
 
 Prints one JSON line.  Options:
   --gpus N            only 1 is supported (the method runs on one GPU here)
   --steps K --warmup W
   --no-cpu-baseline   skip the CPU oracle timing
   --no-decode         skip the decode measurement
-  --only {prefill,decode,copy}  run one part only (for profiler runs)
+  --no-backward       skip the backward measurement
+  --only {prefill,decode,backward,copy}  run one part only (for profiler runs)
 """
 import argparse
 import hashlib
@@ -30,7 +32,8 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLO
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd TFLOPS (% bf16 MFMA peak) at b2 s1024 h16 d128; decode HBM GB/s"
 PREFILL_SOURCES = ["exact_attention_43_amd/csrc/fwd_prefill.hip",
-                   "exact_attention_43_amd/csrc/device_common.h"]
+                   "exact_attention_43_amd/csrc/device_common.h",
+                   "exact_attention_43_amd/csrc/tiles.h"]
 DECODE_SOURCES = ["exact_attention_43_amd/csrc/fwd_decode.hip",
                   "exact_attention_43_amd/csrc/device_common.h"]
 
@@ -62,7 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None)
     return ap.parse_args()
 
 
@@ -258,6 +262,57 @@ def run_decode(ex, W, args):
     }
 
 
+def run_backward(ex, W, args):
+    """The backward of the causal prefill workload: one step is one exattn_bwd call (three
+    kernels: row statistics, dK/dV, dQ) on resident q, k, v, o, lse and dO."""
+    import ctypes as C
+    import torch
+    w = W.WORKLOADS["causal_prefill"]
+    qkv = W.packed_qkv(w.batch, w.seqlen_q, w.heads_q, w.head_dim, seed=w.seed).cuda()
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    out, lse = ex.attn_func(q, k, v, causal=True)
+    dout = W.qkv(w.batch, w.seqlen_q, 1, w.heads_q, 1, w.head_dim, seed=w.seed + 7)[0].cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    a = ex.BwdArgs()
+    a.dtype = ex.EXATTN_BF16
+    a.batch, a.seqlen_q, a.seqlen_k = w.batch, w.seqlen_q, w.seqlen_k
+    a.heads_q, a.heads_kv, a.head_dim = w.heads_q, w.heads_kv, w.head_dim
+    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr()
+    a.lse = lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        getattr(a, f"{name}_stride")[:] = list(t.stride()[:3])
+    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    a.causal = 1
+    a.window_left = a.window_right = -1
+    L = ex.lib()
+    wb = C.c_size_t(0)
+    ex._raise_for(L.exattn_bwd_plan(C.byref(a), C.byref(wb)), "exattn_bwd_plan")
+    ws = torch.empty(max(wb.value, 256), dtype=torch.uint8, device="cuda")
+    ref = C.byref(a)
+    ws_ptr, ws_bytes = C.c_void_p(ws.data_ptr()), ws.numel()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        rc = L.exattn_bwd(ref, ws_ptr, ws_bytes, stream)
+        if rc != 0:
+            ex._raise_for(rc, "exattn_bwd")
+
+    steps = max(10, min(args.steps, 100))
+    t = time_steps(step, steps, max(2, args.warmup // 2))
+    fl = W.backward_flops(w)
+    tflops = fl / (t["region"] * 1e-3) / 1e12
+    return {
+        "workload": "backward of the causal prefill: q, k, v (2, 1024, 16, 128) bf16 from packed qkv, "
+                    "o and lse from the forward, dO synthetic",
+        "value": round(tflops, 3), "unit": "TFLOPS", "flops_per_call": fl,
+        "ms_per_call_avg": round(t["region"], 6), "ms_per_call_median": round(t["pair_median"], 6),
+        "ms_per_call_min": round(t["pair_min"], 6), "calls": steps,
+        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+    }
+
+
 def run_copy_calibration():
     """A plain device copy of known size, for scaling the HBM byte counters: 7 launches of a
     256 MiB fp32 multiply-by-one (each reads 256 MiB and writes 256 MiB)."""
@@ -291,6 +346,9 @@ def main():
         return
     if args.only == "decode":
         print(json.dumps(run_decode(ex, W, args)))
+        return
+    if args.only == "backward":
+        print(json.dumps(run_backward(ex, W, args)))
         return
 
     w, fl, t = run_prefill(ex, W, args)
@@ -327,6 +385,8 @@ def main():
     }
     if not args.no_decode:
         rec["decode"] = run_decode(ex, W, args)
+    if not args.no_backward:
+        rec["backward"] = run_backward(ex, W, args)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, fl)
     print(json.dumps(rec))

@@ -3,10 +3,9 @@
 Every HIP source is compiled with packed-fp32 instruction selection switched
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass of
 hipcc warns that it does not know that feature, which is harmless.  MFMA
-accumulators of the forward kernels are kept in architectural VGPRs
-(``-amdgpu-mfma-vgpr-form``), so the softmax and the rare O rescale touch them
-without AGPR copies; the backward (``bwd.hip``) holds dK and dV accumulators
-beside K and V and lets the compiler place accumulators in AGPRs.
+accumulators are kept in architectural VGPRs (``-amdgpu-mfma-vgpr-form``), so
+the softmax, the O rescale and the backward's P and dS touch them without AGPR
+copies; AGPRs then only hold MFMA source operands the allocator moves there.
 
     python -m exact_attention_43_amd.build          # build
     python -m exact_attention_43_amd.build --check  # also build the host-only checker
@@ -28,7 +27,6 @@ LIB = os.path.join(PKG, "libexattn.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["fwd_prefill.hip", "fwd_decode.hip", "bwd.hip", "exattn_api.cpp"]
-AGPR_SOURCES = {"bwd.hip"}  # compiled without -amdgpu-mfma-vgpr-form
 HOST_SOURCES = ["validate.cpp"]
 
 
@@ -59,7 +57,7 @@ def build(verbose: bool = False) -> str:
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         jobs.append([hipcc, f"--offload-arch={ARCH}", *common, "-Xclang", "-target-feature",
                      "-Xclang", "-packed-fp32-ops",
-                     *([] if src in AGPR_SOURCES else ["-mllvm", "-amdgpu-mfma-vgpr-form"]), *lang, "-c",
+                     "-mllvm", "-amdgpu-mfma-vgpr-form", *lang, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")

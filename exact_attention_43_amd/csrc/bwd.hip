@@ -38,6 +38,20 @@ __device__ __forceinline__ bool visible_key(int i, int j, int sq, int sk, int of
   return i < sq && j < sk && (wr < 0 || j <= i + off + wr) && (wl < 0 || j >= i + off - wl);
 }
 
+// Tiles read both as A operands (16 lanes: 16 rows, one 16-byte chunk each)
+// and transposed (lanes of one read: 4 consecutive rows x 2 or 4 adjacent
+// chunks): chunk c of row r is stored at c ^ qswz(r).  Over 16 rows qswz takes
+// 16 distinct values (8 per row parity for 128-byte rows, two of which share a
+// 256-byte bank row), and 4 consecutive rows differ in bits 2-3 (bit 2 for the
+// rows of one parity at d = 64), so both read shapes hit distinct bank groups.
+template <int D>
+__device__ __forceinline__ int qswz(int r) {
+  if constexpr (D == 64)
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  else
+    return 4 * (r & 3) + ((r >> 2) & 3);
+}
+
 // The two 16-bit values of a 32-bit word as floats.
 template <bool BF16>
 __device__ __forceinline__ float lo_f32(uint32_t w) {
@@ -54,33 +68,37 @@ __device__ __forceinline__ float hi_f32(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// D_i = dO_i . O_i (fp32) and LSE_i log2 e, or +inf for a row without keys
-// (then exp2(s - lse2) = 0 everywhere).  One thread per (batch, row, head).
+// Per row: LSE log2 e (+inf for a row without keys, so that exp2(s - lse2) = 0
+// everywhere) and D_i = dO_i . O_i (fp32), stored as one pair.  D / 8 lanes per
+// row read 16 bytes of O and dO each; grid (row blocks, heads, batch).
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
-  const int64_t rows = (int64_t)p.batch * p.s_q * p.h_q;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= rows) return;
-  const int h = (int)(t % p.h_q);
-  const int i = (int)((t / p.h_q) % p.s_q);
-  const int b = (int)(t / ((int64_t)p.h_q * p.s_q));
-  const uint16_t* o = p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
-  const uint16_t* d = p.dout + (int64_t)b * p.do_sb + (int64_t)i * p.do_ss + (int64_t)h * p.do_sh;
+  constexpr int LPR = D / 8;  // lanes per row
+  const int i = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const bool in = i < p.s_q;
   float acc = 0.f;
-#pragma unroll 2
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4_t a = *(const u32x4_t*)(o + 8 * c);
-    const u32x4_t g = *(const u32x4_t*)(d + 8 * c);
+  if (in) {
+    const u32x4_t a = *(const u32x4_t*)(p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh +
+                                        8 * part);
+    const u32x4_t g = *(const u32x4_t*)(p.dout + (int64_t)b * p.do_sb + (int64_t)i * p.do_ss +
+                                        (int64_t)h * p.do_sh + 8 * part);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc = __builtin_fmaf(lo_f32<BF16>(a[e]), lo_f32<BF16>(g[e]), acc);
       acc = __builtin_fmaf(hi_f32<BF16>(a[e]), hi_f32<BF16>(g[e]), acc);
     }
   }
-  const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i];
-  const int64_t w = ((int64_t)b * p.h_q + h) * p.s_q + i;
-  p.ws_d[w] = acc;
-  p.ws_lse2[w] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+  if (in && part == 0) {
+    const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i];
+    f32x2_t st;
+    st[0] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+    st[1] = acc;
+    *(f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * p.s_q + i)) = st;
+  }
 }
 
 // dK, dV for 128 keys of one KV head (4 waves x 32 keys).
@@ -136,33 +154,31 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   const int g = p.group;
   const int steps = nqb * g;  // (head, query block) pairs
 
-  // ---- DMA: tile row r, stored chunk (lane % DCH) at r * D * 2 + 16 * ((lane % DCH) ^ kswz(r)).
+  // ---- DMA: tile row r, stored chunk (lane % DCH) at r * D * 2 + 16 * ((lane % DCH) ^ qswz(r)).
   uint32_t q_ofs[SLICES / 4], d_ofs[SLICES / 4];
 #pragma unroll
   for (int i = 0; i < SLICES / 4; ++i) {
     const int row = (4 * i + wave) * ROWS_PER_KB + lane / DCH;
-    q_ofs[i] = (uint32_t)(row * p.q_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
-    d_ofs[i] = (uint32_t)(row * p.do_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    q_ofs[i] = (uint32_t)(row * p.q_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
+    d_ofs[i] = (uint32_t)(row * p.do_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
   }
+  const uint16_t* const qb_ptr = p.q + (int64_t)b * p.q_sb;
+  const uint16_t* const db_ptr = p.dout + (int64_t)b * p.do_sb;
+  const float* const sb_ptr = p.ws_stats + (int64_t)b * p.h_q * sq * 2;
   auto issue = [&](int st, uint8_t* dst) {
     const int h = hk * g + st / nqb;
     const int q0 = (qb_lo + st % nqb) * kBwdRows;
-    const uint16_t* qg = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    const uint16_t* dg = p.dout + (int64_t)b * p.do_sb + (int64_t)h * p.do_sh;
-    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qg, p.q_ss, q0, sq, kBwdRows);
-    const __amdgpu_buffer_rsrc_t rd = block_rsrc<D>(dg, p.do_ss, q0, sq, kBwdRows);
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qb_ptr + (int64_t)h * p.q_sh, p.q_ss, q0, sq, kBwdRows);
+    const __amdgpu_buffer_rsrc_t rd = block_rsrc<D>(db_ptr + (int64_t)h * p.do_sh, p.do_ss, q0, sq, kBwdRows);
+    // the rows' statistics: 32 (lse2, D) pairs, 256 bytes, by lanes 0-15 of wave 0
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(sb_ptr + ((int64_t)h * sq + q0) * 2), 0, 8 * min(kBwdRows, sq - q0), 0x00020000);
 #pragma unroll
     for (int i = 0; i < SLICES / 4; ++i) {
       buffer_load_lds16(rq, dst + (4 * i + wave) * 1024, q_ofs[i]);
       buffer_load_lds16(rd, dst + TILE + (4 * i + wave) * 1024, d_ofs[i]);
     }
-    // the rows' statistics: 32 floats each, by lanes 0-7 of waves 0 and 1
-    if (wave < 2 && lane < 8) {
-      const float* src = (wave == 0 ? p.ws_lse2 : p.ws_d) + ((int64_t)b * p.h_q + h) * sq;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(src + q0), 0, (int)(4 * max(0, min(kBwdRows, sq - q0))), 0x00020000);
-      buffer_load_lds16(rs, dst + 2 * TILE + 128 * wave, 16u * lane);
-    }
+    if (wave == 0 && lane < 16) buffer_load_lds16(rs, dst + 2 * TILE, 16u * lane);
   };
 
   // ---- loop-invariant LDS addresses.
@@ -171,7 +187,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   const int arow = row_key(l32);
   int aaddr[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) aaddr[ks] = arow * (D * 2) + 16 * ((2 * ks + hsel) ^ kswz<D>(arow));
+  for (int ks = 0; ks < KS; ++ks) aaddr[ks] = arow * (D * 2) + 16 * ((2 * ks + hsel) ^ qswz<D>(arow));
   // Transposed A operands (dO^T, Q^T; rows = head dims, k = 8 consecutive
   // queries per lane half) for MFMA (c, dt): two transposing reads of 4 rows.
   const int gi = lane >> 4, li = lane & 15;
@@ -182,18 +198,19 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
     for (int dt = 0; dt < DT; ++dt) {
       const int row = 8 * (gi >> 1) + 4 * half + (li >> 2);
       const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
-      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ kswz<D>(row)) + 2 * (dcol & 7);
+      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ qswz<D>(row)) + 2 * (dcol & 7);
     }
 
   f32x16_t dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16_t{};
 
-  auto block = [&](int st, const uint8_t* __restrict__ stg) {
+  // One (head, query block) pair: stage stg holds its tiles; the next pair's
+  // DMA into nxt is issued once this pair's first products are under way.
+  auto block = [&](int st, const uint8_t* __restrict__ stg, uint8_t* __restrict__ nxt) {
     const uint8_t* qt = stg;
     const uint8_t* dt_ = stg + TILE;
-    const float* lse2 = reinterpret_cast<const float*>(stg + 2 * TILE);
-    const float* dd = lse2 + 32;
+    const float* stats = reinterpret_cast<const float*>(stg + 2 * TILE);  // (lse2, D) per row
     const int q0 = (qb_lo + st % nqb) * kBwdRows;
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
@@ -201,23 +218,30 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
       s = E::mfma32x32x16(*(const u32x4_t*)(qt + aaddr[ks]), kf[ks], s);
       dp = E::mfma32x32x16(*(const u32x4_t*)(dt_ + aaddr[ks]), vf[ks], dp);
     }
-    // register 8c + u of lane half H holds query q0 + 16 c + 8 H + u
+    if (st + 1 < steps) issue(st + 1, nxt);
+    // register 8c + u of lane half H holds query q0 + 16 c + 8 H + u.  A block whose
+    // 32 x 32 pairs are all visible (rows and keys in range, inside the causal /
+    // window band) skips the mask.
+    const int kc0 = k0 + 32 * wave;
+    const bool full = q0 + kBwdRows <= sq && kc0 + 32 <= sk && (wr < 0 || kc0 + 31 <= q0 + off + wr) &&
+                      (p.wl < 0 || kc0 >= q0 + kBwdRows - 1 + off - p.wl);
     u32x4_t pb[2], sb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qi = 16 * c + 8 * hsel;
-      const u32x4_t l0 = *(const u32x4_t*)(lse2 + qi), l1 = *(const u32x4_t*)(lse2 + qi + 4);
-      const u32x4_t d0 = *(const u32x4_t*)(dd + qi), d1 = *(const u32x4_t*)(dd + qi + 4);
+      f32x4_t rs[4];  // rows qi + 2 j, qi + 2 j + 1: (lse2, D, lse2, D)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rs[j] = *(const f32x4_t*)(stats + 2 * (qi + 2 * j));
       float pv[8], sv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float l = __builtin_bit_cast(float, u < 4 ? l0[u] : l1[u - 4]);
-        const float di = __builtin_bit_cast(float, u < 4 ? d0[u] : d1[u - 4]);
-        const bool vis = visible_key(q0 + qi + u, kcol, sq, sk, off, p.wl, wr);
-        const float pr = vis ? fast_exp2(__builtin_fmaf(s[8 * c + u], p.scale_log2, -l)) : 0.f;
-        pv[u] = pr;
-        sv[u] = pr * (dp[8 * c + u] - di);
+      for (int u = 0; u < 8; ++u) pv[u] = fast_exp2(__builtin_fmaf(s[8 * c + u], p.scale_log2, -rs[u >> 1][2 * (u & 1)]));
+      if (!full) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (!visible_key(q0 + qi + u, kcol, sq, sk, off, p.wl, wr)) pv[u] = 0.f;
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sv[u] = pv[u] * (dp[8 * c + u] - rs[u >> 1][2 * (u & 1) + 1]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pb[c][e] = E::pack2(pv[2 * e], pv[2 * e + 1]);
@@ -242,19 +266,15 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
 
   uint8_t* const st0 = smem;
   uint8_t* const st1 = smem + STAGE;
-  auto step = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int st) {
-    if (st + 1 < steps) issue(st + 1, nxt);
-    block(st, cur);
-  };
   if (steps > 0) issue(0, st0);
   for (int st = 0; st < steps; st += 2) {
     wait_vmem_all();
     __syncthreads();
-    step(st0, st1, st);
+    block(st, st0, st1);
     if (st + 1 < steps) {
       wait_vmem_all();
       __syncthreads();
-      step(st1, st0, st + 1);
+      block(st + 1, st1, st0);
     }
   }
 
@@ -306,7 +326,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
   const int hk = h / p.group;
   const int sq = p.s_q, sk = p.s_k, off = sk - sq;
   const int q0 = qt * kDqRows;
-  const int qrow = q0 + 32 * wave + l32;
+  const int q0w = q0 + 32 * wave;  // this wave's first row
+  const int qrow = q0w + l32;
 
   // ---- visible key blocks of the tile.
   const int t1 = min(q0 + kDqRows, sq) - 1;
@@ -328,9 +349,10 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
       df[ks] = in ? *(const u32x4_t*)(dp + 16 * ks) : u32x4_t{0, 0, 0, 0};
     }
   }
-  const int64_t w = ((int64_t)b * p.h_q + h) * sq + qrow;
-  const float lse2 = qrow < sq ? p.ws_lse2[w] : __builtin_inff();
-  const float drow = qrow < sq ? p.ws_d[w] : 0.f;
+  f32x2_t rst;  // (lse2, D) of this lane's row
+  rst[0] = __builtin_inff(), rst[1] = 0.f;
+  if (qrow < sq) rst = *(const f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * sq + qrow));
+  const float lse2 = rst[0], drow = rst[1];
 
   const uint16_t* kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
   const uint16_t* vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
@@ -338,8 +360,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int i = 0; i < KINST; ++i) {
     const int row = (4 * i + wave) * ROWS_PER_KB + lane / DCH;
-    kofs[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
-    vofs[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    kofs[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
+    vofs[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
   }
   auto issue = [&](int n, uint8_t* kdst, uint8_t* vdst) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
@@ -356,7 +378,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
   const int krow = row_key(l32);
   int aaddr[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) aaddr[ks] = krow * (D * 2) + 16 * ((2 * ks + hsel) ^ kswz<D>(krow));
+  for (int ks = 0; ks < KS; ++ks) aaddr[ks] = krow * (D * 2) + 16 * ((2 * ks + hsel) ^ qswz<D>(krow));
   // K^T operand (rows = head dims, k = 8 consecutive keys per lane half).
   const int gi = lane >> 4, li = lane & 15;
   int tr[2][DT];
@@ -366,7 +388,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
     for (int dt = 0; dt < DT; ++dt) {
       const int row = 8 * (gi >> 1) + 4 * half + (li >> 2);
       const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
-      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ kswz<D>(row)) + 2 * (dcol & 7);
+      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ qswz<D>(row)) + 2 * (dcol & 7);
     }
 
   f32x16_t dq[DT];
@@ -385,7 +407,11 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
         s[t2] = E::mfma32x32x16(*(const u32x4_t*)(kt + o), qf[ks], s[t2]);
         dp[t2] = E::mfma32x32x16(*(const u32x4_t*)(vt + o), df[ks], dp[t2]);
       }
-    // register 8c + u of lane half H in tile t2 holds key n BN + 32 t2 + 16 c + 8 H + u
+    // register 8c + u of lane half H in tile t2 holds key n BN + 32 t2 + 16 c + 8 H + u.
+    // A block whose 32 x BN pairs are all visible skips the mask.
+    const int kb0 = n * BN;
+    const bool full = q0w + 32 <= sq && kb0 + BN <= sk && (p.wr < 0 || kb0 + BN - 1 <= q0w + off + p.wr) &&
+                      (p.wl < 0 || kb0 >= q0w + 31 + off - p.wl);
     u32x4_t sb[NT2][2];
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2)
@@ -393,12 +419,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdParams p) {
       for (int c = 0; c < 2; ++c) {
         float sv[8];
 #pragma unroll
-        for (int uu = 0; uu < 8; ++uu) {
-          const int key = n * BN + 32 * t2 + 16 * c + 8 * hsel + uu;
-          const bool vis = visible_key(qrow, key, sq, sk, off, p.wl, p.wr);
-          const float pr = vis ? fast_exp2(__builtin_fmaf(s[t2][8 * c + uu], p.scale_log2, -lse2)) : 0.f;
-          sv[uu] = pr * (dp[t2][8 * c + uu] - drow);
+        for (int uu = 0; uu < 8; ++uu) sv[uu] = fast_exp2(__builtin_fmaf(s[t2][8 * c + uu], p.scale_log2, -lse2));
+        if (!full) {
+#pragma unroll
+          for (int uu = 0; uu < 8; ++uu)
+            if (!visible_key(qrow, kb0 + 32 * t2 + 16 * c + 8 * hsel + uu, sq, sk, off, p.wl, p.wr)) sv[uu] = 0.f;
         }
+#pragma unroll
+        for (int uu = 0; uu < 8; ++uu) sv[uu] *= dp[t2][8 * c + uu] - drow;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb[t2][c][e] = E::pack2(sv[2 * e], sv[2 * e + 1]);
       }
@@ -461,7 +489,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.s_q * p.h_q;
   hipError_t e = hipSuccess;
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+    constexpr int rows_per_wg = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>),
+                       dim3((unsigned)((p.s_q + rows_per_wg - 1) / rows_per_wg), p.h_q, p.batch), dim3(256), 0,
+                       stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -277,8 +277,7 @@ exattn_status exattn_bwd(const exattn_bwd_args* a, void* workspace, size_t works
     p.dq = static_cast<uint16_t*>(a->dq);
     p.dk = static_cast<uint16_t*>(a->dk);
     p.dv = static_cast<uint16_t*>(a->dv);
-    p.ws_d = static_cast<float*>(workspace);
-    p.ws_lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_lse2_offset);
+    p.ws_stats = static_cast<float*>(workspace);
     p.q_sb = a->q_stride[0], p.q_ss = a->q_stride[1], p.q_sh = a->q_stride[2];
     p.k_sb = a->k_stride[0], p.k_ss = a->k_stride[1], p.k_sh = a->k_stride[2];
     p.v_sb = a->v_stride[0], p.v_ss = a->v_stride[1], p.v_sh = a->v_stride[2];

@@ -79,8 +79,7 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* ws_d;     // [batch][h_q][s_q]: dO_i . O_i
-  float* ws_lse2;  // [batch][h_q][s_q]: LSE log2 e, +inf for rows without keys
+  float* ws_stats;  // [batch][h_q][s_q][2]: LSE log2 e (+inf for rows without keys), dO_i . O_i
   int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh, do_sb, do_ss, do_sh;
   int64_t dq_sb, dq_ss, dq_sh, dk_sb, dk_ss, dk_sh, dv_sb, dv_ss, dv_sh;

@@ -246,8 +246,7 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
   pl->wl = a->window_left < 0 ? -1 : a->window_left;
   pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
   const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)a->seqlen_q;
-  pl->ws_lse2_offset = (rows * 4 + 255) & ~(size_t)255;
-  pl->ws_bytes = rows > 0 ? pl->ws_lse2_offset + ((rows * 4 + 255) & ~(size_t)255) : 0;
+  pl->ws_bytes = (rows * 8 + 255) & ~(size_t)255;  // (LSE log2 e, dO . O) per row
   pl->empty = a->batch == 0 || (a->seqlen_q == 0 && a->seqlen_k == 0);
   if (pl->empty) return EXATTN_OK;
   const void* ptrs[9] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse};
@@ -269,6 +268,8 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
         return fail(EXATTN_E_INVALID, "backward strides must be non-negative multiples of 8 elements");
   if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides are negative");
   if (rows > ((size_t)1 << 31) / 2) return fail(EXATTN_E_INVALID, "too many rows for one backward");
+  if (a->batch > 65535 || a->heads_q > 65535)
+    return fail(EXATTN_E_UNSUPPORTED, "the backward takes at most 65535 batch entries and query heads");
   return EXATTN_OK;
 }
 

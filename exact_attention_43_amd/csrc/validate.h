@@ -67,7 +67,7 @@ struct BwdPlan {
   bool empty = false;  // nothing to compute (batch 0 or no query rows and no keys)
   int head_dim = 0, group = 1, wl = -1, wr = -1;
   float scale = 0.f, scale_log2 = 0.f;
-  size_t ws_bytes = 0, ws_lse2_offset = 0;
+  size_t ws_bytes = 0;
 };
 exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl);
 

@@ -140,6 +140,14 @@ def flops(w: Workload) -> float:
     return f / 2 if w.causal else f
 
 
+def backward_flops(w: Workload) -> float:
+    """FLOPs of the recomputing backward: five products per visible (row, key)
+    pair and head (S again, dP = dO V^T, dV, dK and dQ) against the forward's
+    two, so 2.5 times ``flops`` (the forward's count extended by the number of
+    products; "FlashAttention完整说明", section 二.2 names them)."""
+    return 2.5 * flops(w)
+
+
 def algorithmic_bytes(w: Workload) -> int:
     """Q, K, V read once; O written once (storage dtype); LSE written once (fp32)."""
     e = 2

@@ -215,7 +215,7 @@ exattn_status exattn_decode_paged(const exattn_decode_args *args, const exattn_p
                                   size_t workspace_bytes, void *stream);
 
 /*
- * Backward of the dense forward (the third "next" row): dQ, dK, dV from Q, K,
+ * Backward of the dense forward: dQ, dK, dV from Q, K,
  * V, the forward's O and LSE, and the upstream gradient dO, recomputing S and
  * P ("FlashAttention完整说明", section 二.2: only O and the softmax statistics
  * are kept).  Same layouts and masks as exattn_fwd for fixed lengths
@@ -224,8 +224,13 @@ exattn_status exattn_decode_paged(const exattn_decode_args *args, const exattn_p
  * at lse[b * lse_stride[0] + h * lse_stride[1] + i]).  A KV head's dK and dV
  * sum over the query heads that read it.  Deterministic (no atomics).
  * Provided: head_dim 64 and 128, no softcap, fixed lengths; other cases return
- * EXATTN_E_UNSUPPORTED.  workspace: 2 * batch * heads_q * seqlen_q * 4 bytes
- * (exattn_bwd_plan), 256-byte aligned, scratch owned by the caller.
+ * EXATTN_E_UNSUPPORTED.  workspace: batch * heads_q * seqlen_q * 8 bytes rounded
+ * up to 256 (exattn_bwd_plan), 256-byte aligned, scratch owned by the caller.
+ * Errors (nothing launched): EXATTN_E_INVALID for NULL or misaligned pointers,
+ * negative sizes or strides that are not non-negative multiples of 8 elements;
+ * EXATTN_E_UNSUPPORTED as above; EXATTN_E_WORKSPACE for a missing, short or
+ * misaligned workspace; EXATTN_E_HIP when a launch fails.  Empty problems
+ * (batch 0, or no rows and no keys) launch nothing and return EXATTN_OK.
  */
 typedef struct {
   int32_t dtype; /* exattn_dtype */

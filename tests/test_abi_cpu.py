@@ -286,7 +286,7 @@ def test_bwd_workspace_and_empty(L):
     wb = C.c_size_t(0)
     assert L.exattn_bwd_plan(C.byref(a), C.byref(wb)) == ex.EXATTN_OK
     rows = 2 * 4 * 64
-    assert wb.value == 2 * ((rows * 4 + 255) // 256 * 256)
+    assert wb.value == (rows * 8 + 255) // 256 * 256
     assert L.exattn_bwd(C.byref(a), None, 0, None) == ex.EXATTN_E_WORKSPACE
     assert L.exattn_bwd(C.byref(a), C.c_void_p(FAKE), wb.value - 1, None) == ex.EXATTN_E_WORKSPACE
     assert L.exattn_bwd(C.byref(a), C.c_void_p(FAKE + 16), wb.value, None) == ex.EXATTN_E_WORKSPACE
