@@ -32,7 +32,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libexattn.so")
 
 EXATTN_OK, EXATTN_E_INVALID, EXATTN_E_UNSUPPORTED, EXATTN_E_WORKSPACE, EXATTN_E_HIP = range(5)
-EXATTN_F16, EXATTN_BF16 = 0, 1
+EXATTN_F16, EXATTN_BF16, EXATTN_FP8_E4M3 = 0, 1, 2
+
+
+class Fp8Descale(C.Structure):
+    """Mirror of exattn_fp8_descale."""
+    _fields_ = [("q", C.c_float), ("k", C.c_float), ("v", C.c_float)]
 
 
 class FwdArgs(C.Structure):
@@ -130,6 +135,8 @@ def lib():
             L.exattn_decode_paged.argtypes = [C.POINTER(DecodeArgs), C.POINTER(PagedKv), C.POINTER(KvNew),
                                               C.c_void_p, C.c_size_t, C.c_void_p]
             L.exattn_decode_paged.restype = C.c_int
+            L.exattn_fwd_fp8.argtypes = [C.POINTER(FwdArgs), C.POINTER(Fp8Descale), C.c_void_p]
+            L.exattn_fwd_fp8.restype = C.c_int
             L.exattn_bwd_plan.argtypes = [C.POINTER(BwdArgs), C.POINTER(C.c_size_t)]
             L.exattn_bwd_plan.restype = C.c_int
             L.exattn_bwd.argtypes = [C.POINTER(BwdArgs), C.c_void_p, C.c_size_t, C.c_void_p]
@@ -146,7 +153,8 @@ def lib():
             L.exattn_abi_version.restype = C.c_int32
             if (L.exattn_args_size(0) != C.sizeof(FwdArgs) or L.exattn_args_size(1) != C.sizeof(DecodeArgs)
                     or L.exattn_args_size(2) != C.sizeof(KvNew) or L.exattn_args_size(3) != C.sizeof(PagedKv)
-                    or L.exattn_args_size(4) != C.sizeof(BwdArgs)):
+                    or L.exattn_args_size(4) != C.sizeof(BwdArgs)
+                    or L.exattn_args_size(5) != C.sizeof(Fp8Descale)):
                 raise RuntimeError("libexattn.so struct layout does not match this binding; rebuild it")
             _lib_handle = L
     return _lib_handle
@@ -256,6 +264,48 @@ def attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_s
               q_st=q.stride()[:3], k_st=k.stride()[:3], v_st=v.stride()[:3], o_st=out.stride()[:3],
               lse_st=(lse.stride(0), lse.stride(1)), softmax_scale=softmax_scale, causal=causal,
               window_size=window_size, softcap=softcap)
+    return out, lse
+
+
+def attn_func_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_scale=None, causal=False,
+                  window_size=(-1, -1), out=None, lse=None):
+    """FP8 forward with a bf16 output (FAQ Q20).  q (b, s_q, h_q, d), k, v (b, s_k, h_kv, d) as
+    torch.float8_e4m3fn; the real inputs are the values times the descale factors.  Returns
+    (out bf16 (b, s_q, h_q, d), lse fp32 (b, h_q, s_q)).  head_dim 64 or 128, fixed lengths."""
+    _on_gpu(q, k, v, out, lse)
+    _check_last_dim(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (batch, seqlen, heads, head_dim)")
+    if not (q.dtype == k.dtype == v.dtype == torch.float8_e4m3fn):
+        raise ValueError("q, k and v must be torch.float8_e4m3fn")
+    b, s_q, h_q, d = q.shape
+    s_k, h_kv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != b or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((b, s_q, h_q, d), dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != (b, s_q, h_q, d):
+        raise ValueError("out must be bf16 (batch, seqlen_q, heads_q, head_dim)")
+    _check_last_dim(out)
+    if lse is None:
+        lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    a = FwdArgs()
+    a.dtype = EXATTN_FP8_E4M3
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = b, s_q, s_k, h_q, h_kv, d
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    a.q_stride[:] = list(q.stride()[:3])
+    a.k_stride[:] = list(k.stride()[:3])
+    a.v_stride[:] = list(v.stride()[:3])
+    a.o_stride[:] = list(out.stride()[:3])
+    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    a.softmax_scale = _scale(softmax_scale)
+    a.softcap = 0.0
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = _window(window_size)
+    ds = Fp8Descale(float(q_descale), float(k_descale), float(v_descale))
+    with torch.cuda.device(q.device):
+        st = lib().exattn_fwd_fp8(C.byref(a), C.byref(ds), C.c_void_p(_stream(q.device)))
+    _raise_for(st, "exattn_fwd_fp8")
     return out, lse
 
 
@@ -521,5 +571,5 @@ def auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus):
     return int(lib().exattn_decode_auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus))
 
 
-__all__ = ["attn_func", "attn_qkvpacked_func", "attn_kvpacked_func", "attn_varlen_func",
+__all__ = ["attn_func", "attn_func_fp8", "attn_qkvpacked_func", "attn_kvpacked_func", "attn_varlen_func",
            "attn_with_kvcache", "attn_backward", "decode_plan", "auto_splits", "lib", "library_path"]

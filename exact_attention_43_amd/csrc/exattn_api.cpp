@@ -240,6 +240,42 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
 
 extern "C" {
 
+exattn_status exattn_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d, void* stream) {
+  try {
+    clear_error();
+    Fp8Plan pl;
+    exattn_status st = plan_fwd_fp8(a, d, &pl);
+    if (st != EXATTN_OK) return st;
+    if (pl.empty) return EXATTN_OK;
+    Fp8Params p{};
+    p.q = static_cast<const uint8_t*>(a->q);
+    p.k = static_cast<const uint8_t*>(a->k);
+    p.v = static_cast<const uint8_t*>(a->v);
+    p.o = static_cast<uint16_t*>(a->o);
+    p.lse = a->lse;
+    p.q_sb = a->q_stride[0], p.q_ss = a->q_stride[1], p.q_sh = a->q_stride[2];
+    p.k_sb = a->k_stride[0], p.k_ss = a->k_stride[1], p.k_sh = a->k_stride[2];
+    p.v_sb = a->v_stride[0], p.v_ss = a->v_stride[1], p.v_sh = a->v_stride[2];
+    p.o_sb = a->o_stride[0], p.o_ss = a->o_stride[1], p.o_sh = a->o_stride[2];
+    p.lse_sb = a->lse_stride[0], p.lse_sh = a->lse_stride[1];
+    p.batch = a->batch;
+    p.s_q = a->seqlen_q;
+    p.s_k = a->seqlen_k;
+    p.h_q = a->heads_q;
+    p.h_kv = a->heads_kv;
+    p.group = pl.group;
+    p.scale_log2 = pl.scale_log2;
+    p.v_descale = pl.v_descale;
+    p.wl = pl.wl;
+    p.wr = pl.wr;
+    hipError_t e = launch_fwd_fp8(p, pl.head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("fp8 forward launch: ") + hipGetErrorString(e));
+    return EXATTN_OK;
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
 exattn_status exattn_bwd_plan(const exattn_bwd_args* a, size_t* workspace_bytes_out) {
   try {
     clear_error();
@@ -341,6 +377,7 @@ size_t exattn_args_size(int32_t which) {
          : which == 2 ? sizeof(exattn_kv_new)
          : which == 3 ? sizeof(exattn_paged_kv)
          : which == 4 ? sizeof(exattn_bwd_args)
+         : which == 5 ? sizeof(exattn_fp8_descale)
                       : 0;
 }
 

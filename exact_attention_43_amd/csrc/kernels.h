@@ -68,6 +68,27 @@ struct DecParams {
   int64_t k_sp, v_sp;
 };
 
+// FP8 forward (dense layouts): Q, K, V as E4M3 codes (strides in elements =
+// bytes), O bf16, LSE fp32 (b, h_q, s_q) or null.  scale_log2 folds the softmax
+// scale, both Q and K descales and log2 e; v_descale multiplies O.
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh;
+  int batch, s_q, s_k, h_q, h_kv, group;
+  float scale_log2, v_descale;
+  int wl, wr;  // window edges, -1 = unbounded (wr = 0 for causal)
+};
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int head_dim, hipStream_t stream);
+
 // Backward (dense layouts): dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
 struct BwdParams {
   const uint16_t* q;

@@ -133,6 +133,57 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   return EXATTN_OK;
 }
 
+exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d, Fp8Plan* pl) {
+  if (a == nullptr || pl == nullptr) return fail(EXATTN_E_INVALID, "args is NULL");
+  *pl = Fp8Plan{};
+  if (a->dtype != EXATTN_FP8_E4M3)
+    return fail(EXATTN_E_UNSUPPORTED, "exattn_fwd_fp8 takes dtype EXATTN_FP8_E4M3, got " + str(a->dtype));
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(EXATTN_E_UNSUPPORTED, "the FP8 forward provides head_dim 64 and 128");
+  if (a->batch < 0) return fail(EXATTN_E_INVALID, "batch is negative");
+  if (a->heads_q < 1 || a->heads_kv < 1) return fail(EXATTN_E_INVALID, "heads must be >= 1");
+  if (a->heads_q % a->heads_kv != 0) return fail(EXATTN_E_INVALID, "heads_q is not a multiple of heads_kv");
+  if (a->cu_seqlens_q != nullptr || a->cu_seqlens_k != nullptr)
+    return fail(EXATTN_E_UNSUPPORTED, "the FP8 forward provides fixed lengths only");
+  if (a->seqlen_q < 0 || a->seqlen_k < 0) return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k is negative");
+  float scale_log2, cap_in, cap_out;
+  bool cap;
+  exattn_status st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &scale_log2, &cap_in, &cap_out, &cap);
+  if (st != EXATTN_OK) return st;
+  if (cap) return fail(EXATTN_E_UNSUPPORTED, "the FP8 forward does not provide softcap");
+  float dq = 1.f, dk = 1.f, dv = 1.f;
+  if (d != nullptr) dq = d->q, dk = d->k, dv = d->v;
+  if (!isfinite(dq) || !isfinite(dk) || !isfinite(dv))
+    return fail(EXATTN_E_INVALID, "descale factors must be finite");
+  pl->scale_log2 = scale_log2 * dq * dk;
+  if (!isfinite(pl->scale_log2)) return fail(EXATTN_E_INVALID, "softmax_scale x descales overflows");
+  pl->v_descale = dv;
+  pl->head_dim = a->head_dim;
+  pl->group = a->heads_q / a->heads_kv;
+  pl->wl = a->window_left < 0 ? -1 : a->window_left;
+  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  pl->empty = a->batch == 0 || a->seqlen_q == 0;
+  if (pl->empty) return EXATTN_OK;
+  if (a->q == nullptr || a->o == nullptr) return fail(EXATTN_E_INVALID, "q or o is NULL");
+  if (a->seqlen_k > 0 && (a->k == nullptr || a->v == nullptr)) return fail(EXATTN_E_INVALID, "k or v is NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(EXATTN_E_INVALID, "q, k, v and o must be 16-byte aligned");
+  const int64_t* s8[3] = {a->q_stride, a->k_stride, a->v_stride};
+  for (int t = 0; t < 3; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (s8[t][i] < 0 || s8[t][i] % 16 != 0)
+        return fail(EXATTN_E_INVALID, "FP8 q, k, v strides must be non-negative multiples of 16 elements");
+  for (int i = 0; i < 3; ++i)
+    if (!stride_ok(a->o_stride[i])) return fail(EXATTN_E_INVALID, "o strides must be non-negative multiples of 8");
+  if (a->lse != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
+    if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides must be non-negative");
+  }
+  const int64_t grid = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64);
+  if (grid > 0x7fffffffLL) return fail(EXATTN_E_INVALID, "problem too large for one launch");
+  return EXATTN_OK;
+}
+
 int decode_heads_per_group(int head_dim, int heads_kv) {
   int hpw = head_dim <= 64 ? 16 : head_dim <= 128 ? 8 : 4;
   while (hpw > 1 && hpw > heads_kv) hpw >>= 1;

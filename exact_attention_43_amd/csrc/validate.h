@@ -61,6 +61,14 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
 // (which plan_decode has accepted).
 exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n);
 
+// Checked FP8 forward arguments, resolved for the launch.
+struct Fp8Plan {
+  bool empty = false;
+  int head_dim = 0, group = 1, wl = -1, wr = -1;
+  float scale_log2 = 0.f, v_descale = 1.f;
+};
+exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d, Fp8Plan* pl);
+
 // Checked backward arguments, resolved for the launch.
 struct BwdPlan {
   bool bf16 = false;

@@ -59,7 +59,7 @@ typedef enum {
 
 /* Storage type of Q, K, V and O.  fp16/bf16 only ("FlashAttention完整说明",
  * section 八: half-precision types only).  Accumulation is fp32. */
-typedef enum { EXATTN_F16 = 0, EXATTN_BF16 = 1 } exattn_dtype;
+typedef enum { EXATTN_F16 = 0, EXATTN_BF16 = 1, EXATTN_FP8_E4M3 = 2 } exattn_dtype;
 
 /*
  * Prefill / general forward: flash_attn_func and its packed and varlen forms
@@ -254,6 +254,26 @@ exattn_status exattn_bwd_plan(const exattn_bwd_args *args, size_t *workspace_byt
 exattn_status exattn_bwd(const exattn_bwd_args *args, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/*
+ * FP8 forward with a bf16 output (Inference Cookbook FAQ Q20: FP8 inside, BF16
+ * out; FAQ Q10 gives FP8 a 1e-2 tolerance).  args as for exattn_fwd with
+ * dtype = EXATTN_FP8_E4M3: q, k, v hold OCP FP8 E4M3 codes (1 byte each; the
+ * strides count elements, which are bytes here), o is bf16 (b, s_q, h_q, d),
+ * lse as for exattn_fwd (or NULL).  The real inputs are code x descale, one
+ * fp32 factor per tensor; S = softmax_scale q_descale k_descale (Q K^T) runs
+ * on the FP8 MFMA, P V on the bf16 MFMA against V widened exactly from FP8,
+ * and O is multiplied by v_descale.  Provided: fixed lengths, head_dim 64 and
+ * 128, causal and window masks, GQA, no softcap (else EXATTN_E_UNSUPPORTED).
+ * Errors as for exattn_fwd; in addition q, k, v strides must be non-negative
+ * multiples of 16 elements, o strides multiples of 8, and descale NULL or its
+ * factors finite (EXATTN_E_INVALID).  descale NULL means all factors 1.
+ */
+typedef struct {
+  float q, k, v;
+} exattn_fp8_descale;
+
+exattn_status exattn_fwd_fp8(const exattn_fwd_args *args, const exattn_fp8_descale *descale, void *stream);
+
 /* The automatic split count, as a pure function (no device query).  One work
  * group covers up to 1024/head_dim adjacent KV heads (16 at d = 64, 8 at
  * d = 128, 4 at d = 256; a power of two no larger than heads_kv) and 16 of
@@ -265,7 +285,8 @@ int32_t exattn_decode_auto_splits(int32_t batch, int32_t heads_q, int32_t heads_
 
 /* sizeof(exattn_fwd_args) for which = 0, sizeof(exattn_decode_args) for which = 1,
  * sizeof(exattn_kv_new) for which = 2, sizeof(exattn_paged_kv) for which = 3,
- * sizeof(exattn_bwd_args) for which = 4, 0 otherwise: lets a binding check its
+ * sizeof(exattn_bwd_args) for which = 4, sizeof(exattn_fp8_descale) for which = 5,
+ * 0 otherwise: lets a binding check its
  * mirror of the structs. */
 size_t exattn_args_size(int32_t which);
 

@@ -300,6 +300,36 @@ def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=Fal
     return mq, mk, mv
 
 
+def decode_e4m3(codes):
+    """Real values of OCP FP8 E4M3 codes (the variant without infinities): sign
+    bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+    subnormal, (-1)^s 2^-6 m/8; S.1111.111 is NaN; the largest value is 448.
+    Accepts uint8 codes or a torch float8_e4m3fn tensor (its bytes)."""
+    x = codes
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().cpu().contiguous().view(torch.uint8).numpy()
+    c = np.asarray(x).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def attention_fp8(q, k, v, *, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_scale=None,
+                  causal=False, window_size=(-1, -1), rows=None, heads=None):
+    """The FP8 forward (FAQ Q20): Q, K, V are E4M3 codes whose real values are
+    code x descale (one factor per tensor); the result is exact attention of
+    those real values (default scale 1/sqrt(d)).  The output precision (bf16)
+    and the internal FP8 products are the kernel's business: the reference is
+    the definition in float64."""
+    return attention(decode_e4m3(q) * float(q_descale), decode_e4m3(k) * float(k_descale),
+                     decode_e4m3(v) * float(v_descale), softmax_scale=softmax_scale, causal=causal,
+                     window_size=window_size, rows=rows, heads=heads)
+
+
 def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new):
     """The cache update of flash_attn_with_kvcache(q, k_cache, v_cache, k=k_new,
     v=v_new, cache_seqlens=...) (FAQ Q17): token t of k_new / v_new

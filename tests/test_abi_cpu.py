@@ -42,6 +42,7 @@ def test_struct_layout_and_version(L):
     assert L.exattn_args_size(2) == C.sizeof(ex.KvNew)
     assert L.exattn_args_size(3) == C.sizeof(ex.PagedKv)
     assert L.exattn_args_size(4) == C.sizeof(ex.BwdArgs)
+    assert L.exattn_args_size(5) == C.sizeof(ex.Fp8Descale)
     assert L.exattn_args_size(7) == 0
     assert L.exattn_abi_version() == 1
     assert L.exattn_status_string(0) == b"EXATTN_OK"
@@ -234,6 +235,48 @@ def test_decode_workspace_checks(L):
     assert L.exattn_decode_plan(C.byref(a2), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
     assert ns.value == 4
     assert L.exattn_decode(C.byref(_dec(batch=0)), None, 0, None) == ex.EXATTN_OK
+
+
+def _f8(**kw):
+    a = _fwd(dtype=ex.EXATTN_FP8_E4M3)
+    for n in ("q_stride", "k_stride", "v_stride"):
+        getattr(a, n)[:] = [64 * 4 * 128, 4 * 128, 128]
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(a, key)[:] = val
+        else:
+            setattr(a, key, val)
+    return a
+
+
+BAD_FP8 = [
+    ("dtype bf16", dict(dtype=1), None, ex.EXATTN_E_UNSUPPORTED),
+    ("head_dim 256", dict(head_dim=256), None, ex.EXATTN_E_UNSUPPORTED),
+    ("softcap", dict(softcap=20.0), None, ex.EXATTN_E_UNSUPPORTED),
+    ("varlen", dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE), None, ex.EXATTN_E_UNSUPPORTED),
+    ("stride not 16", dict(k_stride=[64 * 4 * 128, 4 * 128 + 8, 128]), None, ex.EXATTN_E_INVALID),
+    ("odd o stride", dict(o_stride=[64 * 4 * 128, 4 * 128 + 4, 128]), None, ex.EXATTN_E_INVALID),
+    ("null q", dict(q=None), None, ex.EXATTN_E_INVALID),
+    ("misaligned v", dict(v=FAKE + 8), None, ex.EXATTN_E_INVALID),
+    ("heads ratio", dict(heads_q=3), None, ex.EXATTN_E_INVALID),
+    ("nan descale", dict(), (1.0, float("nan"), 1.0), ex.EXATTN_E_INVALID),
+    ("inf descale", dict(), (1.0, 1.0, float("inf")), ex.EXATTN_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,ds,status", BAD_FP8, ids=[c[0] for c in BAD_FP8])
+def test_fp8_rejects(L, name, kw, ds, status):
+    d = ex.Fp8Descale(*ds) if ds is not None else None
+    st = L.exattn_fwd_fp8(C.byref(_f8(**kw)), C.byref(d) if d is not None else None, None)
+    assert st == status, (name, st, L.exattn_last_error())
+    assert L.exattn_last_error()
+
+
+def test_fp8_empty_and_fwd_refuses_fp8(L):
+    assert L.exattn_fwd_fp8(C.byref(_f8(batch=0, q=None, o=None)), None, None) == ex.EXATTN_OK
+    assert L.exattn_fwd_fp8(C.byref(_f8(seqlen_q=0)), None, None) == ex.EXATTN_OK
+    assert L.exattn_fwd_fp8(None, None, None) == ex.EXATTN_E_INVALID
+    assert L.exattn_fwd(C.byref(_f8()), None) == ex.EXATTN_E_UNSUPPORTED  # the 16-bit path takes no FP8
 
 
 def _bwd(**kw):

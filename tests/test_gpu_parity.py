@@ -424,6 +424,66 @@ def test_backward_empty_side(s_q, s_k):
         assert torch.equal(t, torch.zeros_like(t))
 
 
+FP8_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, causal, window, (q, k, v descale), seed
+    (2, 200, 200, 4, 4, 128, True, (-1, -1), (0.5, 2.0, 1.5), 220),
+    (1, 130, 300, 8, 2, 64, False, (-1, -1), (1.0, 1.0, 1.0), 221),
+    (2, 257, 100, 4, 1, 128, True, (-1, -1), (1.0, 0.25, 4.0), 222),   # rows without keys
+    (1, 300, 300, 2, 2, 128, False, (50, 10), (2.0, 2.0, 0.5), 223),
+    (1, 1, 513, 4, 2, 64, True, (-1, -1), (1.0, 1.0, 1.0), 224),      # one row
+    (2, 1024, 1024, 16, 16, 128, True, (-1, -1), (1.0, 1.0, 1.0), 225),  # the causal prefill shape
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[f"f{c[-1]}" for c in FP8_CASES])
+def test_fp8_forward(case):
+    """The FP8 forward (bf16 out) against the oracle on the decoded inputs, FAQ Q10's FP8
+    tolerance (1e-2 / 1e-2) on O, 1e-4 on LSE; two runs bitwise equal."""
+    b, sq, sk, hq, hkv, d, causal, window, (dsq, dsk, dsv), seed = case
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=seed, dtype=torch.float8_e4m3fn)
+    gq, gk, gv = _dev(q, k, v)
+    out, lse = ex.attn_func_fp8(gq, gk, gv, q_descale=dsq, k_descale=dsk, v_descale=dsv, causal=causal,
+                                window_size=window)
+    out2, lse2 = ex.attn_func_fp8(gq, gk, gv, q_descale=dsq, k_descale=dsk, v_descale=dsv, causal=causal,
+                                  window_size=window)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    ro, rl = oracle.attention_fp8(q, k, v, q_descale=dsq, k_descale=dsk, v_descale=dsv, causal=causal,
+                                  window_size=window)
+    # FAQ Q10's FP8 tolerance is for values at the codes' own scale: O is compared after
+    # dividing by v_descale (the real V is code x v_descale, so P's rounding moves O by
+    # amounts proportional to it).
+    assert_o_close(out.float() / dsv, np.nan_to_num(ro) / dsv, "fp8", "fp8 O")
+    # LSE: the FP8 MFMA sums its 16 products with a shorter mantissa than fp32 (a probe
+    # of 16-term dot products measured errors near 2^-15 of the sum of |products|), and a
+    # score takes d / 16 such sums, so a score may move by about (d / 16) 2^-15 of
+    # scale * sum_i |q_i k_i|; the LSE moves by at most the largest such move.  Bound per
+    # row: 1e-4 + 2^-11 * scale_eff * max_j sum_i |q_i k_i| (d = 128 gives 2^-12 per
+    # sum, times 2 in reserve).
+    qa = np.abs(oracle.decode_e4m3(q))
+    ka = np.abs(oracle.decode_e4m3(k))
+    g = hq // hkv
+    mag = np.stack([np.stack([(qa[bi, :, h] @ ka[bi, :, h // g].T).max(axis=1) if sk else np.zeros(sq)
+                              for h in range(hq)]) for bi in range(b)])  # (b, h, s_q)
+    scale_eff = abs(dsq * dsk) / math.sqrt(d)
+    lg = lse.detach().cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl)), "fp8 LSE: -inf pattern differs"
+    fin = ~np.isneginf(rl)
+    bound = 1e-4 + 2.0 ** -11 * scale_eff * mag
+    err = np.abs(lg - rl)
+    assert not np.isnan(lg).any()
+    assert np.all(err[fin] <= bound[fin]), f"fp8 LSE: max err {err[fin].max():.3e}, worst err/bound {(err[fin] / bound[fin]).max():.3f}"
+
+
+def test_fp8_rejects_on_gpu():
+    q, k, v = _dev(*W.qkv(1, 64, 64, 2, 2, 128, seed=226, dtype=torch.float8_e4m3fn))
+    with pytest.raises(NotImplementedError):
+        ex.attn_func_fp8(q[..., :96].contiguous(), k[..., :96].contiguous(), v[..., :96].contiguous())
+    with pytest.raises(ValueError):
+        ex.attn_func_fp8(q.to(torch.bfloat16), k, v)
+
+
 # --------------------------------------------------------------------------
 # masks, tails and degenerate cases
 # --------------------------------------------------------------------------

@@ -529,6 +529,42 @@ def pin_backward_magnitudes():
     assert np.allclose(mv, wv, rtol=1e-12, atol=1e-14)
 
 
+def pin_fp8():
+    """The E4M3 decoding against torch's float8_e4m3fn conversion for all 256
+    codes and against values fixed by the format (1.0, the largest 448, the
+    smallest subnormal 2^-9, negative zero, NaN); attention_fp8 depends on the
+    Q and K descales only through their product (with the softmax scale), and
+    the V descale scales O and leaves LSE."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = OA.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)) and int(np.isnan(ours).sum()) == 2
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+    assert ours[0x80] == 0.0 and np.signbit(ours[0x80]) and ours[0xB8] == -1.0
+    # from a torch tensor: the same bytes
+    assert np.array_equal(OA.decode_e4m3(torch.from_numpy(codes).view(torch.float8_e4m3fn))[fin], ours[fin])
+    r = _rng(26)
+    q = torch.from_numpy(r.standard_normal((2, 9, 4, 16))).to(torch.float8_e4m3fn)
+    k = torch.from_numpy(r.standard_normal((2, 11, 2, 16))).to(torch.float8_e4m3fn)
+    v = torch.from_numpy(r.standard_normal((2, 11, 2, 16))).to(torch.float8_e4m3fn)
+    o1, l1 = oracle.attention_fp8(q, k, v, causal=True)
+    o2, l2 = oracle.attention_fp8(q, k, v, q_descale=4.0, k_descale=0.25, causal=True)
+    o3, l3 = oracle.attention_fp8(q, k, v, q_descale=2.0, causal=True, softmax_scale=0.125)
+    o4, l4 = oracle.attention_fp8(q, k, v, causal=True, softmax_scale=0.25)
+    o5, l5 = oracle.attention_fp8(q, k, v, v_descale=3.0, causal=True)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    assert np.allclose(o3, o4, atol=1e-12) and np.allclose(l3, l4, atol=1e-12)
+    assert np.allclose(o5, 3.0 * o1, atol=1e-12) and np.allclose(l5, l1, atol=1e-12)
+    # the real values are torch's decoding times the descales
+    o6, l6 = oracle.attention(q.to(torch.float64) * 2.0, k.to(torch.float64) * 0.5, v.to(torch.float64) * 3.0,
+                              causal=True)
+    o7, l7 = oracle.attention_fp8(q, k, v, q_descale=2.0, k_descale=0.5, v_descale=3.0, causal=True)
+    assert np.allclose(o6, o7, atol=1e-12) and np.allclose(l6, l7, atol=1e-12)
+
+
 def pin_softcap():
     r = _rng(19)
     q = r.standard_normal((1, 6, 2, 16)) * 4
@@ -570,7 +606,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_backward, pin_backward_magnitudes, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_backward, pin_backward_magnitudes, pin_fp8, pin_softcap,
         pin_default_scale]
 
 
@@ -641,6 +677,13 @@ OA_visible = OA.visible
 OA_softmax = OA.softmax_rows
 OA_append = OA.kvcache_append
 
+def _bad_e4m3_bias(codes):
+    return ORIG_DECODE_E4M3(codes) * 0.5  # exponent bias 8 instead of 7
+
+
+ORIG_DECODE_E4M3 = OA.decode_e4m3
+
+
 MUTATIONS = [
     ("scores", _bad_scores_noscale),
     ("scores", _bad_scores_transposed),
@@ -654,6 +697,7 @@ MUTATIONS = [
     ("_kv_head", _bad_kv_head_modulo),
     ("kvcache_append", _bad_append_offset),
     ("paged_to_contiguous", _bad_paged_row),
+    ("decode_e4m3", _bad_e4m3_bias),
 ]
 
 
