@@ -8,7 +8,8 @@ The FLOP count is the pages' 4*b*h*s_q*s_k*d halved for causal (Inference
 Cookbook FAQ Q16).  The KV-cache decode workload (batch 8, 16384 cached
 tokens, 32 query / 8 KV heads, d 128, bf16, automatic num_splits) is timed in
 the same run and reported as HBM GB/s under "decode", and the backward of the
-prefill workload (dQ, dK, dV from O, LSE and dO) as TFLOPS under "backward".
+prefill workload (dQ, dK, dV from O, LSE and dO) as TFLOPS under "backward", and the
+FP8 forward (E4M3 inputs, bf16 output) of the same shape under "fp8".
 
 Prints one JSON line.  Options:
   --gpus N            only 1 is supported (the method runs on one GPU here)
@@ -16,7 +17,8 @@ Prints one JSON line.  Options:
   --no-cpu-baseline   skip the CPU oracle timing
   --no-decode         skip the decode measurement
   --no-backward       skip the backward measurement
-  --only {prefill,decode,backward,copy}  run one part only (for profiler runs)
+  --no-fp8            skip the FP8 forward measurement
+  --only {prefill,decode,backward,fp8,copy}  run one part only (for profiler runs)
 """
 import argparse
 import hashlib
@@ -29,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense FP8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd TFLOPS (% bf16 MFMA peak) at b2 s1024 h16 d128; decode HBM GB/s"
 PREFILL_SOURCES = ["exact_attention_43_amd/csrc/fwd_prefill.hip",
@@ -66,7 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None)
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "fp8", "copy"], default=None)
     return ap.parse_args()
 
 
@@ -313,6 +317,53 @@ def run_backward(ex, W, args):
     }
 
 
+def run_fp8(ex, W, args):
+    """The FP8 forward on the causal prefill shape: q, k, v (2, 1024, 16, 128) E4M3 codes of a
+    seeded N(0,1) draw, descales 1, bf16 output; one step is one exattn_fwd_fp8 call."""
+    import ctypes as C
+    import torch
+    w = W.WORKLOADS["causal_prefill"]
+    q, k, v = (t.cuda() for t in W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim,
+                                       seed=w.seed, dtype=torch.float8_e4m3fn))
+    out = torch.empty((w.batch, w.seqlen_q, w.heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
+    a = ex.FwdArgs()
+    a.dtype = ex.EXATTN_FP8_E4M3
+    a.batch, a.seqlen_q, a.seqlen_k = w.batch, w.seqlen_q, w.seqlen_k
+    a.heads_q, a.heads_kv, a.head_dim = w.heads_q, w.heads_kv, w.head_dim
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    a.q_stride[:] = list(q.stride()[:3])
+    a.k_stride[:] = list(k.stride()[:3])
+    a.v_stride[:] = list(v.stride()[:3])
+    a.o_stride[:] = list(out.stride()[:3])
+    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    a.causal = 1
+    a.window_left = a.window_right = -1
+    ds = ex.Fp8Descale(1.0, 1.0, 1.0)
+    L = ex.lib()
+    ref, dref = C.byref(a), C.byref(ds)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        rc = L.exattn_fwd_fp8(ref, dref, stream)
+        if rc != 0:
+            ex._raise_for(rc, "exattn_fwd_fp8")
+
+    steps = max(10, min(args.steps, 100))
+    t = time_steps(step, steps, max(2, args.warmup // 2))
+    fl = W.flops(w)
+    tflops = fl / (t["region"] * 1e-3) / 1e12
+    return {
+        "workload": "FP8 forward of the causal prefill shape: q, k, v (2, 1024, 16, 128) E4M3, descales 1, "
+                    "bf16 out",
+        "value": round(tflops, 3), "unit": "TFLOPS", "flops_per_call": fl,
+        "ms_per_call_avg": round(t["region"], 6), "ms_per_call_median": round(t["pair_median"], 6),
+        "ms_per_call_min": round(t["pair_min"], 6), "calls": steps,
+        "frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "note": "S on the FP8 MFMA, PV on the bf16 MFMA (P rounded to bf16)",
+    }
+
+
 def run_copy_calibration():
     """A plain device copy of known size, for scaling the HBM byte counters: 7 launches of a
     256 MiB fp32 multiply-by-one (each reads 256 MiB and writes 256 MiB)."""
@@ -349,6 +400,9 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps(run_backward(ex, W, args)))
+        return
+    if args.only == "fp8":
+        print(json.dumps(run_fp8(ex, W, args)))
         return
 
     w, fl, t = run_prefill(ex, W, args)
@@ -387,6 +441,8 @@ def main():
         rec["decode"] = run_decode(ex, W, args)
     if not args.no_backward:
         rec["backward"] = run_backward(ex, W, args)
+    if not args.no_fp8:
+        rec["fp8"] = run_fp8(ex, W, args)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, fl)
     print(json.dumps(rec))
