@@ -4,26 +4,31 @@
 //
 // Inputs Q, K, V are OCP FP8 E4M3 codes with one fp32 descale factor each:
 // the real value is code x descale.  S = scale q_descale k_descale (Q K^T) is
-// formed on the FP8 MFMA (v_mfma_f32_32x32x16_fp8_fp8: exact products, fp32
-// sums), the softmax runs in fp32 with a running max and sum as in the bf16
-// forward ("FlashAttention完整说明", section 二.1), and O = P V takes P rounded
-// to bf16 against V widened exactly from FP8 to bf16 in LDS (every E4M3 value
-// is a bf16 value).  Rounding P to E4M3 instead (3 mantissa bits) would move
-// rows that see few keys by several percent, beyond the tolerance.  O is
-// scaled by v_descale / l and written as bf16; LSE is the natural log of the
-// sum of exp over the row's final scores.
+// formed on the FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales:
+// exact products, sums a little shorter than fp32), the softmax runs in fp32
+// with a running max and sum as in the bf16 forward ("FlashAttention完整说明",
+// section 二.1), and O = P V takes P rounded to bf16 against V widened exactly
+// from FP8 to bf16 in registers (every E4M3 value is a bf16 value).  Rounding
+// P to E4M3 instead (3 mantissa bits) would move rows that see few keys by
+// several percent, beyond the tolerance.  O is scaled by v_descale / l and
+// written as bf16; LSE is the natural log of the sum of exp over the row's
+// final scores.
 //
 // Layout per work group: NW waves x 32 query rows of one query head; a wave's
 // lane owns one query row (S^T = K Q^T, Q^T the B operand from registers).
-// Key blocks of 64 rows stream by DMA into double-buffered LDS: K as FP8
-// (read as A operands), V as FP8 staging, widened by all waves into one bf16
-// tile that the PV products read transposed.
+// Key blocks of 64 rows stream by DMA into double-buffered LDS as FP8.  K is
+// read as A operands; V is read with the 8-bit transposing read, whose lane i
+// receives byte i % 8 of 8 rows (the rows of source lanes 2 e + i / 8 of its
+// 16-lane group), and widened to bf16 in registers as the PV A operand.
 #include "device_common.h"
 #include "kernels.h"
 #include "tiles.h"
 
 namespace exattn {
 namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kF8Keys = 64;  // keys per block
 
@@ -39,16 +44,17 @@ __device__ __forceinline__ int f8swz(int r) {
     return (r >> 2) & 3;
 }
 
-// bf16 V tile (rows of 2 D bytes), read only transposed by the PV products
-// (4 consecutive rows x 2-4 adjacent chunks per read):
-// chunk c of row r at c ^ vswz16(r), 4 consecutive rows differing in bits 2-3
-// (d = 128) or bit 2 within a parity (d = 64).
+// FP8 V tile (rows of D bytes), read by 8-bit transposing reads: the 32 lanes
+// served together read 8 consecutive rows x 2 adjacent 16-byte chunks (c, c+1,
+// c even).  Chunk c of row r sits at c ^ v8swz(r): rows of one parity (d = 128,
+// two rows per 256-byte bank row) or of one residue mod 4 (d = 64) differ in
+// bits 1-2 of the swizzle, so the 16 chunks land in 16 bank groups.
 template <int D>
-__device__ __forceinline__ int vswz16(int r) {
-  if constexpr (D == 64)
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+__device__ __forceinline__ int v8swz(int r) {
+  if constexpr (D == 128)
+    return 2 * ((r >> 1) & 3);
   else
-    return 4 * (r & 3) + ((r >> 2) & 3);
+    return 2 * ((r >> 2) & 1);
 }
 
 __device__ __forceinline__ bool f8_visible(int i, int j, int sk, int off, int wl, int wr) {
@@ -66,22 +72,26 @@ __device__ __forceinline__ uint32_t f8pair_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// 8 bytes of one 16-lane group's transposing read of the FP8 V tile (see the
+// file comment for which bytes each lane receives).
+__device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* p) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p)));
+}
+
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p) {
   constexpr int BN = kF8Keys;
   constexpr int NT2 = BN / 32;       // 32-key tiles per block
-  constexpr int KP = D / 32;         // pairs of 16-wide k-steps over head_dim
+  constexpr int KS = D / 64;         // 64-wide k-steps over head_dim (QK)
   constexpr int DT = D / 32;         // 32-wide head_dim tiles of O^T
   constexpr int F8TILE = BN * D;     // bytes of an FP8 K or V tile
-  constexpr int VTILE = BN * D * 2;  // bytes of the bf16 V tile
-  constexpr int STAGE = 2 * F8TILE;  // K and V (FP8)
+  constexpr int STAGE = 2 * F8TILE;  // K and V
   constexpr int SLICES = F8TILE / 1024;
   static_assert(SLICES % NW == 0, "DMA slices per wave");
   constexpr int ROWS_PER_KB = 1024 / D;
   constexpr int CH = D / 16;         // 16-byte chunks per FP8 row
-  static_assert((64 * NW) % BN == 0 && (D / ((64 * NW) / BN)) % 16 == 0, "widening split");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + VTILE];
-  uint8_t* const vb = smem + 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -109,19 +119,22 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
   const int n_lo = kmax >= kmin ? kmin / BN : 0;
   const int n_hi = kmax >= kmin ? kmax / BN + 1 : 0;
 
-  // ---- Q^T as B operand.  Head dims are taken in a fixed order shared with the
-  // K reads: k-step pair j, lane half H holds dims 32 j + 16 H .. + 15, its
-  // first 8 bytes k-step 2 j and its last 8 bytes k-step 2 j + 1.
-  u32x4_t qf[KP];
+  // ---- Q^T as B operand of the 64-wide k-steps: lane half H of step s holds head
+  // dims 64 s + 32 H .. + 31 (32 bytes); K's A operands use the same assignment,
+  // so every dim meets itself.
+  i32x8_t qf[KS];
   {
     const bool in = qrow < sq;
-    const uint8_t* qp = p.q + (int64_t)b * p.q_sb + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 16 * hsel;
+    const uint8_t* qp = p.q + (int64_t)b * p.q_sb + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 32 * hsel;
 #pragma unroll
-    for (int j = 0; j < KP; ++j) qf[j] = in ? *(const u32x4_t*)(qp + 32 * j) : u32x4_t{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t lo = in ? *(const u32x4_t*)(qp + 64 * ks) : u32x4_t{0, 0, 0, 0};
+      const u32x4_t hi = in ? *(const u32x4_t*)(qp + 64 * ks + 16) : u32x4_t{0, 0, 0, 0};
+      qf[ks] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
   }
 
-  // ---- DMA of the FP8 K and V tiles: tile row r, chunk c at r * D + 16 * (c ^ f8swz(r)) for K,
-  // plain for V.
+  // ---- DMA of the FP8 K and V tiles: row r, chunk c at r * D + 16 * (c ^ swz(r)).
   const uint8_t* kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
   const uint8_t* vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
   uint32_t kofs[SLICES / NW], vofs[SLICES / NW];
@@ -129,7 +142,7 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
   for (int i = 0; i < SLICES / NW; ++i) {
     const int row = (NW * i + wave) * ROWS_PER_KB + lane / CH;
     kofs[i] = (uint32_t)(row * p.k_ss + 16 * ((lane % CH) ^ f8swz<D>(row)));
-    vofs[i] = (uint32_t)(row * p.v_ss + 16 * (lane % CH));
+    vofs[i] = (uint32_t)(row * p.v_ss + 16 * ((lane % CH) ^ v8swz<D>(row)));
   }
   auto issue = [&](int n, uint8_t* dst) {
     const int kb = n * BN;
@@ -144,65 +157,53 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
     }
   };
 
-  // ---- LDS addresses.  K A operand: tile t2 row m = l32 is key 32 t2 + row_key(l32),
-  // k-step pair j at chunk 2 j + H.
+  // ---- LDS addresses.  K A operand of tile t2, step s: row m = l32 is key
+  // 32 t2 + row_key(l32), bytes 64 s + 32 H .. + 31 = chunks 4 s + 2 H, + 1.
   const int krow = row_key(l32);
-  int kaddr[KP];
+  int kaddr[KS][2];
 #pragma unroll
-  for (int j = 0; j < KP; ++j) kaddr[j] = krow * D + 16 * ((2 * j + hsel) ^ f8swz<D>(krow));
-  // V^T operand of O^T += V^T P^T: rows = head dims, k = 8 consecutive keys per lane half.
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kaddr[ks][e] = krow * D + 16 * ((4 * ks + 2 * hsel + e) ^ f8swz<D>(krow));
+  // V^T operand of O^T += V^T P^T for dim tile dt and 16 keys: group g = lane / 16
+  // covers dims 32 dt + 16 (g & 1) .. + 15 and keys 8 (g >> 1) .. + 7; as a source
+  // lane, lane i of the group reads key 8 (g >> 1) + i / 2, dims + 8 (i & 1) .. + 7.
   const int gi = lane >> 4, li = lane & 15;
-  int tr[2][DT];
+  const int vrow = 8 * (gi >> 1) + (li >> 1);
+  int vaddr[DT];
 #pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int row = 8 * (gi >> 1) + 4 * half + (li >> 2);
-      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
-      tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ vswz16<D>(row)) + 2 * (dcol & 7);
-    }
-  // Widening: thread t takes V row t / TPR (TPR threads per row), bytes SEG * (t % TPR) .. + SEG - 1.
-  constexpr int TPR = 64 * NW / BN;           // threads per V row
-  constexpr int SEG = D / TPR;                // FP8 bytes per thread, a multiple of 16
-  const int wrow = tid / TPR, wseg = tid % TPR;
+  for (int dt = 0; dt < DT; ++dt)
+    vaddr[dt] = vrow * D + 16 * ((2 * dt + (gi & 1)) ^ v8swz<D>(vrow)) + 8 * (li & 1);
 
   float m = -__builtin_inff(), l = 0.f;  // running max (log2 domain) and sum
   f32x16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
 
-  auto block = [&](int n, const uint8_t* __restrict__ kt, const uint8_t* __restrict__ v8,
+  auto block = [&](int n, const uint8_t* __restrict__ kt, const uint8_t* __restrict__ vt,
                    uint8_t* __restrict__ nxt) {
-    // S^T = K Q^T on the FP8 MFMA
+    // S^T = K Q^T on the FP8 MFMA (unit block scales: E8M0 127)
     f32x16_t s[NT2];
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2) s[t2] = f32x16_t{};
 #pragma unroll
-    for (int j = 0; j < KP; ++j)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int t2 = 0; t2 < NT2; ++t2) {
-        const u32x4_t a = *(const u32x4_t*)(kt + kaddr[j] + t2 * 32 * D);
-        const long a0 = __builtin_bit_cast(long, u32x2_t{a[0], a[1]});
-        const long a1 = __builtin_bit_cast(long, u32x2_t{a[2], a[3]});
-        const long b0 = __builtin_bit_cast(long, u32x2_t{qf[j][0], qf[j][1]});
-        const long b1 = __builtin_bit_cast(long, u32x2_t{qf[j][2], qf[j][3]});
-        s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, s[t2], 0, 0, 0);
-        s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, s[t2], 0, 0, 0);
+        const u32x4_t lo = *(const u32x4_t*)(kt + kaddr[ks][0] + t2 * 32 * D);
+        const u32x4_t hi = *(const u32x4_t*)(kt + kaddr[ks][1] + t2 * 32 * D);
+        const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        s[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[t2], 0, 0, 0, 127, 0, 127);
       }
     if (n + 1 < n_hi) issue(n + 1, nxt);
-    // widen V: FP8 row-major staging -> bf16 tile
+    // the V reads do not depend on P: issue them all now, under the softmax
+    u32x2_t vw[NT2][2][DT];
 #pragma unroll
-    for (int c = 0; c < SEG / 16; ++c) {
-      const u32x4_t w = *(const u32x4_t*)(v8 + wrow * D + SEG * wseg + 16 * c);
-      u32x4_t lo, hi;
-      lo[0] = f8pair_bf16<false>(w[0]), lo[1] = f8pair_bf16<true>(w[0]);
-      lo[2] = f8pair_bf16<false>(w[1]), lo[3] = f8pair_bf16<true>(w[1]);
-      hi[0] = f8pair_bf16<false>(w[2]), hi[1] = f8pair_bf16<true>(w[2]);
-      hi[2] = f8pair_bf16<false>(w[3]), hi[3] = f8pair_bf16<true>(w[3]);
-      const int ch = (SEG * wseg + 16 * c) / 8;  // first bf16 chunk of these 16 values
-      *(u32x4_t*)(vb + wrow * (D * 2) + 16 * (ch ^ vswz16<D>(wrow))) = lo;
-      *(u32x4_t*)(vb + wrow * (D * 2) + 16 * ((ch + 1) ^ vswz16<D>(wrow))) = hi;
-    }
+    for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vw[t2][c][dt] = lds_read_tr8(vt + vaddr[dt] + (32 * t2 + 16 * c) * D);
     // scores in the log2 domain; register 8c + u of tile t2 is key n BN + 32 t2 + 16 c + 8 H + u
     const int kb0 = n * BN;
     const bool full = q0w + 32 <= sq && kb0 + BN <= sk && (p.wr < 0 || kb0 + BN - 1 <= q0w + off + p.wr) &&
@@ -241,20 +242,21 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
         for (int e = 0; e < 4; ++e) pb[t2][c][e] = Elem<true>::pack2(pv[2 * e], pv[2 * e + 1]);
       }
     l = l * alpha + halves_sum(rs);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // the running max grew for some row
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    __syncthreads();  // the bf16 V tile is complete
-    // O^T += V^T P^T
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    // O^T += V^T P^T, V^T widened from FP8 in registers
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int rows = (32 * t2 + 16 * c) * (D * 2);
-          const u32x2_t lo = lds_read_tr16(vb + tr[0][dt] + rows), hi = lds_read_tr16(vb + tr[1][dt] + rows);
+          const u32x2_t w = vw[t2][c][dt];
           u32x4_t a;
-          a[0] = lo[0], a[1] = lo[1], a[2] = hi[0], a[3] = hi[1];
+          a[0] = f8pair_bf16<false>(w[0]), a[1] = f8pair_bf16<true>(w[0]);
+          a[2] = f8pair_bf16<false>(w[1]), a[3] = f8pair_bf16<true>(w[1]);
           o[dt] = Elem<true>::mfma32x32x16(a, pb[t2][c], o[dt]);
         }
   };
