@@ -16,6 +16,8 @@
 //
 // Layout per work group: NW waves x 32 query rows of one query head; a wave's
 // lane owns one query row (S^T = K Q^T, Q^T the B operand from registers).
+// With NG = 2 a second group of NW waves takes every other key block of the
+// same rows, and the groups' (max, sum, O) merge through LDS at the end.
 // Key blocks of 64 rows stream by DMA into double-buffered LDS as FP8.  K is
 // read as A operands; V is read with the 8-bit transposing read, whose lane i
 // receives byte i % 8 of 8 rows (the rows of source lanes 2 e + i / 8 of its
@@ -79,8 +81,8 @@ __device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p)));
 }
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p) {
+template <int D, int NW, int NG>
+__global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Params p) {
   constexpr int BN = kF8Keys;
   constexpr int NT2 = BN / 32;       // 32-key tiles per block
   constexpr int KS = D / 64;         // 64-wide k-steps over head_dim (QK)
@@ -91,11 +93,13 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
   static_assert(SLICES % NW == 0, "DMA slices per wave");
   constexpr int ROWS_PER_KB = 1024 / D;
   constexpr int CH = D / 16;         // 16-byte chunks per FP8 row
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NG * 2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv / NW;   // key-block group: blocks n_lo + grp, + NG, ...
+  const int wave = wv % NW;  // row slice of the tile
   const int hsel = lane >> 5;
   const int l32 = lane & 31;
 
@@ -195,7 +199,7 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
         const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         s[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[t2], 0, 0, 0, 127, 0, 127);
       }
-    if (n + 1 < n_hi) issue(n + 1, nxt);
+    if (n + NG < n_hi) issue(n + NG, nxt);
     // the V reads do not depend on P: issue them all now, under the softmax
     u32x2_t vw[NT2][2][DT];
 #pragma unroll
@@ -261,18 +265,72 @@ __global__ void __launch_bounds__(64 * NW) fp8_prefill_kernel(const Fp8Params p)
         }
   };
 
-  uint8_t* const s0 = smem;
-  uint8_t* const s1 = smem + STAGE;
-  if (n_lo < n_hi) issue(n_lo, s0);
-  for (int n = n_lo; n < n_hi; n += 2) {
-    wait_vmem_all();
-    __syncthreads();
-    block(n, s0, s0 + F8TILE, s1);
-    if (n + 1 < n_hi) {
+  // Group grp takes blocks n_lo + grp, + NG, ...; both groups run the same number
+  // of iterations so that every wave meets every barrier.
+  uint8_t* const s0 = smem + grp * 2 * STAGE;
+  uint8_t* const s1 = s0 + STAGE;
+  if constexpr (NG == 1) {
+    if (n_lo < n_hi) issue(n_lo, s0);
+    for (int n = n_lo; n < n_hi; n += 2) {
       wait_vmem_all();
       __syncthreads();
-      block(n + 1, s1, s1 + F8TILE, s0);
+      block(n, s0, s0 + F8TILE, s1);
+      if (n + 1 < n_hi) {
+        wait_vmem_all();
+        __syncthreads();
+        block(n + 1, s1, s1 + F8TILE, s0);
+      }
     }
+  } else {
+    const int iters = (n_hi - n_lo + NG - 1) / NG;
+    const int nf = n_lo + grp;  // this group's first block
+    if (nf < n_hi) issue(nf, s0);
+    for (int t = 0; t < iters; t += 2) {
+      wait_vmem_all();
+      __syncthreads();
+      if (nf + NG * t < n_hi) block(nf + NG * t, s0, s0 + F8TILE, s1);
+      if (t + 1 < iters) {
+        wait_vmem_all();
+        __syncthreads();
+        if (nf + NG * (t + 1) < n_hi) block(nf + NG * (t + 1), s1, s1 + F8TILE, s0);
+      }
+    }
+  }
+
+  // ---- merge the groups: group g > 0 hands (m, l, O^T) to group 0 through LDS
+  // (the stages are free once every wave has passed this barrier).
+  if constexpr (NG > 1) {
+    static_assert(NG == 2, "two groups");
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(smem);                       // [wave][dt][4][lane][4]
+    float* xm = reinterpret_cast<float*>(smem) + NW * DT * 16 * 64;   // [wave][lane] m, then l
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t w = {o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
+          *(f32x4_t*)(xo + (((wave * DT + dt) * 4 + j) * 64 + lane) * 4) = w;
+        }
+      xm[wave * 64 + lane] = m;
+      xm[NW * 64 + wave * 64 + lane] = l;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    const float m1 = xm[wave * 64 + lane], l1 = xm[NW * 64 + wave * 64 + lane];
+    const float mt = fmaxf(m, m1);
+    const float mu = mt == -__builtin_inff() ? 0.f : mt;
+    const float a0 = fast_exp2(m - mu), a1 = fast_exp2(m1 - mu);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t w = *(const f32x4_t*)(xo + (((wave * DT + dt) * 4 + j) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[dt][4 * j + e] = o[dt][4 * j + e] * a0 + w[e] * a1;
+      }
+    l = l * a0 + l1 * a1;
+    m = mt;
   }
 
   // ---- O = (O^T)^T v_descale / l as bf16; lane holds head dims 32 dt + 8 J + 4 H + 0..3 of row qrow.
@@ -299,7 +357,15 @@ hipError_t launch_fp8_t(const Fp8Params& p, hipStream_t stream) {
   constexpr int NW = 2;
   const int n_qt = (p.s_q + 32 * NW - 1) / (32 * NW);
   if (n_qt == 0 || p.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL((fp8_prefill_kernel<D, NW>), dim3(n_qt * p.h_q * p.batch), dim3(64 * NW), 0, stream, p);
+  const int64_t grid = (int64_t)n_qt * p.h_q * p.batch;
+  // Fewer than 1024 tiles leave under two waves per SIMD on 256 CUs: split each
+  // tile's keys across two wave groups then (measured 21.9 us against 27.9 at the
+  // causal b2 s1024 h16 d128 shape); with more tiles the split only adds the merge
+  // (1114 us against 1032 at s16384).
+  if (grid < 1024)
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 2>), dim3((unsigned)grid), dim3(64 * NW * 2), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 1>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
