@@ -432,6 +432,9 @@ FP8_CASES = [
     (1, 300, 300, 2, 2, 128, False, (50, 10), (2.0, 2.0, 0.5), 223),
     (1, 1, 513, 4, 2, 64, True, (-1, -1), (1.0, 1.0, 1.0), 224),      # one row
     (2, 1024, 1024, 16, 16, 128, True, (-1, -1), (1.0, 1.0, 1.0), 225),  # the causal prefill shape
+    # 1024 tiles and more take the kernel without the key split
+    (1, 2048, 2048, 32, 8, 128, True, (-1, -1), (0.5, 1.0, 2.0), 227),
+    (1, 2048, 1500, 32, 32, 64, False, (300, 40), (1.0, 1.0, 1.0), 228),
 ]
 
 
