@@ -16,10 +16,11 @@
 //   permutation that makes 8 consecutive accumulator registers 8 consecutive
 //   queries), then dV^T += dO^T P and dK^T += Q^T dS with P and dS rounded in
 //   place as the B operand and dO^T / Q^T read transposed from LDS;
-// - bwd_dq_kernel: a work group owns 64 query rows (32 per wave) of one query
+// - bwd_dq_kernel: a group of 2 waves owns 64 query rows (32 per wave) of one query
 //   head and walks its KV blocks (64 keys) like the forward: S^T = K Q^T and
 //   dP^T = V dO^T with Q^T and dO^T in registers, dS^T rounded in place as the
-//   B operand of dQ^T += K^T dS^T, K^T read transposed from LDS.
+//   B operand of dQ^T += K^T dS^T, K^T read transposed from LDS; for small grids
+//   two groups split the blocks (32 keys each) and add their partial dQ in LDS.
 // The row statistics make P exact without a running max: LSE is final.
 #include "device_common.h"
 #include "kernels.h"
@@ -32,7 +33,10 @@ constexpr int kBwdRows = 32;   // query rows per block of the dK/dV kernel
 constexpr int kBwdKeys = 128;  // keys per work group of the dK/dV kernel
 constexpr int kDqWaves = 2;    // waves (32 query rows each) per work group of the dQ kernel
 constexpr int kDqRows = 32 * kDqWaves;
-constexpr int kDqKeys = 64;    // keys per block of the dQ kernel
+// keys per block of the dQ kernel: 64, or 32 when two wave groups split the keys
+// (their four K/V stages then fit 64 KiB of LDS, two work groups per CU)
+template <int NG>
+constexpr int dq_keys() { return NG == 1 ? 64 : 32; }
 
 // Is key j visible from query row i (bottom-right offset off = s_k - s_q)?
 __device__ __forceinline__ bool visible_key(int i, int j, int sq, int sk, int off, int wl, int wr) {
@@ -300,10 +304,10 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
 
 // dQ for 64 query rows of one query head (2 waves x 32 rows; two work groups
 // share a CU, which measured 3% faster than one of 4 waves).
-template <bool BF16, int D>
-__global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_kernel(const BwdParams p) {
+template <bool BF16, int D, int NG>
+__global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdParams p) {
   using E = Elem<BF16>;
-  constexpr int BN = kDqKeys;
+  constexpr int BN = dq_keys<NG>();
   constexpr int NT2 = BN / 32;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
@@ -313,11 +317,13 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_kernel(const BwdParams p
   constexpr int NW = kDqWaves;
   constexpr int KINST = KTILE / (1024 * NW);  // DMA instructions per wave per tile
   static_assert(KINST >= 1, "tile / wave mismatch");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * KTILE];  // K, V double-buffered
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NG * 4 * KTILE];  // per group: K, V double-buffered
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv / NW;   // key-block group: blocks n_lo + grp, + NG, ...
+  const int wave = wv % NW;  // row slice of the tile
   const int hsel = lane >> 5;
   const int l32 = lane & 31;
 
@@ -448,25 +454,66 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_kernel(const BwdParams p
         }
   };
 
-  uint8_t* const k0s = smem;
-  uint8_t* const k1s = smem + KTILE;
-  uint8_t* const v0s = smem + 2 * KTILE;
-  uint8_t* const v1s = smem + 3 * KTILE;
+  uint8_t* const k0s = smem + grp * 4 * KTILE;
+  uint8_t* const k1s = k0s + KTILE;
+  uint8_t* const v0s = k0s + 2 * KTILE;
+  uint8_t* const v1s = k0s + 3 * KTILE;
   auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                   uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
-    if (n + 1 < n_hi) issue(n + 1, kn, vn);
+    if (n + NG < n_hi) issue(n + NG, kn, vn);
     block(n, kc, vc);
   };
-  if (n_lo < n_hi) issue(n_lo, k0s, v0s);
-  for (int n = n_lo; n < n_hi; n += 2) {
-    wait_vmem_all();
-    __syncthreads();
-    step(k0s, v0s, k1s, v1s, n);
-    if (n + 1 < n_hi) {
+  if constexpr (NG == 1) {
+    if (n_lo < n_hi) issue(n_lo, k0s, v0s);
+    for (int n = n_lo; n < n_hi; n += 2) {
       wait_vmem_all();
       __syncthreads();
-      step(k1s, v1s, k0s, v0s, n + 1);
+      step(k0s, v0s, k1s, v1s, n);
+      if (n + 1 < n_hi) {
+        wait_vmem_all();
+        __syncthreads();
+        step(k1s, v1s, k0s, v0s, n + 1);
+      }
     }
+  } else {
+    // both groups run the same number of iterations so that every wave meets every barrier
+    const int iters = (n_hi - n_lo + NG - 1) / NG;
+    const int nf = n_lo + grp;
+    if (nf < n_hi) issue(nf, k0s, v0s);
+    for (int t = 0; t < iters; t += 2) {
+      wait_vmem_all();
+      __syncthreads();
+      if (nf + NG * t < n_hi) step(k0s, v0s, k1s, v1s, nf + NG * t);
+      if (t + 1 < iters) {
+        wait_vmem_all();
+        __syncthreads();
+        if (nf + NG * (t + 1) < n_hi) step(k1s, v1s, k0s, v0s, nf + NG * (t + 1));
+      }
+    }
+    // group 1 hands its partial dQ^T to group 0 through LDS (the stages are free
+    // once every wave has passed the barrier)
+    static_assert(NG == 2, "two groups");
+    __syncthreads();
+    float* xq = reinterpret_cast<float*>(smem);  // [wave][dt][4][lane][4]
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t w = {dq[dt][4 * j], dq[dt][4 * j + 1], dq[dt][4 * j + 2], dq[dt][4 * j + 3]};
+          *(f32x4_t*)(xq + (((wave * DT + dt) * 4 + j) * 64 + lane) * 4) = w;
+        }
+    }
+    __syncthreads();
+    if (grp != 0) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t w = *(const f32x4_t*)(xq + (((wave * DT + dt) * 4 + j) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dq[dt][4 * j + e] += w[e];
+      }
   }
 
   // ---- dQ = scale (dQ^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3 of row qrow.
@@ -507,7 +554,13 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   const int n_qt = (p.s_q + kDqRows - 1) / kDqRows;
   if (n_qt > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(n_qt * p.h_q * p.batch), dim3(64 * kDqWaves), 0, stream, p);
+    const int grid = n_qt * p.h_q * p.batch;
+    // Fewer than 1024 tiles leave under two waves per SIMD on 256 CUs: split each
+    // tile's key blocks between two wave groups then.
+    if (grid < 1024)
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2>), dim3(grid), dim3(64 * kDqWaves * 2), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
     e = hipGetLastError();
   }
   return e;

@@ -387,6 +387,9 @@ BWD_CASES = [
     (1, 1, 513, 4, 2, 128, torch.bfloat16, True, (-1, -1), 205),      # one row
     (1, 77, 40, 4, 2, 64, torch.float16, False, (5, -1), 206),        # left window only
     (2, 1024, 1024, 16, 16, 128, torch.bfloat16, True, (-1, -1), 207),  # the causal training shape
+    # 1024 query tiles and more: the dQ kernel without the key split
+    (1, 2048, 2048, 32, 8, 64, torch.bfloat16, True, (-1, -1), 209),
+    (1, 1024, 1024, 64, 16, 128, torch.float16, False, (-1, -1), 210),
 ]
 
 
