@@ -115,6 +115,12 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
                                           str(strides[t][i]) +
                                           " must be a non-negative multiple of 8 elements");
   }
+  // The kernels address 64 rows of a tile with 32-bit byte offsets from the
+  // tile's first row (DMA offsets, buffer descriptor ranges).
+  for (int t = 0; t < 3; ++t)
+    if (strides[t][1] >= ((int64_t)1 << 24))
+      return fail(EXATTN_E_UNSUPPORTED, std::string(names[t]) + "_stride[1] = " + str(strides[t][1]) +
+                                            " exceeds the supported token stride (2^24 elements)");
   if (a->lse != nullptr) {
     if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0)
       return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");

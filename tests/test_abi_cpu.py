@@ -82,6 +82,8 @@ BAD_FWD = [
     ("misaligned k", dict(k=FAKE + 8), ex.EXATTN_E_INVALID),
     ("odd stride", dict(q_stride=[64 * 4 * 128, 4 * 128 + 4, 128]), ex.EXATTN_E_INVALID),
     ("negative stride", dict(o_stride=[-8, 512, 128]), ex.EXATTN_E_INVALID),
+    ("token stride past 32-bit tile offsets", dict(k_stride=[1 << 30, 1 << 24, 128]),
+     ex.EXATTN_E_UNSUPPORTED),
     ("half varlen", dict(cu_seqlens_q=FAKE), ex.EXATTN_E_INVALID),
     ("inf scale", dict(softmax_scale=float("inf")), ex.EXATTN_E_INVALID),
     ("nan softcap", dict(softcap=float("nan")), ex.EXATTN_E_INVALID),
