@@ -41,9 +41,15 @@ struct DecCfg {
   static constexpr int NW = D == 256 ? 4 : 8;
 };
 
-// Stored position of 16-byte chunk c of K-tile row `key`: c ^ kswz(key).  The 8
-// lanes of one A-operand read phase read keys k0..k0+7 of one chunk column.
-__device__ __forceinline__ int kswz(int key) { return key & 7; }
+// Stored position of 16-byte chunk c of K-tile row `key`: c ^ kswz(key).  A
+// ds_read_b128 pass serves 16 lanes, here 16 consecutive keys of one chunk
+// column of one head; key rows are whole multiples of 256 bytes apart, so the
+// 16 stored chunks must be distinct modulo 16: key & 15 when a head's row has
+// 16 chunks or more (d >= 128; key & 7 left keys k and k + 8 in one bank group,
+// measured as 28% of the LDS busy cycles being bank conflicts).  At d = 64 a
+// head's row has 8 chunks and keeps key & 7.
+template <int D>
+__device__ __forceinline__ int kswz(int key) { return D >= 128 ? key & 15 : key & 7; }
 
 // Stored position of chunk c of V-tile row `key`: c ^ vswz(key).  A transposing
 // read takes 8 bytes from each of 4 consecutive keys x 2 chunks per 16 lanes;
@@ -133,7 +139,7 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     const int o = (wave + NW * t) * 1024 + 16 * lane;
     const int key = o / R, rem = o % R;
     const int head = rem / (2 * D), pos = (rem % (2 * D)) / 16;
-    kofs[t] = (uint32_t)((key * p.k_ss + head * p.k_sh) * 2 + 16 * (pos ^ kswz(key)));
+    kofs[t] = (uint32_t)((key * p.k_ss + head * p.k_sh) * 2 + 16 * (pos ^ kswz<D>(key)));
     vofs[t] = (uint32_t)((key * p.v_ss + head * p.v_sh) * 2 + 16 * (pos ^ vswz<D>(key)));
   }
   // Page of the cache row `key` (paged cache), clamped to the pool.  The table
@@ -226,7 +232,7 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
       f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t a = *(const u32x4_t*)(kt + kaddr0 + hoff + 16 * ((4 * ks + g16) ^ kswz(krow)));
+        const u32x4_t a = *(const u32x4_t*)(kt + kaddr0 + hoff + 16 * ((4 * ks + g16) ^ kswz<D>(krow)));
         s = E::mfma16x16x32(a, qf[i][ks], s);
       }
       // lane (query l16, group g16): scores of keys key0 + 4 g16 + r
