@@ -305,6 +305,12 @@ prefill_kernel(const FwdParams p) {
   auto k_operand = [&](const uint8_t* __restrict__ ks_, int ks, int t2) {
     return *(const u32x4_t*)(ks_ + kaddr[ks % NKA] + 32 * NKA * (ks / NKA) + t2 * 32 * (D * 2));
   };
+  // Eight K reads go out ahead of the MFMAs, then one more per MFMA (d >= 128).
+  // Left to itself the scheduler keeps two in flight and waits for each pair
+  // right before its MFMAs, which exposes the LDS latency in every k-step
+  // whenever a SIMD has no second wave to fill it (measured 2-3% faster at
+  // d = 128; at d = 64, with 8 reads per block, the default order measured
+  // 1.4% faster).
   auto qk = [&](const uint8_t* __restrict__ ks_, f32x16_t (&s)[NT2]) {
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2) s[t2] = f32x16_t{};
@@ -312,6 +318,15 @@ prefill_kernel(const FwdParams p) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int t2 = 0; t2 < NT2; ++t2) s[t2] = E::mfma32x32x16(k_operand(ks_, ks, t2), qf[ks], s[t2]);
+    if constexpr (D >= 128) {
+      constexpr int NQ = KS * NT2, PF = 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + PF < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
   };
   // scores outside the causal / window bounds or past the last key -> -inf
   // (only blocks that straddle a bound carry any)
