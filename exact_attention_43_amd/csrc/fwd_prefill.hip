@@ -369,27 +369,33 @@ prefill_kernel(const FwdParams p) {
     return exps(s, pf, m_ref == kNegInf ? 0.f : m_ref);
   };
   auto sum_too_big = [](float psum) { return __ballot(!(psum <= kSumCap)) != 0; };  // also inf, NaN
+  auto v_operand = [&](const uint8_t* __restrict__ vs_, int t2, int c, int dt) {
+    const int rows = (32 * t2 + 16 * c) * (D * 2);
+    const u32x2_t lo = lds_read_tr16(vs_ + vtr[0][dt] + rows);
+    const u32x2_t hi = lds_read_tr16(vs_ + vtr[1][dt] + rows);
+    u32x4_t a;
+    a[0] = lo[0];
+    a[1] = lo[1];
+    a[2] = hi[0];
+    a[3] = hi[1];
+    return a;
+  };
   auto pv = [&](const uint8_t* __restrict__ vs_, const u32x4_t (&pf)[NT2][2]) {
 #pragma unroll
     for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int rows = (32 * t2 + 16 * c) * (D * 2);
-          u32x4_t a;
-          const u32x2_t lo = lds_read_tr16(vs_ + vtr[0][dt] + rows);
-          const u32x2_t hi = lds_read_tr16(vs_ + vtr[1][dt] + rows);
-          a[0] = lo[0];
-          a[1] = lo[1];
-          a[2] = hi[0];
-          a[3] = hi[1];
-          oacc[dt] = E::mfma32x32x16(a, pf[t2][c], oacc[dt]);
-        }
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = E::mfma32x32x16(v_operand(vs_, t2, c, dt), pf[t2][c], oacc[dt]);
   };
-  // softmax of a block's scores s into pf, then O^T += V^T P^T
+  // softmax of a block's scores s into pf, then O^T += V^T P^T.  The V^T
+  // operands of the first key slice are read before the exponentials, so their
+  // LDS latency passes under the VALU work instead of ahead of the first MFMA.
   auto softmax_pv = [&](const uint8_t* __restrict__ vs_, const f32x16_t (&s)[NT2]) {
     u32x4_t pf[NT2][2];
+    u32x4_t vpre[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vpre[dt] = v_operand(vs_, 0, 0, dt);
     float psum = 0.f;
     bool ok = false;
     if (__ballot(m_ref == kNegInf) == 0) {  // some row without a reference: straight to the max
@@ -398,7 +404,14 @@ prefill_kernel(const FwdParams p) {
     }
     if (!ok) psum = slow(s, pf);
     l_run += psum;
-    pv(vs_, pf);
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          oacc[dt] = E::mfma32x32x16(t2 == 0 && c == 0 ? vpre[dt] : v_operand(vs_, t2, c, dt),
+                                     pf[t2][c], oacc[dt]);
   };
 
   uint8_t* const k0 = gsm;
@@ -531,18 +544,26 @@ prefill_kernel(const FwdParams p) {
     // restrict tells the compiler so, which lets the operand reads of this
     // step proceed while the DMA into the other stage is in flight (without
     // it every LDS read waits for all outstanding DMA).
+    // The next block's V DMA goes out after this block's score MFMAs are
+    // issued, K's at the start.  A wave stalls at issue while the CU's vector
+    // memory path drains the queue (about 20 cycles per 1 KiB instruction):
+    // all waves issuing both tiles at once after the barrier stalled each
+    // about 1100 cycles before its first K read (measured with cycle stamps at
+    // the causal b2 s1024 h16 d128 shape).
     auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                     uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
-      if (n + NG < n_hi) {
-        issue_k(n + NG, kn);
-        issue_v(n + NG, vn);
-      }
+      const bool more = n + NG < n_hi;
+      if (more) issue_k(n + NG, kn);
       if (n >= w_lo && n < w_hi) {  // uniform per wave
         f32x16_t s[NT2];
         qk(kc, s);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) issue_v(n + NG, vn);
         const int kb = n * BN;
         if (kb + BN - 1 > full_r || kb < full_l) mask_keys(s, mhi - kb, mlo - kb);
         softmax_pv(vc, s);
+      } else if (more) {
+        issue_v(n + NG, vn);
       }
     };
     if (n_lo + grp < n_hi) {
