@@ -664,9 +664,12 @@ prefill_kernel(const FwdParams p) {
       for (int dt = 0; dt < DT; ++dt) put(dt, inv);
     }
   }
+  __syncthreads();
+  // LSE after the barrier: the barrier's release fence waits for every
+  // outstanding store, so a store issued before it made all waves wait for a
+  // write round trip to memory.
   if (grp == 0 && my_valid && qrow < sq && hsel == 0 && lseg != nullptr)
     lseg[qrow] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
-  __syncthreads();
   // O tile -> global, 16 bytes per thread: rows 0-63 are tile_a, 64-127 tile_b
   constexpr int NTH = 256 * NG;
   static_assert(kBM * DCH % NTH == 0, "O tile copy");
