@@ -8,8 +8,10 @@ The FLOP count is the pages' 4*b*h*s_q*s_k*d halved for causal (Inference
 Cookbook FAQ Q16).  The KV-cache decode workload (batch 8, 16384 cached
 tokens, 32 query / 8 KV heads, d 128, bf16, automatic num_splits) is timed in
 the same run and reported as HBM GB/s under "decode", and the backward of the
-prefill workload (dQ, dK, dV from O, LSE and dO) as TFLOPS under "backward", and the
-FP8 forward (E4M3 inputs, bf16 output) of the same shape under "fp8".
+prefill workload (dQ, dK, dV from O, LSE and dO) as TFLOPS under "backward", the
+FP8 forward (E4M3 inputs, bf16 output) of the same shape under "fp8", and every
+other forward workload (tiny, the head-dim sweep, varlen + GQA + masks,
+cross-attention, the 16k-token causal prefill) at its own shape under "configs".
 
 Prints one JSON line.  Options:
   --gpus N            only 1 is supported (the method runs on one GPU here)
@@ -18,7 +20,8 @@ Prints one JSON line.  Options:
   --no-decode         skip the decode measurement
   --no-backward       skip the backward measurement
   --no-fp8            skip the FP8 forward measurement
-  --only {prefill,decode,backward,fp8,copy}  run one part only (for profiler runs)
+  --no-configs        skip the other forward workloads
+  --only {prefill,decode,backward,fp8,configs,copy}  run one part only (for profiler runs)
 """
 import argparse
 import hashlib
@@ -70,7 +73,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "fp8", "copy"], default=None)
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "fp8", "configs", "copy"], default=None)
     return ap.parse_args()
 
 
@@ -104,6 +108,88 @@ def prefill_step_fn(ex, qkv, out, lse, causal=True):
         if rc != 0:
             ex._raise_for(rc, "exattn_fwd")
     return step
+
+
+def fwd_step_fn(ex, q, k, v, out, lse, *, batch, s_q, s_k, q_st, k_st, v_st, o_st, lse_st, cu_q=None,
+                cu_k=None, max_q=0, max_k=0, causal=False, window=(-1, -1), softcap=0.0):
+    """exattn_fwd with its argument block built once; the closure only launches."""
+    import ctypes as C
+    import torch
+    a = ex.FwdArgs()
+    a.dtype = ex.EXATTN_BF16 if q.dtype == torch.bfloat16 else ex.EXATTN_F16
+    a.batch, a.seqlen_q, a.seqlen_k = batch, s_q, s_k
+    a.heads_q, a.heads_kv, a.head_dim = q.shape[-2], k.shape[-2], q.shape[-1]
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    for name, st in (("q_stride", q_st), ("k_stride", k_st), ("v_stride", v_st), ("o_stride", o_st)):
+        getattr(a, name)[:] = list(st)
+    a.lse_stride[:] = list(lse_st)
+    a.cu_seqlens_q = cu_q.data_ptr() if cu_q is not None else None
+    a.cu_seqlens_k = cu_k.data_ptr() if cu_k is not None else None
+    a.max_seqlen_q, a.max_seqlen_k = max_q, max_k
+    a.softmax_scale = 0.0
+    a.softcap = softcap
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = window
+    L = ex.lib()
+    ref = C.byref(a)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    keep = (a, q, k, v, out, lse, cu_q, cu_k)
+
+    def step():
+        rc = L.exattn_fwd(ref, stream)
+        if rc != 0:
+            ex._raise_for(rc, "exattn_fwd")
+    step.keep = keep
+    return step
+
+
+# The other forward workloads, each timed at its own shape (back-to-back launches,
+# inputs resident in HBM) against the bf16/fp16 MFMA peak.
+CONFIG_WORKLOADS = ["tiny", "hdim64", "hdim128", "hdim256", "varlen_gqa", "cross", "long_prefill"]
+
+
+def run_configs(ex, W, args):
+    import torch
+    res = {}
+    for name in CONFIG_WORKLOADS:
+        w = W.WORKLOADS[name]
+        dt = W.DTYPES[w.dtype]
+        if w.kind == "varlen":
+            q, k, v, cq, ck = W.varlen_qkv(w.seqlens, w.seqlens, w.heads_q, w.heads_kv, w.head_dim,
+                                           seed=w.seed, dtype=dt)
+            q, k, v, cq, ck = (t.cuda() for t in (q, k, v, cq, ck))
+            out = torch.empty_like(q)
+            lse = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device="cuda")
+            step = fwd_step_fn(ex, q, k, v, out, lse, batch=len(w.seqlens), s_q=0, s_k=0,
+                               q_st=(0, q.stride(0), q.stride(1)), k_st=(0, k.stride(0), k.stride(1)),
+                               v_st=(0, v.stride(0), v.stride(1)), o_st=(0, out.stride(0), out.stride(1)),
+                               lse_st=(0, lse.stride(0)), cu_q=cq, cu_k=ck, max_q=max(w.seqlens),
+                               max_k=max(w.seqlens), causal=w.causal, window=w.window, softcap=w.softcap)
+            desc = (f"varlen lengths {list(w.seqlens)}, h_q {w.heads_q} / h_kv {w.heads_kv}, d {w.head_dim}, "
+                    f"{w.dtype}, causal, window {tuple(w.window)}, softcap {w.softcap}")
+        else:
+            q, k, v = W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed,
+                            dtype=dt)
+            q, k, v = q.cuda(), k.cuda(), v.cuda()
+            out = torch.empty_like(q)
+            lse = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
+            step = fwd_step_fn(ex, q, k, v, out, lse, batch=w.batch, s_q=w.seqlen_q, s_k=w.seqlen_k,
+                               q_st=q.stride()[:3], k_st=k.stride()[:3], v_st=v.stride()[:3],
+                               o_st=out.stride()[:3], lse_st=(lse.stride(0), lse.stride(1)), causal=w.causal,
+                               window=w.window, softcap=w.softcap)
+            desc = (f"b {w.batch}, s_q {w.seqlen_q}, s_k {w.seqlen_k}, h_q {w.heads_q} / h_kv {w.heads_kv}, "
+                    f"d {w.head_dim}, {w.dtype}" + (", causal" if w.causal else ", non-causal"))
+        fl = W.flops(w)
+        reps = 10 if fl > 1e11 else 100
+        t = time_steps(step, reps, 5)
+        tf = fl / (t["region"] * 1e-3) / 1e12
+        res[name] = {"workload": desc, "us_per_call": round(t["region"] * 1e3, 2),
+                     "us_per_call_median": round(t["pair_median"] * 1e3, 2), "tflops": round(tf, 2),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl,
+                     "algorithmic_bytes": W.algorithmic_bytes(w), "calls": reps}
+        del step, q, k, v, out, lse
+        torch.cuda.empty_cache()
+    return res
 
 
 def time_steps(step, steps, warmup, between=None):
@@ -404,6 +490,9 @@ def main():
     if args.only == "fp8":
         print(json.dumps(run_fp8(ex, W, args)))
         return
+    if args.only == "configs":
+        print(json.dumps(run_configs(ex, W, args)))
+        return
 
     w, fl, t = run_prefill(ex, W, args)
     if args.only == "prefill":
@@ -443,6 +532,8 @@ def main():
         rec["backward"] = run_backward(ex, W, args)
     if not args.no_fp8:
         rec["fp8"] = run_fp8(ex, W, args)
+    if not args.no_configs:
+        rec["configs"] = run_configs(ex, W, args)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, fl)
     print(json.dumps(rec))
