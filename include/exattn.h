@@ -105,7 +105,10 @@ typedef struct {
 
 /* Run the forward.  head_dim must be 64, 128 or 256; heads_q % heads_kv == 0.
  * Sizes of 0 (batch, seqlen_q) launch nothing and return EXATTN_OK; seqlen_k
- * of 0 writes O = 0 and LSE = -inf. */
+ * of 0 writes O = 0 and LSE = -inf.  Strides must be non-negative multiples
+ * of 8 elements (EXATTN_E_INVALID); a token stride (index 1) of q, k or v of
+ * 2^24 elements or more returns EXATTN_E_UNSUPPORTED (the kernels address a
+ * 64-row tile with 32-bit byte offsets). */
 exattn_status exattn_fwd(const exattn_fwd_args *args, void *stream);
 
 /*
