@@ -78,7 +78,9 @@ __device__ __forceinline__ void mask_keys(f32x16_t (&s)[NT2], int hi, int lo) {
     }
 }
 
-template <bool BF16, int D, bool SOFTCAP, int NG>
+// PAIR: a two-group work group takes a light and a heavy 64-row tile (launch
+// shape chosen on the host); its own instances carry the idle-pair DMA.
+template <bool BF16, int D, bool SOFTCAP, int NG, bool PAIR>
 __global__ void __launch_bounds__(256 * NG)
 prefill_kernel(const FwdParams p) {
   using E = Elem<BF16>;
@@ -154,7 +156,8 @@ prefill_kernel(const FwdParams p) {
   // each tile; otherwise waves 0-1 of each group take the first tile.
   const int n64 = (sq + 63) / 64;
   if (2 * qt >= n64) return;  // uniform across the work group
-  const bool paired = NG > 1 && p.pair_tiles != 0;
+  static_assert(!PAIR || NG == 2, "pairing needs two groups");
+  constexpr bool paired = PAIR;
   const int tile_a = paired ? qt : 2 * qt;
   const int tile_b = paired ? n64 - 1 - qt : 2 * qt + 1;
   const bool b_valid = tile_b > tile_a && tile_b < n64;  // an odd tile count leaves one alone
@@ -263,6 +266,30 @@ prefill_kernel(const FwdParams p) {
     const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
 #pragma unroll
     for (int i = 0; i < KINST; ++i) buffer_load_lds16(rv, vdst + (4 * i + wg) * 1024, vofs_ld[i]);
+  };
+  // The partner wave's share (slices 4 i + (wg ^ 2): the other tile's wave of
+  // the group), issued together with this wave's own share in steps where
+  // only the partner has a block to compute.
+  uint32_t kofs_pt[KINST], vofs_pt[KINST];
+#pragma unroll
+  for (int i = 0; i < KINST; ++i) {
+    const int row = (4 * i + (wg ^ 2)) * ROWS_PER_KB + lane / DCH;
+    kofs_pt[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    vofs_pt[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ vswz<D>(row))) * 2u;
+  }
+  auto issue_kv_both = [&](int n, uint8_t* kdst, uint8_t* vdst) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
+#pragma unroll
+    for (int i = 0; i < KINST; ++i) {
+      buffer_load_lds16(rk, kdst + (4 * i + wg) * 1024, kofs_ld[i]);
+      buffer_load_lds16(rk, kdst + (4 * i + (wg ^ 2)) * 1024, kofs_pt[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < KINST; ++i) {
+      buffer_load_lds16(rv, vdst + (4 * i + wg) * 1024, vofs_ld[i]);
+      buffer_load_lds16(rv, vdst + (4 * i + (wg ^ 2)) * 1024, vofs_pt[i]);
+    }
   };
 
   f32x16_t oacc[DT];
@@ -544,25 +571,40 @@ prefill_kernel(const FwdParams p) {
     // restrict tells the compiler so, which lets the operand reads of this
     // step proceed while the DMA into the other stage is in flight (without
     // it every LDS read waits for all outstanding DMA).
-    // The next block's V DMA goes out after this block's score MFMAs are
-    // issued, K's at the start.  A wave stalls at issue while the CU's vector
-    // memory path drains the queue (about 20 cycles per 1 KiB instruction):
-    // all waves issuing both tiles at once after the barrier stalled each
-    // about 1100 cycles before its first K read (measured with cycle stamps at
-    // the causal b2 s1024 h16 d128 shape).
+    // Who issues the DMA of the group's next block.  A wave stalls at issue
+    // while the CU's vector memory path drains the queue (about 20 cycles per
+    // 1 KiB instruction): all waves issuing both tiles at once after the
+    // barrier stalled each about 1100 cycles before its first K read (measured
+    // with cycle stamps at the causal b2 s1024 h16 d128 shape).  So each wave
+    // issues its share of K at the start of the step and its share of V after
+    // its score MFMAs; and in a light + heavy pairing, in a step where only
+    // one tile's wave of a group pair has a block to compute, the idle wave
+    // issues both shares at the start and the busy one none (measured -4% at
+    // that shape, -6% at b1 s2048 causal; only paired instances carry this).
+    const bool o_valid = !my_a || b_valid;  // the partner's tile exists
+    const int o_lo = my_a ? b_lo : a_lo, o_hi = o_valid ? (my_a ? b_hi : a_hi) : 0;
     auto step = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                     uint8_t* __restrict__ kn, uint8_t* __restrict__ vn, int n) {
       const bool more = n + NG < n_hi;
-      if (more) issue_k(n + NG, kn);
+      const bool mine_ = n >= w_lo && n < w_hi;
+      // 0: own share (K now, V after the score MFMAs); 1: own and the partner's
+      // (this wave idle, the partner busy); 2: none (this wave busy, the partner idle)
+      int mode = 0;
+      if constexpr (PAIR && !SOFTCAP) {
+        const bool other = n >= o_lo && n < o_hi;
+        mode = mine_ == other ? 0 : (mine_ ? 2 : 1);
+      }
+      if (more && mode == 0) issue_k(n + NG, kn);
+      if (more && mode == 1) issue_kv_both(n + NG, kn, vn);
       if (n >= w_lo && n < w_hi) {  // uniform per wave
         f32x16_t s[NT2];
         qk(kc, s);
         __builtin_amdgcn_sched_barrier(0);
-        if (more) issue_v(n + NG, vn);
+        if (more && mode == 0) issue_v(n + NG, vn);
         const int kb = n * BN;
         if (kb + BN - 1 > full_r || kb < full_l) mask_keys(s, mhi - kb, mlo - kb);
         softmax_pv(vc, s);
-      } else if (more) {
+      } else if (more && mode == 0) {
         issue_v(n + NG, vn);
       }
     };
@@ -685,13 +727,24 @@ prefill_kernel(const FwdParams p) {
   }
 }
 
+template <bool BF16, int D, bool SOFTCAP, int NG>
+void launch_s(const FwdParams& p, int grid, hipStream_t stream) {
+  const dim3 block(256 * NG);
+  if constexpr (NG == 2) {
+    if (p.pair_tiles != 0) {
+      hipLaunchKernelGGL((prefill_kernel<BF16, D, SOFTCAP, 2, true>), dim3(grid), block, 0, stream, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((prefill_kernel<BF16, D, SOFTCAP, NG, false>), dim3(grid), block, 0, stream, p);
+}
+
 template <bool BF16, int D, int NG>
 hipError_t launch_g(const FwdParams& p, bool softcap, int grid, hipStream_t stream) {
-  const dim3 block(256 * NG);
   if (softcap)
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, true, NG>), dim3(grid), block, 0, stream, p);
+    launch_s<BF16, D, true, NG>(p, grid, stream);
   else
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, false, NG>), dim3(grid), block, 0, stream, p);
+    launch_s<BF16, D, false, NG>(p, grid, stream);
   return hipGetLastError();
 }
 
