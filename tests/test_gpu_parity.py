@@ -76,6 +76,21 @@ def test_causal_prefill_qkvpacked():
     assert_lse_close(lse, l_ref, "causal_prefill")
 
 
+# Paired launches (a light and a heavy 64-row tile per work group, one work
+# group per CU) under windows: the tiles' key ranges start above key 0, one
+# tile's waves idle while the other's compute, and the idle wave of a group
+# pair issues the next block's DMA for both.
+@pytest.mark.parametrize("causal,window,dtype", [
+    (False, (256, 0), torch.bfloat16),
+    (True, (100, -1), torch.float16),
+    (False, (128, 64), torch.bfloat16),
+    (True, (-1, -1), torch.float16),
+], ids=["w256_0", "causal_w100", "w128_64", "causal_f16"])
+def test_paired_launch_windows(causal, window, dtype):
+    q, k, v = W.qkv(2, 1024, 1024, 16, 16, 128, seed=107, dtype=dtype)
+    run_dense(q, k, v, f"paired causal={causal} window={window}", causal=causal, window_size=window)
+
+
 @pytest.mark.parametrize("name", ["hdim64", "hdim128", "hdim256"])
 def test_head_dim_sweep(name):
     w = W.WORKLOADS[name]
