@@ -15,6 +15,11 @@ a 256 MiB fp32 multiply-by-one, which reads and writes 256 MiB each)::
 
 writes ``NAME_traffic.json`` (read back by bench.py, and only trusted while the
 sha256 of the listed kernel sources still matches) and ``NAME_traffic.txt``.
+
+MFMA busy time and executed MFMA FLOPs from one counter pass
+(``--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16``)::
+
+    python -m exact_attention_43_amd.counters mfma DIR --kernel REGEX --flops F --out FILE.txt --cmd "..."
 """
 from __future__ import annotations
 
@@ -140,6 +145,49 @@ def cmd_traffic(a):
     print(text)
 
 
+def cmd_mfma(a):
+    """MFMA busy time per SIMD against the dispatch's duration, and MFMA FLOPs
+    executed against the workload's algorithmic FLOPs, from one counter pass
+    (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16; one MOP is 512
+    FLOPs).  The duration comes from the dispatch's own timestamps, which run
+    longer under counter collection than in a plain run; the clock is the
+    nominal peak clock, so the busy fraction is a lower bound."""
+    rx = re.compile(a.kernel)
+    per = {}
+    for r in _csvs(a.dir, "counter_collection.csv"):
+        if not rx.search(r["Kernel_Name"]):
+            continue
+        d = per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    names = {k[0] for k in per}
+    if len(names) != 1:
+        raise SystemExit(f"expected one kernel for {a.kernel!r}, found {len(names)}")
+    name = names.pop()
+    disp = list(per.values())
+    busy = statistics.median(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in disp) / a.simds
+    mops = statistics.median(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in disp)
+    ns = statistics.median(d["ns"] for d in disp)
+    frac = busy / (ns * a.clock_ghz)
+    lines = [
+        f"# MFMA counters per dispatch of {name[:100]}",
+        f"# command: {a.cmd}",
+        "",
+        f"dispatches: {len(disp)} (medians below)",
+        f"SQ_VALU_MFMA_BUSY_CYCLES per SIMD: {busy:.0f} cycles ({a.simds} SIMDs)",
+        f"dispatch duration under counter collection: {ns / 1e3:.2f} us",
+        f"MFMA busy fraction at the nominal {a.clock_ghz} GHz: {100 * frac:.1f}%",
+        f"MFMA FLOPs executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): {mops * 512:.4g}",
+    ]
+    if a.flops:
+        lines.append(f"algorithmic FLOPs: {a.flops:.4g}; executed / algorithmic = {mops * 512 / a.flops:.3f} "
+                     "(masked blocks on the mask boundary are computed whole)")
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -162,6 +210,15 @@ def main(argv=None):
     r.add_argument("--cmd", required=True)
     r.add_argument("--out-dir", default="profiles")
     r.set_defaults(fn=cmd_traffic)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--flops", type=float, default=0.0)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--clock-ghz", type=float, default=2.4)
+    m.add_argument("--out", required=True)
+    m.add_argument("--cmd", required=True)
+    m.set_defaults(fn=cmd_mfma)
     a = ap.parse_args(argv)
     a.fn(a)
 
