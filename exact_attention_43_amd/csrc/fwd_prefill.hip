@@ -668,11 +668,16 @@ prefill_kernel(const FwdParams p) {
       const int ex = rs * NG + grp, pe = rs * NG + (1 - h);
       xm[(ex * 2 + 0) * 64 + lane] = m_ref;
       xm[(ex * 2 + 1) * 64 + lane] = l_tot;
+      // four values per lane and access: [slot][d tile][r / 4][lane][r % 4]
+      f32x4_t* const xo4 = reinterpret_cast<f32x4_t*>(xo);
 #pragma unroll
       for (int j = 0; j < DTH; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          xo[((ex * DTH + j) * 16 + r) * 64 + lane] = oacc[(1 - h) * DTH + j][r];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16_t& src = oacc[(1 - h) * DTH + j];
+          xo4[((ex * DTH + j) * 4 + r4) * 64 + lane] =
+              f32x4_t{src[4 * r4], src[4 * r4 + 1], src[4 * r4 + 2], src[4 * r4 + 3]};
+        }
       __syncthreads();
       const float m1 = xm[(pe * 2 + 0) * 64 + lane];
       const float l1 = xm[(pe * 2 + 1) * 64 + lane];
@@ -683,9 +688,12 @@ prefill_kernel(const FwdParams p) {
 #pragma unroll
       for (int j = 0; j < DTH; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          oacc[h * DTH + j][r] =
-              oacc[h * DTH + j][r] * a0 + xo[((pe * DTH + j) * 16 + r) * 64 + lane] * a1;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t o1 = xo4[((pe * DTH + j) * 4 + r4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            oacc[h * DTH + j][4 * r4 + e] = oacc[h * DTH + j][4 * r4 + e] * a0 + o1[e] * a1;
+        }
       // the same terms in both groups, so both get the same l and m
       l_tot = l_tot * a0 + l1 * a1;
       m_ref = mm;
