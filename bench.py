@@ -95,7 +95,8 @@ def prefill_step_fn(ex, qkv, out, lse, causal=True):
         getattr(a, n)[:] = [st[0], st[1], st[3]]
     a.o_stride[:] = list(out.stride()[:3])
     a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
-    a.softmax_scale = 0.0
+    a.softmax_scale = float("nan")  # the default 1/sqrt(head_dim)
+    a.pack_gqa = -1
     a.softcap = 0.0
     a.causal = 1 if causal else 0
     a.window_left = a.window_right = -1
@@ -126,7 +127,8 @@ def fwd_step_fn(ex, q, k, v, out, lse, *, batch, s_q, s_k, q_st, k_st, v_st, o_s
     a.cu_seqlens_q = cu_q.data_ptr() if cu_q is not None else None
     a.cu_seqlens_k = cu_k.data_ptr() if cu_k is not None else None
     a.max_seqlen_q, a.max_seqlen_k = max_q, max_k
-    a.softmax_scale = 0.0
+    a.softmax_scale = float("nan")  # the default 1/sqrt(head_dim)
+    a.pack_gqa = -1
     a.softcap = softcap
     a.causal = 1 if causal else 0
     a.window_left, a.window_right = window
@@ -374,6 +376,7 @@ def run_backward(ex, W, args):
                     ("dv", dv)):
         getattr(a, f"{name}_stride")[:] = list(t.stride()[:3])
     a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    a.softmax_scale = float("nan")  # the default 1/sqrt(head_dim), as in the forward above
     a.causal = 1
     a.window_left = a.window_right = -1
     L = ex.lib()

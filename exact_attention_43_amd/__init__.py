@@ -53,6 +53,7 @@ class FwdArgs(C.Structure):
         ("max_seqlen_q", C.c_int32), ("max_seqlen_k", C.c_int32),
         ("softmax_scale", C.c_float), ("softcap", C.c_float),
         ("causal", C.c_int32), ("window_left", C.c_int32), ("window_right", C.c_int32),
+        ("pack_gqa", C.c_int32),
     ]
 
 
@@ -206,7 +207,35 @@ def _check_dropout(dropout_p):
 
 
 def _scale(softmax_scale):
-    return 0.0 if softmax_scale is None else float(softmax_scale)
+    """None selects the library default 1/sqrt(head_dim) (passed as NaN); any other value as given."""
+    return float("nan") if softmax_scale is None else float(softmax_scale)
+
+
+def _pack(pack_gqa):
+    """None: automatic (-1); True / False: on / off."""
+    if pack_gqa is None:
+        return -1
+    return 1 if pack_gqa else 0
+
+
+def _check_out(out, shape, dtype, what="out"):
+    """A caller-supplied output must match what the kernel writes: dtype, shape and a
+    contiguous last dimension."""
+    if out is None:
+        return
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{what} must be {dtype} of shape {tuple(shape)}, got {out.dtype} {tuple(out.shape)}")
+    if out.stride(-1) != 1:
+        raise ValueError(f"{what} must have a contiguous last dimension")
+
+
+def _check_lse(lse, shape, contiguous=False):
+    if lse is None:
+        return
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape):
+        raise ValueError(f"lse must be float32 of shape {tuple(shape)}, got {lse.dtype} {tuple(lse.shape)}")
+    if lse.stride(-1) != 1 or (contiguous and not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous" if contiguous else "lse must have a contiguous last dimension")
 
 
 def _window(window_size):
@@ -220,7 +249,7 @@ def _stream(dev):
 
 def _fwd_call(q, k, v, out, lse, *, batch, s_q, s_k, h_q, h_kv, d, q_st, k_st, v_st, o_st, lse_st,
               cu_q=None, cu_k=None, max_q=0, max_k=0, softmax_scale=None, causal=False,
-              window_size=(-1, -1), softcap=0.0):
+              window_size=(-1, -1), softcap=0.0, pack_gqa=None):
     a = FwdArgs()
     a.dtype = _dtype_code(q)
     a.batch, a.seqlen_q, a.seqlen_k = batch, s_q, s_k
@@ -237,17 +266,20 @@ def _fwd_call(q, k, v, out, lse, *, batch, s_q, s_k, h_q, h_kv, d, q_st, k_st, v
     a.softcap = float(softcap or 0.0)
     a.causal = 1 if causal else 0
     a.window_left, a.window_right = _window(window_size)
+    a.pack_gqa = _pack(pack_gqa)
     with torch.cuda.device(q.device):
         st = lib().exattn_fwd(C.byref(a), C.c_void_p(_stream(q.device)))
     _raise_for(st, "exattn_fwd")
 
 
 def attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
-              softcap=0.0, out=None, lse=None):
-    """Dense forward.  q (b, s_q, h_q, d); k, v (b, s_k, h_kv, d); returns (out, lse)."""
+              softcap=0.0, out=None, lse=None, pack_gqa=None):
+    """Dense forward.  q (b, s_q, h_q, d); k, v (b, s_k, h_kv, d); returns (out, lse).
+
+    ``pack_gqa`` (FAQ Q15): None = automatic, True = one tile holds the rows of all
+    query heads of a KV head, False = one tile per query head; the result is the same.
+    """
     _check_dropout(dropout_p)
-    _on_gpu(q, k, v, out, lse)
-    _check_last_dim(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (batch, seqlen, heads, head_dim)")
     b, s_q, h_q, d = q.shape
@@ -256,6 +288,10 @@ def attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_s
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
+    _check_out(out, (b, s_q, h_q, d), q.dtype)
+    _check_lse(lse, (b, h_q, s_q))
+    _on_gpu(q, k, v, out, lse)
+    _check_last_dim(q, k, v)
     if out is None:
         out = torch.empty((b, s_q, h_q, d), dtype=q.dtype, device=q.device)
     if lse is None:
@@ -263,7 +299,7 @@ def attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_s
     _fwd_call(q, k, v, out, lse, batch=b, s_q=s_q, s_k=s_k, h_q=h_q, h_kv=h_kv, d=d,
               q_st=q.stride()[:3], k_st=k.stride()[:3], v_st=v.stride()[:3], o_st=out.stride()[:3],
               lse_st=(lse.stride(0), lse.stride(1)), softmax_scale=softmax_scale, causal=causal,
-              window_size=window_size, softcap=softcap)
+              window_size=window_size, softcap=softcap, pack_gqa=pack_gqa)
     return out, lse
 
 
@@ -289,6 +325,7 @@ def attn_func_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_
     _check_last_dim(out)
     if lse is None:
         lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    _check_lse(lse, (b, h_q, s_q))
     a = FwdArgs()
     a.dtype = EXATTN_FP8_E4M3
     a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = b, s_q, s_k, h_q, h_kv, d
@@ -319,27 +356,33 @@ def attn_qkvpacked_func(qkv, dropout_p=0.0, softmax_scale=None, causal=False, wi
 
 
 def attn_kvpacked_func(q, kv, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
-                       softcap=0.0, out=None, lse=None):
+                       softcap=0.0, out=None, lse=None, pack_gqa=None):
     """kv (b, s_k, 2, h_kv, d) as stacked by torch.stack([k, v], dim=2) (FAQ Q7)."""
     if kv.dim() != 5 or kv.shape[2] != 2:
         raise ValueError("kv must be (batch, seqlen_k, 2, heads_kv, head_dim)")
     return attn_func(q, kv[:, :, 0], kv[:, :, 1], dropout_p, softmax_scale, causal, window_size,
-                     softcap, out, lse)
+                     softcap, out, lse, pack_gqa)
 
 
 def attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, dropout_p=0.0,
                      softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, out=None,
-                     lse=None):
+                     lse=None, pack_gqa=None):
     """Packed sequences (FAQ Q8): q (total_q, h_q, d), k/v (total_k, h_kv, d), int32 cu_seqlens.
 
     ``max_seqlen_q`` / ``max_seqlen_k`` are host ints bounding every sequence length.
     Returns out (total_q, h_q, d) and lse (h_q, total_q).
     """
     _check_dropout(dropout_p)
-    _on_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
-    _check_last_dim(q, k, v)
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("varlen q, k, v must be 3-D (total, heads, head_dim)")
+    if k.shape != v.shape or k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    _check_out(out, q.shape, q.dtype)
+    _check_lse(lse, (q.shape[1], q.shape[0]))
+    _on_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
+    _check_last_dim(q, k, v)
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
@@ -358,7 +401,7 @@ def attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seql
               v_st=(0, v.stride(0), v.stride(1)), o_st=(0, out.stride(0), out.stride(1)),
               lse_st=(0, lse.stride(0)), cu_q=cu_seqlens_q, cu_k=cu_seqlens_k, max_q=max_seqlen_q,
               max_k=max_seqlen_k, softmax_scale=softmax_scale, causal=causal, window_size=window_size,
-              softcap=softcap)
+              softcap=softcap, pack_gqa=pack_gqa)
     return out, lse
 
 
@@ -441,6 +484,8 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
         raise ValueError("k_cache and v_cache must be (batch, seqlen_cache, heads_kv, head_dim)")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share one dtype")
+    _check_out(out, q.shape, q.dtype)
+    _check_lse(lse, (q.shape[0], q.shape[2], 1), contiguous=True)  # the kernel writes lse[b * h_q + h]
     _on_gpu(q, k_cache, v_cache, out, lse, cache_seqlens if torch.is_tensor(cache_seqlens) else None,
             workspace, k, v, block_table)
     pg = None

@@ -37,14 +37,17 @@ exattn_status device_cus(int* out) {
   return EXATTN_OK;
 }
 
+// EXATTN_DEBUG, read once per process.
 int debug_level() {
-  const char* s = getenv("EXATTN_DEBUG");
-  return s ? atoi(s) : 0;
+  static const int level = [] {
+    const char* s = getenv("EXATTN_DEBUG");
+    return s ? atoi(s) : 0;
+  }();
+  return level;
 }
 
 // EXATTN_DEBUG=1: print the plan once per distinct launch shape.
 void debug_once(const std::string& key, const std::string& text) {
-  if (debug_level() < 1) return;
   static std::set<std::string> seen;
   std::lock_guard<std::mutex> lk(g_mu);
   if (seen.insert(key).second) fprintf(stderr, "[exattn] %s\n", text.c_str());
@@ -102,12 +105,16 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     p.wl = pl.wl;
     p.wr = pl.wr;
     p.q_sign = pl.q_sign;
-    char buf[256];
-    snprintf(buf, sizeof buf,
-             "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d groups=%d pair=%d",
-             pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, (int)pl.varlen, a->batch,
-             pl.s_q, pl.s_k, a->heads_q, a->heads_kv, pl.wl, pl.wr, pl.grid, groups, p.pair_tiles);
-    debug_once(buf, buf);
+    p.pack = pl.pack ? 1 : 0;
+    if (debug_level() >= 1) {
+      char buf[256];
+      snprintf(buf, sizeof buf,
+               "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d groups=%d "
+               "pair=%d pack=%d",
+               pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, (int)pl.varlen, a->batch, pl.s_q,
+               pl.s_k, a->heads_q, a->heads_kv, pl.wl, pl.wr, pl.grid, groups, p.pair_tiles, p.pack);
+      debug_once(buf, buf);
+    }
     hipError_t e = launch_prefill(p, pl.bf16, pl.head_dim, pl.softcap, pl.grid, groups,
                                   static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("prefill launch: ") + hipGetErrorString(e));
@@ -223,11 +230,13 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
     p.cap_in = pl.cap_in;
     p.cap_out_log2 = pl.cap_out_log2;
     p.wl = pl.wl;
-    char buf[256];
-    snprintf(buf, sizeof buf, "decode %s d=%d softcap=%d b=%d hq=%d hkv=%d cache=%d splits=%d wl=%d",
-             pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, a->batch, a->heads_q,
-             a->heads_kv, a->seqlen_cache, pl.n_split, pl.wl);
-    debug_once(buf, buf);
+    if (debug_level() >= 1) {
+      char buf[256];
+      snprintf(buf, sizeof buf, "decode %s d=%d softcap=%d b=%d hq=%d hkv=%d cache=%d splits=%d wl=%d",
+               pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, a->batch, a->heads_q,
+               a->heads_kv, a->seqlen_cache, pl.n_split, pl.wl);
+      debug_once(buf, buf);
+    }
     hipError_t e = launch_decode(p, pl.bf16, pl.head_dim, pl.softcap, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("decode launch: ") + hipGetErrorString(e));
     return EXATTN_OK;

@@ -110,12 +110,21 @@ prefill_kernel(const FwdParams p) {
   uint8_t* gsm = smem + grp * GROUP_LDS;
 
   // ---- tile scheduler: heaviest query tiles first; (batch, head) fastest.
-  const int units = p.batch * p.h_q;
+  // Packed GQA (p.pack): a unit is one KV head, and its tiles hold the rows of
+  // all `group` query heads that read it, head fastest: virtual row R is
+  // position R / group of query head hk * group + R % group.  Unpacked, a unit
+  // is one query head and virtual row R is position R.
+  const bool pack = p.pack != 0;
+  const int G = pack ? p.group : 1;
+  const int units = p.batch * (pack ? p.h_kv : p.h_q);
   const int bid = blockIdx.x;
   const int qt = p.n_qt - 1 - bid / units;
   const int u = bid % units;
   int b, h;
-  if (p.xcd_group) {
+  if (pack) {
+    b = u / p.h_kv;
+    h = (u % p.h_kv) * p.group;  // the group's first query head
+  } else if (p.xcd_group) {
     // u % 8 picks the XCD; it depends only on the KV unit, so the query heads
     // sharing one K/V also share one L2.
     const int x = u & 7;
@@ -129,6 +138,8 @@ prefill_kernel(const FwdParams p) {
     h = u % p.h_q;
   }
   const int hk = h / p.group;
+  auto vpos = [&](int r) { return pack ? r / G : r; };   // virtual row -> position
+  auto vhead = [&](int r) { return pack ? r % G : 0; };  // virtual row -> head offset
 
   int sq = p.s_q, sk = p.s_k;
   int64_t qoff, koff, voff, ooff, lseoff;
@@ -154,7 +165,8 @@ prefill_kernel(const FwdParams p) {
   // Paired, group 0's waves 0-1 and group 1's waves 2-3 take tile j and the
   // others tile n64 - 1 - j, so each SIMD (waves w and w + 4) holds one wave of
   // each tile; otherwise waves 0-1 of each group take the first tile.
-  const int n64 = (sq + 63) / 64;
+  const int sqv = sq * G;  // virtual rows
+  const int n64 = (sqv + 63) / 64;
   if (2 * qt >= n64) return;  // uniform across the work group
   static_assert(!PAIR || NG == 2, "pairing needs two groups");
   constexpr bool paired = PAIR;
@@ -164,19 +176,16 @@ prefill_kernel(const FwdParams p) {
   const bool my_a = paired ? (wg >> 1) == grp : wg < 2;
   const bool my_valid = my_a || b_valid;
   const int q0 = 64 * (my_a ? tile_a : tile_b);   // first row of this wave's tile
-  const int q_last = min(q0 + 64, sq) - 1;
+  const int q_last = min(q0 + 64, sqv) - 1;
 
-  const uint16_t* qg = p.q + qoff + (int64_t)h * p.q_sh;
   const uint16_t* kg = p.k + koff + (int64_t)hk * p.k_sh;
   const uint16_t* vg = p.v + voff + (int64_t)hk * p.v_sh;
-  uint16_t* og = p.o + ooff + (int64_t)h * p.o_sh;
-  float* lseg = p.lse != nullptr ? p.lse + lseoff + (int64_t)h * p.lse_sh : nullptr;
 
   // ---- visible key blocks [lo, hi) of a 64-row tile (bottom-right aligned);
   // the groups walk the union over both tiles, a wave computes its own tile's.
   const int off = sk - sq;
   auto block_range = [&](int tile, int& lo, int& hi) {
-    const int t0 = 64 * tile, t1 = min(t0 + 64, sq) - 1;
+    const int t0 = vpos(64 * tile), t1 = vpos(min(64 * tile + 64, sqv) - 1);
     int kmin = 0, kmax = sk - 1;
     if (p.wl >= 0) kmin = max(0, t0 + off - p.wl);
     if (p.wr >= 0) kmax = min(kmax, t1 + off + p.wr);
@@ -195,14 +204,21 @@ prefill_kernel(const FwdParams p) {
     n_lo = a_hi > a_lo ? min(a_lo, b_lo) : b_lo;
     n_hi = max(a_hi, b_hi);
   }
+  // Group g takes the blocks whose index is g modulo NG, counted from key 0
+  // (not from the tile's first block): a row then sums the same blocks in the
+  // same group whatever tile holds it, so its result does not depend on the
+  // tiling (packed or not).  Block n_lo - 1 may be loaded and never computed.
+  if (n_hi > n_lo) n_lo -= n_lo % NG;
   const int w_lo = my_a ? a_lo : b_lo;                    // this wave's blocks
   const int w_hi = my_valid ? (my_a ? a_hi : b_hi) : 0;
 
   // ---- Q^T fragments: lane holds Q[row][16 ks + 8 hsel .. +7] for every ks.
-  const int qrow = q0 + 32 * (wg & 1) + l32;
+  const int qrow = q0 + 32 * (wg & 1) + l32;  // virtual row of this lane
+  const int qpos = vpos(qrow);                 // its position
+  const int qhead = h + vhead(qrow);           // its query head
   u32x4_t qf[KS];
-  if (my_valid && qrow < sq) {
-    const uint16_t* qp = qg + (int64_t)qrow * p.q_ss + 8 * hsel;
+  if (my_valid && qrow < sqv) {
+    const uint16_t* qp = p.q + qoff + (int64_t)qhead * p.q_sh + (int64_t)qpos * p.q_ss + 8 * hsel;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
   } else {
@@ -360,10 +376,10 @@ prefill_kernel(const FwdParams p) {
   // Keys <= full_r and >= full_l are visible to every row of the wave's tile,
   // so only blocks that reach past them carry a mask; this lane's row sees
   // keys mlo + 8 hsel .. mhi + 8 hsel.
-  const int full_r = p.wr >= 0 ? min(sk - 1, q0 + off + p.wr) : sk - 1;
-  const int full_l = p.wl >= 0 ? q_last + off - p.wl : -0x3fffffff;
-  const int mhi = (p.wr >= 0 ? min(sk - 1, qrow + off + p.wr) : sk - 1) - 8 * hsel;
-  const int mlo = (p.wl >= 0 ? qrow + off - p.wl : -0x3fffffff) - 8 * hsel;
+  const int full_r = p.wr >= 0 ? min(sk - 1, vpos(q0) + off + p.wr) : sk - 1;
+  const int full_l = p.wl >= 0 ? vpos(q_last) + off - p.wl : -0x3fffffff;
+  const int mhi = (p.wr >= 0 ? min(sk - 1, qpos + off + p.wr) : sk - 1) - 8 * hsel;
+  const int mlo = (p.wl >= 0 ? qpos + off - p.wl : -0x3fffffff) - 8 * hsel;
   // The exponentials are first taken against the current reference; the
   // block's row max is needed only when a lane's block sum exceeds 2^tau (some
   // p may exceed 2^tau, or overflowed) or a row has no reference yet (then the
@@ -718,8 +734,9 @@ prefill_kernel(const FwdParams p) {
   // LSE after the barrier: the barrier's release fence waits for every
   // outstanding store, so a store issued before it made all waves wait for a
   // write round trip to memory.
-  if (grp == 0 && my_valid && qrow < sq && hsel == 0 && lseg != nullptr)
-    lseg[qrow] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+  if (grp == 0 && my_valid && qrow < sqv && hsel == 0 && p.lse != nullptr)
+    p.lse[lseoff + (int64_t)qhead * p.lse_sh + qpos] =
+        l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
   // O tile -> global, 16 bytes per thread: rows 0-63 are tile_a, 64-127 tile_b
   constexpr int NTH = 256 * NG;
   static_assert(kBM * DCH % NTH == 0, "O tile copy");
@@ -727,10 +744,11 @@ prefill_kernel(const FwdParams p) {
   for (int it = 0; it < kBM * DCH / NTH; ++it) {
     const int idx = it * NTH + tid;
     const int row = idx / DCH, chunk = idx % DCH;
-    const int grow = 64 * (row < 64 ? tile_a : tile_b) + (row & 63);
-    if ((row < 64 || b_valid) && grow < sq) {
+    const int grow = 64 * (row < 64 ? tile_a : tile_b) + (row & 63);  // virtual row
+    if ((row < 64 || b_valid) && grow < sqv) {
       const u32x4_t v = *(const u32x4_t*)(otile + row * OROW + 16 * (chunk ^ kswz<D>(row)));
-      *(u32x4_t*)(og + (int64_t)grow * p.o_ss + 8 * chunk) = v;
+      uint16_t* op = p.o + ooff + (int64_t)(h + vhead(grow)) * p.o_sh + (int64_t)vpos(grow) * p.o_ss;
+      *(u32x4_t*)(op + 8 * chunk) = v;
     }
   }
 }

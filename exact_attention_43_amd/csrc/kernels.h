@@ -31,6 +31,7 @@ struct FwdParams {
   float cap_out_log2;  // softcap * log2(e)
   int32_t wl, wr;      // window; wr = 0 for causal; < 0 unbounded
   uint32_t q_sign;     // 0x80008000 when the scale is negative: Q is negated, scale_log2 = |.|
+  int32_t pack;        // 1: a tile packs the rows of the `group` query heads of one KV head
 };
 
 // Split-KV decode: one work group per (split, KV head x query-head group, batch).

@@ -18,6 +18,20 @@ bool stride_ok(int64_t s) { return s >= 0 && s % 8 == 0; }
 
 std::string str(int64_t v) { return std::to_string(v); }
 
+// The kernels address one tile of `rows` consecutive tokens (and `heads`
+// adjacent heads) with 32-bit byte offsets from the tile's first element
+// (DMA lane offsets, buffer-descriptor ranges).  The span from the tile's first
+// byte to the end of its last row must stay below 2^31 bytes.
+exattn_status check_span(const char* name, int64_t rows, int64_t token_stride, int64_t heads,
+                         int64_t head_stride, int64_t head_dim, int64_t elem_bytes) {
+  const int64_t span = ((rows - 1) * token_stride + (heads - 1) * head_stride + head_dim) * elem_bytes;
+  if (span >= ((int64_t)1 << 31))
+    return fail(EXATTN_E_UNSUPPORTED,
+                std::string(name) + ": a tile of " + str(rows) + " tokens spans " + str(span) +
+                    " bytes with these strides, beyond the kernels' 32-bit offsets (2^31 bytes)");
+  return EXATTN_OK;
+}
+
 exattn_status check_common(int32_t dtype, int32_t head_dim, int32_t heads_q, int32_t heads_kv,
                            int32_t batch) {
   if (dtype != EXATTN_F16 && dtype != EXATTN_BF16)
@@ -36,8 +50,11 @@ exattn_status check_common(int32_t dtype, int32_t head_dim, int32_t heads_q, int
 
 exattn_status resolve_scales(float softmax_scale, float softcap, int head_dim, float* scale_log2,
                              float* cap_in, float* cap_out_log2, bool* use_cap) {
+  // NaN selects the default 1/sqrt(head_dim); every other finite value, 0
+  // included (all scores 0: uniform weights over the visible keys), is used as
+  // given.
   float scale = softmax_scale;
-  if (isnan(scale) || scale == 0.0f) scale = 1.0f / sqrtf((float)head_dim);
+  if (isnan(scale)) scale = 1.0f / sqrtf((float)head_dim);
   if (!isfinite(scale)) return fail(EXATTN_E_INVALID, "softmax_scale is not finite");
   if (isnan(softcap) || isinf(softcap)) return fail(EXATTN_E_INVALID, "softcap is not finite");
   *use_cap = softcap > 0.0f;
@@ -130,12 +147,24 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   if (varlen && a->batch > 0 && (a->cu_seqlens_q == nullptr || a->cu_seqlens_k == nullptr))
     return fail(EXATTN_E_INVALID, "cu_seqlens is NULL");
 
-  pl->n_qt = (s_q + rows_per_tile - 1) / rows_per_tile;
-  const int64_t units = (int64_t)a->batch * a->heads_q;
+  // Packed GQA (FAQ Q15): one tile holds the rows of all query heads of a KV
+  // head.  Automatic: packed when that takes fewer work groups, i.e. when
+  // short query sequences leave most rows of the per-head tiles empty.
+  if (a->pack_gqa < -1 || a->pack_gqa > 1)
+    return fail(EXATTN_E_INVALID, "pack_gqa must be -1 (automatic), 0 or 1");
+  const int64_t g = pl->group;
+  const int64_t tiles_plain = (int64_t)a->heads_q * ((s_q + rows_per_tile - 1) / rows_per_tile);
+  const int64_t tiles_packed = (int64_t)a->heads_kv * ((s_q * g + rows_per_tile - 1) / rows_per_tile);
+  pl->pack = a->pack_gqa == 1 || (a->pack_gqa == -1 && g > 1 && tiles_packed < tiles_plain);
+  if (pl->pack && (int64_t)s_q * g > ((int64_t)1 << 30))
+    return fail(EXATTN_E_UNSUPPORTED, "seqlen_q x (heads_q / heads_kv) too large for packed GQA");
+  const int64_t rows = pl->pack ? (int64_t)s_q * g : s_q;
+  pl->n_qt = (int)((rows + rows_per_tile - 1) / rows_per_tile);
+  const int64_t units = (int64_t)a->batch * (pl->pack ? a->heads_kv : a->heads_q);
   const int64_t grid = units * pl->n_qt;
   if (grid > 0x7fffffffLL) return fail(EXATTN_E_INVALID, "problem too large for one launch");
   pl->grid = (int)grid;
-  pl->xcd_group = (pl->group > 1 && ((int64_t)a->batch * a->heads_kv) % 8 == 0) ? 1 : 0;
+  pl->xcd_group = (!pl->pack && pl->group > 1 && ((int64_t)a->batch * a->heads_kv) % 8 == 0) ? 1 : 0;
   return EXATTN_OK;
 }
 
@@ -181,6 +210,12 @@ exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d
         return fail(EXATTN_E_INVALID, "FP8 q, k, v strides must be non-negative multiples of 16 elements");
   for (int i = 0; i < 3; ++i)
     if (!stride_ok(a->o_stride[i])) return fail(EXATTN_E_INVALID, "o strides must be non-negative multiples of 8");
+  // 64-key K / V tiles (and 64-row Q tiles) of one head, 1 byte per element
+  const char* n8[3] = {"q", "k", "v"};
+  for (int t = 0; t < 3; ++t) {
+    st = check_span(n8[t], 64, s8[t][1], 1, 0, a->head_dim, 1);
+    if (st != EXATTN_OK) return st;
+  }
   if (a->lse != nullptr) {
     if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
     if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides must be non-negative");
@@ -260,6 +295,13 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
       return fail(EXATTN_E_INVALID, "k/v strides must be non-negative multiples of 8 elements");
   if (a->lse != nullptr && (reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0)
     return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
+  // One step's tile: its keys times the work group's adjacent KV heads.
+  const int kstep = decode_keys_per_step(a->head_dim, pl->hpw);
+  const int span_heads = a->heads_kv < pl->hpw ? a->heads_kv : pl->hpw;
+  st = check_span("k_cache", kstep, a->k_stride[1], span_heads, a->k_stride[2], a->head_dim, 2);
+  if (st != EXATTN_OK) return st;
+  st = check_span("v_cache", kstep, a->v_stride[1], span_heads, a->v_stride[2], a->head_dim, 2);
+  if (st != EXATTN_OK) return st;
   if ((int64_t)pl->n_hk * pl->n_hg > 65535 || a->batch > 65535)
     return fail(EXATTN_E_INVALID, "too many heads or batch entries for one launch");
   return EXATTN_OK;
@@ -324,6 +366,12 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
       if (!stride_ok(strides[t][i]))
         return fail(EXATTN_E_INVALID, "backward strides must be non-negative multiples of 8 elements");
   if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides are negative");
+  // Q and dO tiles of 32 rows, K and V tiles of up to 64 keys, one head each.
+  const char* bn[5] = {"q", "k", "v", "o", "dout"};
+  for (int t = 0; t < 5; ++t) {
+    st = check_span(bn[t], 64, strides[t][1], 1, 0, a->head_dim, 2);
+    if (st != EXATTN_OK) return st;
+  }
   if (rows > ((size_t)1 << 31) / 2) return fail(EXATTN_E_INVALID, "too many rows for one backward");
   if (a->batch > 65535 || a->heads_q > 65535)
     return fail(EXATTN_E_UNSUPPORTED, "the backward takes at most 65535 batch entries and query heads");

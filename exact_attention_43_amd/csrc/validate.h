@@ -33,6 +33,7 @@ struct FwdPlan {
   float scale_log2, cap_in, cap_out_log2;
   uint32_t q_sign;  // 0x80008000: negative scale, applied by negating Q (scale_log2 holds |scale|)
   int wl, wr;
+  bool pack;        // packed GQA: tiles over (position, query head of one KV head)
 };
 
 // Check `a` and fill `plan`.  rows_per_tile is the kernel's query tile height.

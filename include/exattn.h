@@ -21,7 +21,9 @@
  *   - softcap c > 0: score -> c * tanh(score / c) after scaling and before
  *     masking (Q22); c <= 0 disables it;
  *   - a row that sees no key gets O = 0 and LSE = -inf.
- * The default scale is 1/sqrt(head_dim) (Q12).
+ * The default scale is 1/sqrt(head_dim) (Q12), selected by softmax_scale = NaN;
+ * any finite softmax_scale, 0 and negative values included, is used as given
+ * (0 gives every visible key the same weight).
  *
  * Ownership and threading: the caller allocates and owns every buffer.  The
  * library keeps no pointer after a call returns, never allocates or frees
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define EXATTN_ABI_VERSION 1
+#define EXATTN_ABI_VERSION 2
 
 typedef enum {
   EXATTN_OK = 0,
@@ -57,8 +59,10 @@ typedef enum {
   EXATTN_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } exattn_status;
 
-/* Storage type of Q, K, V and O.  fp16/bf16 only ("FlashAttention完整说明",
- * section 八: half-precision types only).  Accumulation is fp32. */
+/* Storage type of Q, K, V (and O).  exattn_fwd, exattn_decode* and exattn_bwd
+ * take fp16 or bf16 ("FlashAttention完整说明", section 八: half-precision types
+ * only); EXATTN_FP8_E4M3 is accepted only by exattn_fwd_fp8 (Inference
+ * Cookbook FAQ Q20), whose output is bf16.  Accumulation is fp32 throughout. */
 typedef enum { EXATTN_F16 = 0, EXATTN_BF16 = 1, EXATTN_FP8_E4M3 = 2 } exattn_dtype;
 
 /*
@@ -97,10 +101,19 @@ typedef struct {
   int64_t lse_stride[2];                                       /* elements: batch, head */
   const int32_t *cu_seqlens_q, *cu_seqlens_k;                  /* device int32[batch+1] or NULL */
   int32_t max_seqlen_q, max_seqlen_k;                          /* varlen only */
-  float softmax_scale; /* 0 or NaN: 1/sqrt(head_dim) */
+  float softmax_scale; /* NaN: 1/sqrt(head_dim); any finite value (0 included) as given */
   float softcap;       /* <= 0: off */
   int32_t causal;      /* nonzero: bottom-right causal, forces window_right = 0 */
   int32_t window_left, window_right; /* < 0: unbounded */
+  /* Packed GQA (FAQ Q15): 1 = one query tile holds the rows of all
+   * heads_q / heads_kv query heads that read one KV head (position-major, head
+   * fastest), so short query sequences fill the tiles; 0 = one tile per query
+   * head; -1 = automatic (packed when that takes fewer work groups).  The
+   * results are the same either way: bitwise equal whenever both launches use
+   * the same kernel variant (the variant depends on the grid size), else within
+   * rounding (each row then sums its key blocks in another grouping).  Other
+   * values: EXATTN_E_INVALID.  exattn_fwd_fp8 ignores it. */
+  int32_t pack_gqa;
 } exattn_fwd_args;
 
 /* Run the forward.  head_dim must be 64, 128 or 256; heads_q % heads_kv == 0.
@@ -138,7 +151,7 @@ typedef struct {
   int64_t q_stride[2], o_stride[2];  /* elements: batch, head */
   int64_t k_stride[3], v_stride[3];  /* elements: batch, token, head */
   const int32_t *cache_seqlens;      /* device int32[batch] or NULL */
-  float softmax_scale;               /* 0 or NaN: 1/sqrt(head_dim) */
+  float softmax_scale;               /* NaN: 1/sqrt(head_dim); else as given */
   float softcap;                     /* <= 0: off */
   int32_t causal;
   int32_t window_left, window_right; /* < 0: unbounded */
@@ -244,7 +257,7 @@ typedef struct {
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], dout_stride[3];
   int64_t dq_stride[3], dk_stride[3], dv_stride[3];
   int64_t lse_stride[2];
-  float softmax_scale; /* 0 or NaN: 1/sqrt(head_dim) */
+  float softmax_scale; /* NaN: 1/sqrt(head_dim); else as given */
   float softcap;       /* must be <= 0 (off) */
   int32_t causal;
   int32_t window_left, window_right;

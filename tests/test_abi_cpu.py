@@ -44,7 +44,7 @@ def test_struct_layout_and_version(L):
     assert L.exattn_args_size(4) == C.sizeof(ex.BwdArgs)
     assert L.exattn_args_size(5) == C.sizeof(ex.Fp8Descale)
     assert L.exattn_args_size(7) == 0
-    assert L.exattn_abi_version() == 1
+    assert L.exattn_abi_version() == 2
     assert L.exattn_status_string(0) == b"EXATTN_OK"
     assert L.exattn_status_string(3) == b"EXATTN_E_WORKSPACE"
 
@@ -88,6 +88,8 @@ BAD_FWD = [
     ("inf scale", dict(softmax_scale=float("inf")), ex.EXATTN_E_INVALID),
     ("nan softcap", dict(softcap=float("nan")), ex.EXATTN_E_INVALID),
     ("misaligned lse", dict(lse=FAKE + 2), ex.EXATTN_E_INVALID),
+    ("pack_gqa 2", dict(pack_gqa=2), ex.EXATTN_E_INVALID),
+    ("pack_gqa -2", dict(pack_gqa=-2), ex.EXATTN_E_INVALID),
 ]
 
 
@@ -134,6 +136,12 @@ BAD_DEC = [
     ("negative cache", dict(seqlen_cache=-1), ex.EXATTN_E_INVALID),
     ("null cache", dict(k_cache=None), ex.EXATTN_E_INVALID),
     ("odd stride", dict(k_stride=[16384 * 8 * 128, 8 * 128 + 2, 128]), ex.EXATTN_E_INVALID),
+    # head-major cache: a step's tile spans 8 adjacent KV heads, 7 head strides of 2^28
+    # elements = 3.5 GiB, beyond the kernel's 32-bit offsets
+    ("head stride past 32-bit tile offsets", dict(v_stride=[8 << 28, 128, 1 << 28]),
+     ex.EXATTN_E_UNSUPPORTED),
+    ("token stride past 32-bit tile offsets", dict(k_stride=[1 << 40, 1 << 27, 128]),
+     ex.EXATTN_E_UNSUPPORTED),
 ]
 
 
@@ -263,6 +271,8 @@ BAD_FP8 = [
     ("heads ratio", dict(heads_q=3), None, ex.EXATTN_E_INVALID),
     ("nan descale", dict(), (1.0, float("nan"), 1.0), ex.EXATTN_E_INVALID),
     ("inf descale", dict(), (1.0, 1.0, float("inf")), ex.EXATTN_E_INVALID),
+    ("token stride past 32-bit tile offsets", dict(v_stride=[1 << 40, 1 << 26, 128]), None,
+     ex.EXATTN_E_UNSUPPORTED),
 ]
 
 
@@ -315,6 +325,8 @@ BAD_BWD = [
     ("odd stride", dict(dv_stride=[96 * 2 * 128, 2 * 128 + 2, 128]), ex.EXATTN_E_INVALID),
     ("negative lse stride", dict(lse_stride=[-64, 64]), ex.EXATTN_E_INVALID),
     ("inf scale", dict(softmax_scale=float("inf")), ex.EXATTN_E_INVALID),
+    ("token stride past 32-bit tile offsets", dict(dout_stride=[1 << 40, 1 << 25, 128]),
+     ex.EXATTN_E_UNSUPPORTED),
 ]
 
 
@@ -360,3 +372,67 @@ def test_auto_splits_rules(L):
     assert ex.auto_splits(1, 8, 8, 0, 128, 256) == 1
     assert ex.auto_splits(2, 64, 1, 1 << 20, 128, 256) == 32    # one KV head, 4 groups of 16 queries
     assert ex.auto_splits(2, 6, 3, 1 << 20, 64, 256) == 64      # 3 KV heads -> 2 per work group
+
+
+def test_head_major_decode_cache_within_offsets_is_accepted(L):
+    """A head-major cache (b, h, s, d) whose 8-head tile stays below 2^31 bytes plans fine."""
+    a = _dec(k_stride=[8 * 16384 * 128, 128, 16384 * 128], v_stride=[8 * 16384 * 128, 128, 16384 * 128])
+    assert L.exattn_decode_plan(C.byref(a), None, None) == ex.EXATTN_OK, L.exattn_last_error()
+
+
+def test_fwd_pack_gqa_values_accepted(L):
+    for v in (-1, 0, 1):
+        assert L.exattn_fwd(C.byref(_fwd(pack_gqa=v, batch=0)), None) == ex.EXATTN_OK
+
+
+# --------------------------------------------------------------------------
+# the binding's own checks of caller-supplied outputs (before any device use)
+# --------------------------------------------------------------------------
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float16)
+
+
+def test_binding_rejects_mismatched_out_and_lse():
+    import torch
+    q = _t(1, 8, 2, 64)
+    with pytest.raises(ValueError, match="out must be"):
+        ex.attn_func(q, q, q, out=_t(1, 8, 2, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        ex.attn_func(q, q, q, out=_t(1, 8, 2, 32))
+    with pytest.raises(ValueError, match="contiguous last dimension"):
+        ex.attn_func(q, q, q, out=_t(1, 8, 2, 128)[..., ::2])
+    with pytest.raises(ValueError, match="lse must be"):
+        ex.attn_func(q, q, q, lse=_t(1, 2, 8))  # fp16, not fp32
+    with pytest.raises(ValueError, match="lse must be"):
+        ex.attn_func(q, q, q, lse=_t(1, 8, 2, dtype=torch.float32))  # (b, s, h) instead of (b, h, s)
+    with pytest.raises(ValueError, match="contiguous last dimension"):
+        ex.attn_func(q, q, q, lse=_t(1, 2, 16, dtype=torch.float32)[..., ::2])
+
+
+def test_binding_varlen_checks():
+    import torch
+    q, k = _t(10, 4, 64), _t(12, 2, 64)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    cuk = torch.tensor([0, 12], dtype=torch.int32)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        ex.attn_varlen_func(q, k, _t(12, 2, 32), cu, cuk, 10, 12)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        ex.attn_varlen_func(q, _t(12, 2, 128), _t(12, 2, 128), cu, cuk, 10, 12)
+    with pytest.raises(ValueError, match="one dtype"):
+        ex.attn_varlen_func(q, k, _t(12, 2, 64, dtype=torch.bfloat16), cu, cuk, 10, 12)
+    with pytest.raises(ValueError, match="out must be"):
+        ex.attn_varlen_func(q, k, k, cu, cuk, 10, 12, out=_t(10, 4, 32))
+    with pytest.raises(ValueError, match="lse must be"):
+        ex.attn_varlen_func(q, k, k, cu, cuk, 10, 12, lse=_t(10, 4, dtype=torch.float32))
+
+
+def test_binding_kvcache_checks():
+    import torch
+    q, kc = _t(2, 1, 8, 128), _t(2, 100, 2, 128)
+    with pytest.raises(ValueError, match="out must be"):
+        ex.attn_with_kvcache(q, kc, kc, out=_t(2, 1, 8, 64))
+    with pytest.raises(ValueError, match="lse must be contiguous"):
+        ex.attn_with_kvcache(q, kc, kc, lse=_t(2, 16, 1, dtype=torch.float32)[:, ::2])
+    with pytest.raises(ValueError, match="lse must be"):
+        ex.attn_with_kvcache(q, kc, kc, lse=_t(2, 8, dtype=torch.float32))

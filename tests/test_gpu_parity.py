@@ -121,6 +121,143 @@ def _dense_grid(b, s_q, h_q):
     return b * h_q * math.ceil(s_q / 128)
 
 
+def _launch(b, s_q, h_q, h_kv, d, masked, pack=False):
+    """The prefill launch the library picks (exattn_api.cpp): (groups, paired)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = b * h_kv * math.ceil(s_q * (h_q // h_kv) / 128) if pack else _dense_grid(b, s_q, h_q)
+    groups = 1 if d == 256 or grid >= 2 * cus else 2
+    return groups, groups == 2 and masked and grid <= cus
+
+
+# Every instance of the prefill kernel template, each at a shape that makes the
+# library pick it: (dtype, head_dim, softcap on/off, one group / two groups /
+# two groups pairing a light and a heavy tile).  Masks, GQA and the sign of the
+# scale vary along the way (a negative scale negates Q inside the kernel).
+INSTANCE_CASES = []
+for _dt in (torch.float16, torch.bfloat16):
+    for _d in (64, 128, 256):
+        for _cap in (0.0, 30.0):
+            for _kind in (("one",) if _d == 256 else ("one", "two", "paired")):
+                INSTANCE_CASES.append((_dt, _d, _cap, _kind))
+
+
+def _instance_shape(d, kind):
+    # (b, s_q, s_k, h_q, h_kv, causal, window)
+    if kind == "one":
+        return (2, 2100, 2100, 16, 4, True, (-1, -1)) if d < 256 else (2, 1100, 1100, 8, 4, True, (-1, -1))
+    if kind == "two":
+        return (1, 700, 900, 8, 2, False, (-1, -1))
+    return (1, 1024, 1024, 4, 2, True, (-1, -1))
+
+
+@pytest.mark.parametrize("case", INSTANCE_CASES,
+                         ids=[f"{'f16' if c[0] == torch.float16 else 'bf16'}-d{c[1]}-cap{int(c[2])}-{c[3]}"
+                              for c in INSTANCE_CASES])
+def test_prefill_instances(case):
+    dt, d, cap, kind = case
+    b, sq, sk, hq, hkv, causal, window = _instance_shape(d, kind)
+    idx = INSTANCE_CASES.index(case)
+    # a negative scale: causal one-group and paired launches at d = 128, and the
+    # two-group launches with softcap
+    neg = (d == 128 and kind in ("one", "paired")) or (kind == "two" and cap > 0)
+    scale = -0.7 / math.sqrt(d) if neg else None
+    groups, paired = _launch(b, sq, hq, hkv, d, causal or window != (-1, -1))
+    want = {"one": (1, False), "two": (2, False), "paired": (2, True)}[kind]
+    if kind == "one" and d != 256:
+        assert _dense_grid(b, sq, hq) >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert (groups, paired) == want, f"shape picks {(groups, paired)}, not {kind}"
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=300 + idx, dtype=dt)
+    dq, dk, dv = _dev(q, k, v)
+    out = _poison_out(q.shape, dt)
+    lse = _poison_lse((b, hq, sq))
+    ex.attn_func(dq, dk, dv, causal=causal, window_size=window, softcap=cap, softmax_scale=scale,
+                 out=out, lse=lse)
+    torch.cuda.synchronize()
+    heads = sorted({0, hq // 2 + 1, hq - 1})
+    o_ref, l_ref = oracle.attention(q, k, v, causal=causal, window_size=window, softcap=cap,
+                                    softmax_scale=scale, heads=heads)
+    o_cpu, l_cpu = out.cpu(), lse.cpu()
+    assert not torch.isnan(o_cpu).any()
+    for h in heads:
+        assert_o_close(o_cpu[:, :, h], o_ref[:, :, h], dt, f"{kind} d{d} cap{cap} h{h}")
+        assert_lse_close(l_cpu[:, h], l_ref[:, h], f"{kind} d{d} cap{cap} h{h}")
+
+
+# Packed GQA (FAQ Q15): the rows of all query heads of a KV head share the tiles.
+PACK_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, dtype, causal, window, softcap, seed
+    (2, 16, 500, 32, 4, 128, torch.bfloat16, True, (-1, -1), 0.0, 400),     # short queries, causal
+    (3, 7, 7, 16, 2, 64, torch.float16, True, (-1, -1), 0.0, 401),          # s_q = s_k, tiny
+    (1, 100, 1000, 8, 1, 128, torch.bfloat16, False, (300, 20), 20.0, 402),  # window, softcap, MQA
+    (2, 33, 33, 12, 3, 256, torch.float16, True, (-1, -1), 0.0, 403),
+    (1, 300, 300, 8, 2, 128, torch.float16, True, (64, 0), 0.0, 404),        # tiles of several positions
+    (64, 16, 200, 64, 8, 128, torch.bfloat16, True, (-1, -1), 0.0, 405),     # one-group launches both ways
+]
+
+
+@pytest.mark.parametrize("case", PACK_CASES, ids=[f"k{c[-1]}" for c in PACK_CASES])
+def test_pack_gqa(case):
+    """pack_gqa on against the oracle; off and on bitwise equal when both launches pick the
+    same number of wave groups (then every row sums the same key blocks in the same order)."""
+    b, sq, sk, hq, hkv, d, dt, causal, window, cap, seed = case
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=seed, dtype=dt)
+    dq, dk, dv = _dev(q, k, v)
+    res = {}
+    for pack in (True, False):
+        out = _poison_out(q.shape, dt)
+        lse = _poison_lse((b, hq, sq))
+        ex.attn_func(dq, dk, dv, causal=causal, window_size=window, softcap=cap, pack_gqa=pack, out=out,
+                     lse=lse)
+        res[pack] = (out, lse)
+    torch.cuda.synchronize()
+    heads = None if b * hq <= 64 else [0, 9, hq - 1]
+    o_ref, l_ref = oracle.attention(q, k, v, causal=causal, window_size=window, softcap=cap, heads=heads)
+    for pack in (True, False):
+        o, l = res[pack][0].cpu(), res[pack][1].cpu()
+        if heads is None:
+            assert_o_close(o, o_ref, dt, f"pack={pack}")
+            assert_lse_close(l, l_ref, f"pack={pack}")
+        else:
+            for h in heads:
+                assert_o_close(o[:, :, h], o_ref[:, :, h], dt, f"pack={pack} h{h}")
+                assert_lse_close(l[:, h], l_ref[:, h], f"pack={pack} h{h}")
+    masked = causal or window != (-1, -1)
+    if _launch(b, sq, hq, hkv, d, masked, True)[0] == _launch(b, sq, hq, hkv, d, masked, False)[0]:
+        assert torch.equal(res[True][0], res[False][0]) and torch.equal(res[True][1], res[False][1])
+
+
+def test_pack_gqa_varlen():
+    lens_q = [5, 0, 17, 64, 1]
+    lens_k = [40, 3, 17, 300, 1]
+    hq, hkv = 16, 4
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, hq, hkv, 128, seed=406)
+    dq, dk, dv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((hq, q.shape[0]))
+    ex.attn_varlen_func(dq, dk, dv, dcq, dck, max(lens_q), max(lens_k), causal=True, pack_gqa=True,
+                        out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal=True)
+    assert_o_close(out, o_ref, q.dtype, "pack varlen")
+    assert_lse_close(lse, l_ref, "pack varlen")
+
+
+def test_zero_scale_is_uniform():
+    """softmax_scale = 0 is a scale like any other (not the default): every visible key gets
+    the same weight, so O is the mean of the visible V rows and LSE = ln(count)."""
+    q, k, v = W.qkv(2, 100, 150, 4, 2, 128, seed=407)
+    run_dense(q, k, v, "scale 0", causal=True, softmax_scale=0.0)
+    qd, kc, vc = W.kvcache(2, 300, 8, 2, 128, seed=408)
+    lens = torch.tensor([300, 77], dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(qd, kc, vc, lens)
+    out, lse = ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, softmax_scale=0.0, num_splits=3)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_kvcache(qd, kc, vc, lens, softmax_scale=0.0)
+    assert_o_close(out, o_ref, qd.dtype, "decode scale 0")
+    assert_lse_close(lse, l_ref, "decode scale 0")
+    np.testing.assert_allclose(lse.cpu().numpy()[:, 0, 0], np.log(300.0), atol=1e-4)
+
+
 ONE_GROUP_CASES = [
     # dtype, b, s_q, s_k, h_q, h_kv, d, causal, window, softcap
     (torch.bfloat16, 4, 1061, 1061, 16, 4, 128, True, (-1, -1), 0.0),
@@ -492,8 +629,9 @@ def test_fp8_forward(case):
     assert np.array_equal(np.isneginf(lg), np.isneginf(rl)), "fp8 LSE: -inf pattern differs"
     fin = ~np.isneginf(rl)
     bound = 1e-4 + 2.0 ** -11 * scale_eff * mag
-    err = np.abs(lg - rl)
     assert not np.isnan(lg).any()
+    err = np.zeros_like(rl)
+    err[fin] = np.abs(lg[fin] - rl[fin])  # -inf rows already matched exactly above
     assert np.all(err[fin] <= bound[fin]), f"fp8 LSE: max err {err[fin].max():.3e}, worst err/bound {(err[fin] / bound[fin]).max():.3f}"
 
 
@@ -712,3 +850,40 @@ def test_graph_capture_decode_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
+
+
+def test_graph_capture_prefill_and_backward():
+    """The forward and the backward captured in one graph (fixed addresses, FAQ Q19) replay
+    to the eager results, with eager work and synchronisations between the replays."""
+    q, k, v = W.qkv(2, 300, 300, 8, 2, 128, seed=409)
+    dout = W.qkv(2, 300, 1, 8, 1, 128, seed=410)[0]
+    dq_, dk_, dv_, ddo = _dev(q, k, v, dout)
+    out = torch.empty_like(dq_)
+    lse = torch.empty((2, 8, 300), dtype=torch.float32, device=DEV)
+    gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+
+    def calls():
+        ex.attn_func(dq_, dk_, dv_, causal=True, out=out, lse=lse)
+        ex.attn_backward(ddo, dq_, dk_, dv_, out, lse, causal=True, dq=gq, dk=gk, dv=gv, workspace=ws)
+
+    calls()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, lse, gq, gk, gv)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (out, lse, gq, gk, gv):
+            t.fill_(float("nan"))
+        junk = (dq_.float() @ dq_.float().transpose(-1, -2)).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for t, e in zip((out, lse, gq, gk, gv), eager):
+            assert torch.equal(t, e), f"replay {rep}"
