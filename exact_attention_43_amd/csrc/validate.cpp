@@ -1,6 +1,7 @@
 // Host-side argument checks and launch planning (no HIP dependency).
 #include "validate.h"
 
+#include <float.h>
 #include <math.h>
 
 #include <string>
@@ -106,6 +107,10 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
     pl->scale_log2 = -pl->scale_log2;
     pl->cap_in = -pl->cap_in;
   }
+  // It also masks raw scores (-inf) before scaling, and -inf * 0 is NaN: a zero
+  // scale is applied as the smallest normal float, whose products with finite
+  // scores are so small that every exponential is exactly 1, as for scale 0.
+  if (pl->scale_log2 == 0.0f) pl->scale_log2 = FLT_MIN;
 
   pl->bf16 = a->dtype == EXATTN_BF16;
   pl->head_dim = a->head_dim;
