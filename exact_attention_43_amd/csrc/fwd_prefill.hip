@@ -138,8 +138,18 @@ prefill_kernel(const FwdParams p) {
     h = u % p.h_q;
   }
   const int hk = h / p.group;
-  auto vpos = [&](int r) { return pack ? r / G : r; };   // virtual row -> position
-  auto vhead = [&](int r) { return pack ? r % G : 0; };  // virtual row -> head offset
+  // Virtual row -> position and head offset.  Rows divide through a float
+  // reciprocal, exact after the +-1 correction for rows below 2^22 (the host
+  // limits packed launches to that); unpacked rows are positions.
+  const float rcp_g = __builtin_amdgcn_rcpf((float)G);
+  auto vpos = [&](int r) {
+    if (!pack) return r;
+    int q = (int)((float)r * rcp_g);
+    q += (q + 1) * G <= r ? 1 : 0;
+    q -= q * G > r ? 1 : 0;
+    return q;
+  };
+  auto vhead = [&](int r) { return pack ? r - vpos(r) * G : 0; };
 
   int sq = p.s_q, sk = p.s_k;
   int64_t qoff, koff, voff, ooff, lseoff;

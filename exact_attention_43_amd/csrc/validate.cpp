@@ -161,8 +161,10 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   const int64_t tiles_plain = (int64_t)a->heads_q * ((s_q + rows_per_tile - 1) / rows_per_tile);
   const int64_t tiles_packed = (int64_t)a->heads_kv * ((s_q * g + rows_per_tile - 1) / rows_per_tile);
   pl->pack = a->pack_gqa == 1 || (a->pack_gqa == -1 && g > 1 && tiles_packed < tiles_plain);
-  if (pl->pack && (int64_t)s_q * g > ((int64_t)1 << 30))
-    return fail(EXATTN_E_UNSUPPORTED, "seqlen_q x (heads_q / heads_kv) too large for packed GQA");
+  const bool pack_fits = (int64_t)s_q * g < ((int64_t)1 << 22);  // the kernel's row division
+  if (a->pack_gqa == 1 && !pack_fits)
+    return fail(EXATTN_E_UNSUPPORTED, "packed GQA takes seqlen_q x (heads_q / heads_kv) below 2^22");
+  pl->pack = pl->pack && pack_fits;
   const int64_t rows = pl->pack ? (int64_t)s_q * g : s_q;
   pl->n_qt = (int)((rows + rows_per_tile - 1) / rows_per_tile);
   const int64_t units = (int64_t)a->batch * (pl->pack ? a->heads_kv : a->heads_q);
