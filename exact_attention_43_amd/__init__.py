@@ -130,6 +130,8 @@ def lib():
             L.exattn_decode_plan.restype = C.c_int
             L.exattn_decode.argtypes = [C.POINTER(DecodeArgs), C.c_void_p, C.c_size_t, C.c_void_p]
             L.exattn_decode.restype = C.c_int
+            L.exattn_decode_noalloc.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
+            L.exattn_decode_noalloc.restype = C.c_int
             L.exattn_decode_append.argtypes = [C.POINTER(DecodeArgs), C.POINTER(KvNew), C.c_void_p,
                                                C.c_size_t, C.c_void_p]
             L.exattn_decode_append.restype = C.c_int

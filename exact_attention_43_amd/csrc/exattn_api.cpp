@@ -356,6 +356,34 @@ exattn_status exattn_decode(const exattn_decode_args* a, void* workspace, size_t
   return run_decode(a, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
+exattn_status exattn_decode_noalloc(const exattn_decode_args* a, void* stream) {
+  try {
+    clear_error();
+    DecodePlan pl;
+    exattn_status st = plan_decode(a, 1, &pl);
+    if (st != EXATTN_OK) return st;
+    if (a->num_splits == 0) {
+      int cus = 1;
+      st = device_cus(&cus);
+      if (st != EXATTN_OK) return st;
+      st = plan_decode(a, cus, &pl);
+      if (st != EXATTN_OK) return st;
+    }
+    if (pl.empty) return EXATTN_OK;
+    if (pl.ws_bytes > kDecodeScratchBytes)
+      return fail(EXATTN_E_WORKSPACE, "the split partials need " + std::to_string(pl.ws_bytes) +
+                                          " bytes, more than the static scratch (" +
+                                          std::to_string(kDecodeScratchBytes) +
+                                          "): lower num_splits or use exattn_decode");
+    void* ptr = nullptr;
+    hipError_t e = decode_scratch(&ptr);
+    if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("scratch lookup: ") + hipGetErrorString(e));
+    return run_decode(a, nullptr, nullptr, ptr, kDecodeScratchBytes, stream);
+  } catch (...) {
+    return fail(EXATTN_E_HIP, "unexpected host exception");
+  }
+}
+
 exattn_status exattn_decode_append(const exattn_decode_args* a, const exattn_kv_new* kv_new,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   if (kv_new == nullptr) {

@@ -28,6 +28,9 @@
 // Kernel 2 (combine_kernel): LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s -
 // LSE) O_s, the merge of partial softmax results ("FlashAttention完整说明",
 // section 二.1); a split with no keys has LSE_s = -inf and weight 0.
+#include <mutex>
+#include <vector>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -491,12 +494,38 @@ hipError_t launch_t(const DecParams& p, int head_dim, bool softcap, hipStream_t 
   }
 }
 
+// Static scratch for the split partials of exattn_decode_noalloc: device memory
+// the library holds on every device it runs on, for callers that cannot
+// allocate.  In host code `scratch` names a host-side stand-in, not a device
+// address: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device; nullptr = not looked up yet
+
 }  // namespace
 
 hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softcap,
                          hipStream_t stream) {
   return bf16 ? launch_t<true>(p, head_dim, softcap, stream)
               : launch_t<false>(p, head_dim, softcap, stream);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = addr;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace exattn

@@ -118,6 +118,11 @@ hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool soft
                           int groups, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softcap,
                          hipStream_t stream);
+
+// Bytes of the static scratch array behind exattn_decode_noalloc (one per device).
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+// Device address of the current device's scratch array (looked up once per device).
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_bwd(const BwdParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace exattn

@@ -172,6 +172,20 @@ exattn_status exattn_decode_plan(const exattn_decode_args *args, int32_t *num_sp
 exattn_status exattn_decode(const exattn_decode_args *args, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* exattn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the split partials go to a static scratch array of 8 MiB that the library
+ * keeps on every device it runs on until the process ends, instead of a caller
+ * workspace.  Allocates nothing (no hipMalloc, no hipFree); the first call on a
+ * device looks up that device's array.  A plan whose partials need more than
+ * 8 MiB (splits x batch x heads_q x (head_dim + 1) x 4 bytes, rounded up)
+ * returns EXATTN_E_WORKSPACE with nothing launched: pass a smaller num_splits
+ * or use exattn_decode.  All calls on one device share the array and it keeps
+ * the last call's contents (nothing in it has to start at zero); calls that
+ * overlap on one device race on it, so order them on one stream.  Arguments,
+ * results and errors otherwise as exattn_decode. */
+exattn_status exattn_decode_noalloc(const exattn_decode_args *args, void *stream);
+
 /*
  * New tokens for exattn_decode_append: flash_attn_with_kvcache called with
  * k=k_new, v=v_new (FAQ Q17).  k_new and v_new are (batch, seqlen_new,
