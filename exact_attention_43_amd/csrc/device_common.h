@@ -92,6 +92,20 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t* lds) {
       u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)lds));
 }
 
+// Touch every 64-byte line of the kernel-argument block in one batch of scalar
+// loads and wait once.  The compiler loads argument fields when first used,
+// and the first use of each line would otherwise cost its own dependent round
+// trip to memory before the kernel's first loads can go out.
+template <int BYTES>
+__device__ __forceinline__ void prefetch_kernargs() {
+  const __attribute__((address_space(4))) uint32_t* ka =
+      (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t acc = ka[BYTES / 4 - 1];
+#pragma unroll
+  for (int o = 0; o < BYTES; o += 64) acc ^= ka[o / 4];
+  asm volatile("" ::"s"(acc));
+}
+
 // Swap values between the two 32-lane halves of the wave (lane i <-> lane i ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }

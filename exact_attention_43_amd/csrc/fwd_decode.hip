@@ -27,7 +27,8 @@
 //   workspace.
 // Kernel 2 (combine_kernel): LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s -
 // LSE) O_s, the merge of partial softmax results ("FlashAttention完整说明",
-// section 二.1); a split with no keys has LSE_s = -inf and weight 0.
+// section 二.1); a split with no keys has LSE_s = -inf and weight 0.  One
+// wave per (row, 64 head dims), so the partials are read by many CUs at once.
 #include <mutex>
 #include <vector>
 
@@ -94,6 +95,7 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+  prefetch_kernargs<sizeof(DecParams)>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,6 +175,11 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
 #pragma unroll
     for (int t = 0; t < KI; ++t) buffer_load_lds16(rv, dst + KTILE + (wave + NW * t) * 1024, vofs[t]);
   };
+
+  // the first step's DMA goes out before the Q loads (with an append it waits
+  // for the new rows, below)
+  const bool early = p.seq_add == 0 && s_lo < s_hi;
+  if (early) issue(s_lo, smem, paged ? page_of(kb + s_lo * KSTEP) : 0);
 
   // ---- Q^T fragments (B operand): lane (query column l16, group g16) holds
   // Q[head][32 ks + 8 g16 .. + 7] of query head hk * group + hg * 16 + l16.
@@ -317,7 +324,7 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   }
 
   if (s_lo < s_hi) {
-    issue(s_lo, smem, paged ? page_of(kb + s_lo * KSTEP) : 0);
+    if (!early) issue(s_lo, smem, paged ? page_of(kb + s_lo * KSTEP) : 0);
     if (paged && s_lo + 1 < s_hi) pg_next = page_of(kb + (s_lo + 1) * KSTEP);
   }
   for (int st = s_lo; st < s_hi; ++st) {
@@ -402,34 +409,41 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
 // threads cover 1024 / D rows.  The splits are taken 32 at a time with all
 // their loads issued together and merged with a running maximum, so a call
 // with up to 32 splits waits for one round trip to memory.
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 64;
 
+// One wave per (row, 64 head dims): lane = (split group sg = lane / 16, column
+// quad c = lane % 16).  Split group sg takes splits sg, sg + 4, ...; all its
+// loads go out together, the four groups merge by log-sum-exp through two
+// lane exchanges, and group 0 writes.  Rows x D/64 work groups, so every CU
+// gets some of the 4 MB of partials and each lane waits for one round trip.
 template <bool BF16, int D>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const DecParams p) {
   using E = Elem<BF16>;
-  constexpr int kU = 32;
-  constexpr int TPR = D / 4;  // threads per row
+  const int row = blockIdx.x / (D / 64);
+  const int cb = blockIdx.x % (D / 64);
+  const int lane = threadIdx.x;
+  const int sg = lane >> 4;
+  const int col = 64 * cb + 4 * (lane & 15);
   const int rows = p.batch * p.h_q;
-  const int row0 = blockIdx.x * (kCombineThreads / TPR) + threadIdx.x / TPR;
-  const int c4 = 4 * (threadIdx.x % TPR);
-  if (row0 >= rows) return;
   const int64_t stride = rows;
+  constexpr int kU = 16;  // splits per group per pass
   float m = kNegInf, ws = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.n_split; s0 += kU) {
+  for (int s0 = 0; s0 < p.n_split; s0 += 4 * kU) {
     float l[kU];
     f32x4_t v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool in = s0 + u < p.n_split;
-      const int64_t r = (s0 + u) * stride + row0;
+      const int s = s0 + sg + 4 * u;
+      const bool in = s < p.n_split;
+      const int64_t r = (int64_t)s * stride + row;
       l[u] = in ? p.ws_lse[r] : kNegInf;
-      v[u] = in ? *(const f32x4_t*)(p.ws_o + r * D + c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      v[u] = in ? *(const f32x4_t*)(p.ws_o + r * D + col) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     float mb = l[0];
 #pragma unroll
     for (int u = 1; u < kU; ++u) mb = fmaxf(mb, l[u]);
-    if (mb > m) {  // move the reference; nothing to rescale while it was -inf
+    if (mb > m) {
       const float sc = m == kNegInf ? 0.f : fast_exp2((m - mb) * kLog2e);
       ws *= sc;
       acc *= sc;
@@ -438,19 +452,35 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const DecParam
     if (m != kNegInf) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const float w = fast_exp2((l[u] - m) * kLog2e);  // 0 for an empty split
+        const float w = fast_exp2((l[u] - m) * kLog2e);
         ws += w;
         acc += w * v[u];
       }
     }
   }
+  // merge the four split groups (lanes c, c + 16, c + 32, c + 48)
+#pragma unroll
+  for (int sh = 16; sh <= 32; sh *= 2) {
+    const float m2 = __shfl_xor(m, sh, 64);
+    const float w2 = __shfl_xor(ws, sh, 64);
+    f32x4_t a2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a2[e] = __shfl_xor(acc[e], sh, 64);
+    const float mm = fmaxf(m, m2);
+    const float bm = mm == kNegInf ? 0.f : mm;
+    const float f1 = fast_exp2((m - bm) * kLog2e), f2 = fast_exp2((m2 - bm) * kLog2e);
+    ws = ws * f1 + w2 * f2;
+    acc = acc * f1 + a2 * f2;
+    m = mm;
+  }
+  if (sg != 0) return;
   const float inv = m != kNegInf ? 1.0f / ws : 0.f;
-  const int b = row0 / p.h_q, h = row0 % p.h_q;
+  const int b = row / p.h_q, h = row % p.h_q;
   u32x2_t w2;
   w2[0] = E::pack2(acc[0] * inv, acc[1] * inv);
   w2[1] = E::pack2(acc[2] * inv, acc[3] * inv);
-  *(u32x2_t*)(p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + c4) = w2;
-  if (c4 == 0 && p.lse != nullptr) p.lse[row0] = m != kNegInf ? m + fast_log2(ws) * kLn2 : kNegInf;
+  *(u32x2_t*)(p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + col) = w2;
+  if (cb == 0 && lane == 0 && p.lse != nullptr) p.lse[row] = m != kNegInf ? m + fast_log2(ws) * kLn2 : kNegInf;
 }
 
 template <bool BF16, int D, int HPWV>
@@ -478,9 +508,8 @@ hipError_t launch_d(const DecParams& p, bool softcap, hipStream_t stream) {
   else
     e = launch_h<BF16, D, 1>(p, softcap, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
-  const int rows_per_wg = kCombineThreads / (D / 4);
-  hipLaunchKernelGGL((combine_kernel<BF16, D>), dim3((p.batch * p.h_q + rows_per_wg - 1) / rows_per_wg),
-                     dim3(kCombineThreads), 0, stream, p);
+  hipLaunchKernelGGL((combine_kernel<BF16, D>), dim3(p.batch * p.h_q * (D / 64)), dim3(kCombineThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
