@@ -383,6 +383,46 @@ def pin_decode_append():
                                                                                 kc[0, :s_cache - 2])
 
 
+def pin_decode_multi_query():
+    """Several query tokens against the KV cache after an append (FAQ Q17 passes
+    k=k_new, v=v_new with causal=True; the mask is bottom-right, FAQ Q6): with
+    s_q = s_new new tokens and n cached rows, query t sits at position n + t of
+    the n + s_new keys.  With Q = 0 every visible score is 0, so query t's O is
+    the mean of the updated cache's rows 0..n+t and its LSE is ln(n + t + 1);
+    without causal every query sees all n + s_new rows; a window (2, 0) leaves
+    min(n + t, 2) + 1 rows; a query past the keys (s_q > n + s_new) sees none."""
+    r = _rng(24)
+    b, s_cache, h_q, h_kv, d, s_new = 3, 40, 4, 2, 8, 3
+    kc = r.standard_normal((b, s_cache, h_kv, d))
+    vc = r.standard_normal((b, s_cache, h_kv, d))
+    kn = r.standard_normal((b, s_new, h_kv, d))
+    vn = r.standard_normal((b, s_new, h_kv, d))
+    lens = [0, 5, 30]
+    q = np.zeros((b, s_new, h_q, d))
+    o, lse, kc2, vc2 = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens, causal=True)
+    assert o.shape == (b, s_new, h_q, d) and lse.shape == (b, h_q, s_new)
+    for bi, n in enumerate(lens):
+        for t in range(s_new):
+            for h in range(h_q):
+                hk = h // 2
+                assert abs(lse[bi, h, t] - math.log(n + t + 1)) < 1e-13
+                assert np.allclose(o[bi, t, h], vc2[bi, :n + t + 1, hk].mean(axis=0), atol=1e-13)
+    o, lse, _, _ = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens, causal=False)
+    for bi, n in enumerate(lens):
+        for t in range(s_new):
+            assert abs(lse[bi, 0, t] - math.log(n + s_new)) < 1e-13
+    o, lse, _, _ = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens, causal=True, window_size=(2, 0))
+    for bi, n in enumerate(lens):
+        for t in range(s_new):
+            assert abs(lse[bi, 1, t] - math.log(min(n + t, 2) + 1)) < 1e-13
+    # more queries than keys: the first ones see nothing (O = 0, LSE = -inf)
+    q5 = np.zeros((1, 5, 2, d))
+    o5, l5 = oracle.attention_kvcache(q5, kc[:1], vc[:1], [3], causal=True)
+    assert np.all(np.isneginf(l5[0, :, :2])) and np.all(o5[0, :2] == 0)
+    for t in range(2, 5):
+        assert abs(l5[0, 0, t] - math.log(t - 1)) < 1e-13
+
+
 def pin_paged():
     """A paged cache (FAQ Q18) read back as contiguous: the pool is built here by
     scattering the pages of a contiguous cache to a random permutation of page
@@ -606,7 +646,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_paged, pin_backward, pin_backward_magnitudes, pin_fp8, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_decode_multi_query, pin_paged, pin_backward, pin_backward_magnitudes, pin_fp8, pin_softcap,
         pin_default_scale]
 
 
