@@ -69,7 +69,8 @@ class DecodeArgs(C.Structure):
         ("cache_seqlens", C.c_void_p),
         ("softmax_scale", C.c_float), ("softcap", C.c_float),
         ("causal", C.c_int32), ("window_left", C.c_int32), ("window_right", C.c_int32),
-        ("num_splits", C.c_int32),
+        ("num_splits", C.c_int32), ("seqlen_q", C.c_int32),
+        ("q_token_stride", C.c_int64), ("o_token_stride", C.c_int64),
     ]
 
 
@@ -424,7 +425,10 @@ def _workspace(dev, nbytes):
 
 def _decode_args(q, k_cache, v_cache, out, lse, cache_seqlens, softmax_scale, causal, window_size,
                  softcap, num_splits, block_table=None):
-    b, h_q, d = q.shape[0], q.shape[-2], q.shape[-1]
+    """q and out are (b, s_q, h_q, d) (or (b, h_q, d) for one token)."""
+    if q.dim() == 3:
+        q, out = q.unsqueeze(1), out.unsqueeze(1)
+    b, s_q, h_q, d = q.shape
     s_cache, h_kv = k_cache.shape[1], k_cache.shape[2]
     if block_table is not None:  # pools of pages: capacity = pages per sequence x page size
         s_cache = block_table.shape[1] * k_cache.shape[1]
@@ -433,8 +437,10 @@ def _decode_args(q, k_cache, v_cache, out, lse, cache_seqlens, softmax_scale, ca
     a.batch, a.heads_q, a.heads_kv, a.head_dim, a.seqlen_cache = b, h_q, h_kv, d, s_cache
     a.q, a.k_cache, a.v_cache, a.o = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
-    a.q_stride[:] = [q.stride(0), q.stride(-2)]
-    a.o_stride[:] = [out.stride(0), out.stride(-2)]
+    a.q_stride[:] = [q.stride(0), q.stride(2)]
+    a.o_stride[:] = [out.stride(0), out.stride(2)]
+    a.seqlen_q = s_q
+    a.q_token_stride, a.o_token_stride = q.stride(1), out.stride(1)
     a.k_stride[:] = list(k_cache.stride()[:3])
     a.v_stride[:] = list(v_cache.stride()[:3])
     if block_table is not None:  # the batch stride is replaced by the page table
@@ -465,9 +471,11 @@ def decode_plan(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, cau
 def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, softmax_scale=None,
                       causal=False, window_size=(-1, -1), softcap=0.0, num_splits=0, out=None, lse=None,
                       workspace=None, block_table=None):
-    """KV-cache decode with one query token (FAQ Q17).
+    """KV-cache decode (FAQ Q17) for one or a few query tokens.
 
-    q (b, 1, h_q, d); k_cache, v_cache (b, s_cache, h_kv, d); cache_seqlens an
+    q (b, s_q, h_q, d), token t at position len - s_q + t of the len attended keys
+    (bottom-right: with causal, token t sees keys up to that position);
+    k_cache, v_cache (b, s_cache, h_kv, d); cache_seqlens an
     int32 GPU tensor (b,), an int, or None for the full cache.  With k, v
     (b, s_new, h_kv, d) the new tokens are first written to cache rows
     cache_seqlens[b] .. cache_seqlens[b] + s_new - 1 (k_cache and v_cache are
@@ -480,14 +488,14 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     """
     if (k is None) != (v is None):
         raise ValueError("pass both k and v to append, or neither")
-    if q.dim() != 4 or q.shape[1] != 1:
-        raise ValueError("q must be (batch, 1, heads_q, head_dim)")
+    if q.dim() != 4 or q.shape[1] < 1:
+        raise ValueError("q must be (batch, seqlen_q >= 1, heads_q, head_dim)")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must be (batch, seqlen_cache, heads_kv, head_dim)")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share one dtype")
     _check_out(out, q.shape, q.dtype)
-    _check_lse(lse, (q.shape[0], q.shape[2], 1), contiguous=True)  # the kernel writes lse[b * h_q + h]
+    _check_lse(lse, (q.shape[0], q.shape[2], q.shape[1]), contiguous=True)  # lse[(b * h_q + h) * s_q + t]
     _on_gpu(q, k_cache, v_cache, out, lse, cache_seqlens if torch.is_tensor(cache_seqlens) else None,
             workspace, k, v, block_table)
     pg = None
@@ -501,7 +509,7 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
         pg.page_size, pg.num_pages = k_cache.shape[1], k_cache.shape[0]
         pg.k_page_stride, pg.v_page_stride = k_cache.stride(0), v_cache.stride(0)
     _check_last_dim(q, k_cache, v_cache)
-    b, _, h_q, d = q.shape
+    b, s_q, h_q, d = q.shape
     kv = None
     if k is not None:
         if k.dim() != 4 or v.shape != k.shape or k.shape[0] != b or k.shape[2:] != k_cache.shape[2:]:
@@ -521,10 +529,10 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
         if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != b or not cache_seqlens.is_contiguous():
             raise ValueError("cache_seqlens must be a contiguous int32 tensor of batch entries")
     if out is None:
-        out = torch.empty((b, 1, h_q, d), dtype=q.dtype, device=q.device)
+        out = torch.empty((b, s_q, h_q, d), dtype=q.dtype, device=q.device)
     if lse is None:
-        lse = torch.empty((b, h_q, 1), dtype=torch.float32, device=q.device)
-    a = _decode_args(q[:, 0], k_cache, v_cache, out[:, 0], lse, cache_seqlens, softmax_scale, causal,
+        lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    a = _decode_args(q, k_cache, v_cache, out, lse, cache_seqlens, softmax_scale, causal,
                      window_size, softcap, num_splits, block_table)
     L = lib()
     with torch.cuda.device(q.device):

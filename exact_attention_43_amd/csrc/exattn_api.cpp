@@ -230,6 +230,10 @@ exattn_status run_decode(const exattn_decode_args* a, const exattn_kv_new* kv_ne
     p.cap_in = pl.cap_in;
     p.cap_out_log2 = pl.cap_out_log2;
     p.wl = pl.wl;
+    p.wr = pl.wr;
+    p.s_q = pl.s_q;
+    p.q_ss = a->q_token_stride;
+    p.o_ss = a->o_token_stride;
     if (debug_level() >= 1) {
       char buf[256];
       snprintf(buf, sizeof buf, "decode %s d=%d softcap=%d b=%d hq=%d hkv=%d cache=%d splits=%d wl=%d",

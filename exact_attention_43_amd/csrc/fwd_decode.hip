@@ -120,11 +120,12 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   // memory outside the cache.
   const int nk = p.cache_seqlens != nullptr ? min(max(p.cache_seqlens[b] + p.seq_add, 0), p.s_cache)
                                             : p.s_cache;
-  // The query sits at position nk - 1; only the left window edge removes keys.
-  // A paged cache starts the steps on a multiple of the step size, so that a
-  // step never straddles a page, and masks the keys before kb_w.
+  // Query token t sits at position nk - s_q + t (bottom-right); keys before
+  // the first token's left window edge are never needed.  A paged cache starts
+  // the steps on a multiple of the step size, so that a step never straddles a
+  // page, and masks the keys before kb_w.
   constexpr bool paged = PAGED;  // p.block_table != nullptr
-  const int kb_w = p.wl >= 0 ? max(0, nk - 1 - p.wl) : 0;
+  const int kb_w = p.wl >= 0 ? max(0, nk - p.s_q - p.wl) : 0;
   const int kb = paged ? kb_w - kb_w % KSTEP : kb_w;
   const int nsteps = nk > kb ? (nk - kb + KSTEP - 1) / KSTEP : 0;
   const int per = (nsteps + p.n_split - 1) / p.n_split;
@@ -183,16 +184,20 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
 
   // ---- Q^T fragments (B operand): lane (query column l16, group g16) holds
   // Q[head][32 ks + 8 g16 .. + 7] of query head hk * group + hg * 16 + l16.
-  const int qj = hg * 16 + l16;
+  // query column of this lane: token qt, query head qj of the group
+  const int qc = hg * 16 + l16;
+  const bool col_valid = qc < p.s_q * p.group;
+  const int qt = qc / p.group, qj = qc - qt * p.group;
   u32x4_t qf[HPWV][KS];
   bool hvalid[HPWV];
 #pragma unroll
   for (int i = 0; i < HPWV; ++i) {
     const int hh = slot * HPWV + i;
     hvalid[i] = hh < nh_valid;
-    const bool qv = hvalid[i] && qj < p.group;
+    const bool qv = hvalid[i] && col_valid;
     const uint16_t* qp =
-        p.q + (int64_t)b * p.q_sb + (int64_t)((hk0 + hh) * p.group + qj) * p.q_sh + 8 * g16;
+        p.q + (int64_t)b * p.q_sb + (int64_t)qt * p.q_ss + (int64_t)((hk0 + hh) * p.group + qj) * p.q_sh +
+        8 * g16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[i][ks] = qv ? *(const u32x4_t*)(qp + 32 * ks) : u32x4_t{0, 0, 0, 0};
@@ -203,6 +208,11 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   for (int i = 0; i < HPWV; ++i)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[i][ks]));
+
+  // ---- this lane's visible keys [k_lo, k_hi] (its token's causal / window band)
+  const int qpos = nk - p.s_q + qt;
+  const int k_hi = p.wr >= 0 ? min(nk - 1, qpos + p.wr) : nk - 1;
+  const int k_lo = p.wl >= 0 ? max(kb_w, qpos - p.wl) : kb_w;
 
   // ---- loop-invariant LDS operand offsets within a stage.
   const int krow = 16 * sub + l16;                      // K A-operand row (key in the tile)
@@ -254,7 +264,7 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
         else
           x[r] = s[r] * p.scale_log2;
         const int key = key0 + 4 * g16 + r;
-        if (key >= nk || key < kb_w) x[r] = kNegInf;
+        if (key > k_hi || key < k_lo) x[r] = kNegInf;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = fmaxf(mx, xor16(mx));
@@ -379,13 +389,13 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
   // ---- outputs: lane (query l16, group g16) holds O^T[16 dt + 4 g16 + r][l16].
 #pragma unroll
   for (int i = 0; i < HPWV; ++i) {
-    if (!hvalid[i] || qj >= p.group) continue;
+    if (!hvalid[i] || !col_valid) continue;
     const int h = (hk0 + slot * HPWV + i) * p.group + qj;
     const bool empty = !(l_tot[i] > 0.f);
     const float inv = empty ? 0.f : 1.0f / l_tot[i];
     const float lse = empty ? kNegInf : (m_run[i] + fast_log2(l_tot[i])) * kLn2;
     if (p.n_split == 1) {
-      uint16_t* op = p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + 4 * g16;
+      uint16_t* op = p.o + (int64_t)b * p.o_sb + (int64_t)qt * p.o_ss + (int64_t)h * p.o_sh + 4 * g16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x2_t w2;
@@ -393,9 +403,9 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
         w2[1] = E::pack2(oacc[i][dt][2] * inv, oacc[i][dt][3] * inv);
         *(u32x2_t*)(op + 16 * dt) = w2;
       }
-      if (g16 == 0 && p.lse != nullptr) p.lse[(int64_t)b * p.h_q + h] = lse;
+      if (g16 == 0 && p.lse != nullptr) p.lse[((int64_t)b * p.h_q + h) * p.s_q + qt] = lse;
     } else {
-      const int64_t row = ((int64_t)split * p.batch + b) * p.h_q + h;
+      const int64_t row = (((int64_t)split * p.batch + b) * p.s_q + qt) * p.h_q + h;
       float* wo = p.ws_o + row * D + 4 * g16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(wo + 16 * dt) = oacc[i][dt] * inv;
@@ -424,7 +434,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const DecParam
   const int lane = threadIdx.x;
   const int sg = lane >> 4;
   const int col = 64 * cb + 4 * (lane & 15);
-  const int rows = p.batch * p.h_q;
+  const int rows = p.batch * p.s_q * p.h_q;  // (b, token, head)
   const int64_t stride = rows;
   constexpr int kU = 16;  // splits per group per pass
   float m = kNegInf, ws = 0.f;
@@ -475,12 +485,14 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const DecParam
   }
   if (sg != 0) return;
   const float inv = m != kNegInf ? 1.0f / ws : 0.f;
-  const int b = row / p.h_q, h = row % p.h_q;
+  const int h = row % p.h_q, bt = row / p.h_q;
+  const int t = bt % p.s_q, b = bt / p.s_q;
   u32x2_t w2;
   w2[0] = E::pack2(acc[0] * inv, acc[1] * inv);
   w2[1] = E::pack2(acc[2] * inv, acc[3] * inv);
-  *(u32x2_t*)(p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + col) = w2;
-  if (cb == 0 && lane == 0 && p.lse != nullptr) p.lse[row] = m != kNegInf ? m + fast_log2(ws) * kLn2 : kNegInf;
+  *(u32x2_t*)(p.o + (int64_t)b * p.o_sb + (int64_t)t * p.o_ss + (int64_t)h * p.o_sh + col) = w2;
+  if (cb == 0 && lane == 0 && p.lse != nullptr)
+    p.lse[((int64_t)b * p.h_q + h) * p.s_q + t] = m != kNegInf ? m + fast_log2(ws) * kLn2 : kNegInf;
 }
 
 template <bool BF16, int D, int HPWV>
@@ -508,8 +520,8 @@ hipError_t launch_d(const DecParams& p, bool softcap, hipStream_t stream) {
   else
     e = launch_h<BF16, D, 1>(p, softcap, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<BF16, D>), dim3(p.batch * p.h_q * (D / 64)), dim3(kCombineThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((combine_kernel<BF16, D>), dim3(p.batch * p.s_q * p.h_q * (D / 64)),
+                     dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -48,7 +48,12 @@ struct DecParams {
   float* ws_o;                   // [split][batch][h_q][D] fp32 partial outputs
   float* ws_lse;                 // [split][batch][h_q] fp32 partial LSE
   int32_t batch, h_q, h_kv, group, s_cache;
-  int32_t n_split, n_hg;  // splits; query-head groups of 16 per KV head
+  int32_t n_split, n_hg;  // splits; groups of 16 query columns per KV head
+  // Several query tokens: query column c of a KV head is token c / group,
+  // query head c % group; token t sits at position (keys - s_q + t), bottom-right.
+  int32_t s_q;
+  int64_t q_ss, o_ss;     // token strides of q and o
+  int32_t wr;             // right window edge (0 for causal), < 0 unbounded
   int32_t hpw;            // adjacent KV heads per work group (a power of two)
   float scale_log2, cap_in, cap_out_log2;
   int32_t wl;

@@ -239,11 +239,11 @@ int decode_heads_per_group(int head_dim, int heads_kv) {
 }
 
 int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,
-                    int32_t head_dim, int32_t num_cus) {
+                    int32_t head_dim, int32_t num_cus, int32_t seqlen_q) {
   if (batch <= 0 || seqlen_k <= 0 || heads_kv <= 0 || heads_q <= 0 || num_cus <= 0) return 1;
-  const int64_t group = heads_q / heads_kv;
+  const int64_t cols = (int64_t)(heads_q / heads_kv) * (seqlen_q > 1 ? seqlen_q : 1);
   const int64_t hpw = decode_heads_per_group(head_dim, heads_kv);
-  const int64_t units = (int64_t)batch * ((heads_kv + hpw - 1) / hpw) * ((group + 15) / 16);
+  const int64_t units = (int64_t)batch * ((heads_kv + hpw - 1) / hpw) * ((cols + 15) / 16);
   const int64_t target_wgs = num_cus;  // one work group (two 64 KiB LDS stages) per compute unit
   if (units >= target_wgs) return 1;
   int64_t splits = (target_wgs + units - 1) / units;
@@ -265,14 +265,21 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
   if (st != EXATTN_OK) return st;
   pl->bf16 = a->dtype == EXATTN_BF16;
   pl->head_dim = a->head_dim;
+  if (a->seqlen_q < 0) return fail(EXATTN_E_INVALID, "seqlen_q is negative");
+  pl->s_q = a->seqlen_q > 1 ? a->seqlen_q : 1;
   pl->group = a->heads_q / a->heads_kv;
-  pl->n_hg = (pl->group + 15) / 16;
+  // MFMA query columns per KV head: every query token of every query head of
+  // the group, in groups of 16 (one work group each)
+  const int64_t cols = (int64_t)pl->group * pl->s_q;
+  if (cols > 16 * 4096) return fail(EXATTN_E_UNSUPPORTED, "seqlen_q x (heads_q / heads_kv) above 65536");
+  pl->n_hg = (int)((cols + 15) / 16);
   pl->hpw = decode_heads_per_group(a->head_dim, a->heads_kv);
   pl->n_hk = (a->heads_kv + pl->hpw - 1) / pl->hpw;
   pl->wl = a->window_left < 0 ? -1 : a->window_left;
+  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
   int64_t ns = a->num_splits == 0
                    ? auto_splits(a->batch, a->heads_q, a->heads_kv, a->seqlen_cache, a->head_dim,
-                                 num_cus)
+                                 num_cus, pl->s_q)
                    : a->num_splits;
   const int64_t chunks = (a->seqlen_cache + 31) / 32;
   if (ns > chunks) ns = chunks;
@@ -281,7 +288,7 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
   pl->n_split = (int)ns;
   pl->empty = a->batch == 0;
   if (pl->n_split > 1) {
-    const size_t rows = (size_t)pl->n_split * (size_t)a->batch * (size_t)a->heads_q;
+    const size_t rows = (size_t)pl->n_split * (size_t)a->batch * (size_t)pl->s_q * (size_t)a->heads_q;
     const size_t o_bytes = rows * (size_t)a->head_dim * 4;
     pl->ws_lse_offset = (o_bytes + 255) & ~(size_t)255;
     pl->ws_bytes = (pl->ws_lse_offset + rows * 4 + 255) & ~(size_t)255;
@@ -293,8 +300,9 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
     return fail(EXATTN_E_INVALID, "k_cache or v_cache is NULL");
   if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || !aligned16(a->o))
     return fail(EXATTN_E_INVALID, "q, k_cache, v_cache and o must be 16-byte aligned");
-  const int64_t s2[4] = {a->q_stride[0], a->q_stride[1], a->o_stride[0], a->o_stride[1]};
-  for (int i = 0; i < 4; ++i)
+  const int64_t s2[6] = {a->q_stride[0], a->q_stride[1], a->o_stride[0], a->o_stride[1],
+                         pl->s_q > 1 ? a->q_token_stride : 0, pl->s_q > 1 ? a->o_token_stride : 0};
+  for (int i = 0; i < 6; ++i)
     if (!stride_ok(s2[i]))
       return fail(EXATTN_E_INVALID, "q/o strides must be non-negative multiples of 8 elements");
   for (int i = 0; i < 3; ++i)

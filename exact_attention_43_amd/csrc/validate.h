@@ -52,7 +52,8 @@ struct DecodePlan {
   size_t ws_bytes;
   size_t ws_lse_offset;  // byte offset of the LSE partials inside the workspace
   float scale_log2, cap_in, cap_out_log2;
-  int wl;
+  int wl, wr;   // window edges for the query tokens (wr = 0 for causal); < 0 unbounded
+  int s_q;      // query tokens per batch entry (>= 1)
 };
 
 // Check `a` and fill `plan` for a device with `num_cus` compute units.
@@ -95,6 +96,6 @@ exattn_status check_paged(const exattn_decode_args* a, const DecodePlan& pl, con
 int decode_heads_per_group(int head_dim, int heads_kv);
 
 int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,
-                    int32_t head_dim, int32_t num_cus);
+                    int32_t head_dim, int32_t num_cus, int32_t seqlen_q = 1);
 
 }  // namespace exattn

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define EXATTN_ABI_VERSION 2
+#define EXATTN_ABI_VERSION 3
 
 typedef enum {
   EXATTN_OK = 0,
@@ -125,20 +125,23 @@ typedef struct {
 exattn_status exattn_fwd(const exattn_fwd_args *args, void *stream);
 
 /*
- * KV-cache decode: flash_attn_with_kvcache with seqlen_q = 1 (FAQ Q17), split
- * over the key axis into num_splits parts whose partial results are merged by
- * their log-sum-exp (FAQ Q14; the merge is the online-softmax merge of
- * "FlashAttention完整说明" section 二.1).
+ * KV-cache decode: flash_attn_with_kvcache (FAQ Q17) for one or a few query
+ * tokens, split over the key axis into num_splits parts whose partial results
+ * are merged by their log-sum-exp (FAQ Q14; the merge is the online-softmax
+ * merge of "FlashAttention完整说明" section 二.1).
  *
- * q (batch, 1, heads_q, head_dim) addressed by q_stride (batch, head); o the
- * same by o_stride; k_cache and v_cache (batch, seqlen_cache, heads_kv,
- * head_dim) by k_stride / v_stride (batch, token, head); lse fp32 (batch,
- * heads_q) contiguous, or NULL.
+ * q (batch, seqlen_q, heads_q, head_dim) addressed by q_stride (batch, head)
+ * and q_token_stride; o the same by o_stride and o_token_stride; k_cache and
+ * v_cache (batch, seqlen_cache, heads_kv, head_dim) by k_stride / v_stride
+ * (batch, token, head); lse fp32 (batch, heads_q, seqlen_q) contiguous, or
+ * NULL.  The query tokens of all heads_q / heads_kv query heads of a KV head
+ * share each key read (up to 16 of them per pass over the keys).
  * cache_seqlens: device int32[batch], the number of valid cache rows per batch
  * entry, or NULL for seqlen_cache.  The caller maintains it (FAQ Q17: the call
  * never advances it).  Precondition: 0 <= cache_seqlens[b] <= seqlen_cache.
- * The single query sits at position cache_seqlens[b] - 1 (bottom-right), so
- * causal changes nothing and only window_left narrows the keys.
+ * With one query token it sits at position cache_seqlens[b] - 1
+ * (bottom-right), so causal changes nothing and only window_left narrows the
+ * keys; with seqlen_q > 1 see the field below.
  * num_splits: 0 = automatic (compute-unit count, KV size per split, length);
  * otherwise the number of key ranges, clamped to [1, 256].
  */
@@ -156,6 +159,15 @@ typedef struct {
   int32_t causal;
   int32_t window_left, window_right; /* < 0: unbounded */
   int32_t num_splits;                /* 0: automatic */
+  /* Query tokens per batch entry (0 is taken as 1), e.g. the s_new tokens of
+   * an append (FAQ Q17 with causal) or a few speculative tokens.  Token t sits
+   * at position len - seqlen_q + t of the len = cache_seqlens[b] (+ seqlen_new)
+   * keys, so causal and the window are bottom-right aligned (FAQ Q6, Q21);
+   * a token before position 0 sees no key (O = 0, LSE = -inf).  q and o are
+   * (batch, seqlen_q, heads_q, head_dim) with these token strides (elements,
+   * multiples of 8); lse is (batch, heads_q, seqlen_q) contiguous. */
+  int32_t seqlen_q;
+  int64_t q_token_stride, o_token_stride;
 } exattn_decode_args;
 
 /* Host-only: resolve num_splits and the workspace size (bytes) that

@@ -44,7 +44,7 @@ def test_struct_layout_and_version(L):
     assert L.exattn_args_size(4) == C.sizeof(ex.BwdArgs)
     assert L.exattn_args_size(5) == C.sizeof(ex.Fp8Descale)
     assert L.exattn_args_size(7) == 0
-    assert L.exattn_abi_version() == 2
+    assert L.exattn_abi_version() == 3
     assert L.exattn_status_string(0) == b"EXATTN_OK"
     assert L.exattn_status_string(3) == b"EXATTN_E_WORKSPACE"
 
@@ -121,7 +121,7 @@ def _dec(**kw):
     a.window_left = a.window_right = -1
     a.num_splits = 4
     for key, val in kw.items():
-        if key.endswith("_stride"):
+        if key.endswith("_stride") and isinstance(val, list):
             getattr(a, key)[:] = val
         else:
             setattr(a, key, val)
@@ -142,6 +142,9 @@ BAD_DEC = [
      ex.EXATTN_E_UNSUPPORTED),
     ("token stride past 32-bit tile offsets", dict(k_stride=[1 << 40, 1 << 27, 128]),
      ex.EXATTN_E_UNSUPPORTED),
+    ("negative seqlen_q", dict(seqlen_q=-1), ex.EXATTN_E_INVALID),
+    ("odd query token stride", dict(seqlen_q=3, q_token_stride=4100), ex.EXATTN_E_INVALID),
+    ("too many query columns", dict(seqlen_q=20000), ex.EXATTN_E_UNSUPPORTED),
 ]
 
 
@@ -436,3 +439,16 @@ def test_binding_kvcache_checks():
         ex.attn_with_kvcache(q, kc, kc, lse=_t(2, 16, 1, dtype=torch.float32)[:, ::2])
     with pytest.raises(ValueError, match="lse must be"):
         ex.attn_with_kvcache(q, kc, kc, lse=_t(2, 8, dtype=torch.float32))
+
+
+def test_decode_plan_counts_query_tokens(L):
+    """Several query tokens: the workspace holds partials for every (split, batch, token, head)."""
+    a = _dec(num_splits=4, seqlen_q=3, q_token_stride=32 * 128, o_token_stride=32 * 128)
+    ns, wb = C.c_int32(0), C.c_size_t(0)
+    assert L.exattn_decode_plan(C.byref(a), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK, L.exattn_last_error()
+    rows = 4 * 8 * 3 * 32
+    assert wb.value == ((rows * 128 * 4 + 255) // 256 * 256 + rows * 4 + 255) // 256 * 256
+    # 0 query tokens is taken as 1
+    a1 = _dec(num_splits=4, seqlen_q=0)
+    assert L.exattn_decode_plan(C.byref(a1), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
+    assert wb.value == ((4 * 8 * 32 * 128 * 4 + 255) // 256 * 256 + 4 * 8 * 32 * 4 + 255) // 256 * 256

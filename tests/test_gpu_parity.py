@@ -419,6 +419,72 @@ def test_decode_append_steps():
     assert torch.equal(dkc.cpu(), kc_ref) and torch.equal(dvc.cpu(), vc_ref)
 
 
+MULTI_CASES = [
+    # b, s_cache, h_q, h_kv, d, dtype, lens, s_q, s_new, causal, window, softcap, splits, paged, seed
+    (4, 2048, 32, 8, 128, torch.bfloat16, [0, 5, 1000, 2040], 4, 4, True, (-1, -1), 0.0, 0, 0, 420),   # 16 columns
+    (3, 777, 16, 2, 64, torch.float16, [1, 300, 760], 7, 7, True, (100, -1), 30.0, 0, 0, 421),   # 56 columns
+    (2, 4096, 8, 8, 256, torch.bfloat16, [4000, 17], 2, 0, True, (-1, -1), 0.0, 5, 0, 422),
+    (2, 1000, 16, 4, 128, torch.float16, [996, 0], 3, 1, True, (-1, -1), 0.0, 1, 0, 423),     # s_q != s_new
+    (2, 3000, 32, 8, 128, torch.bfloat16, [3000, 1234], 5, 0, False, (-1, -1), 0.0, 0, 0, 424),  # non-causal
+    (3, 1024, 16, 8, 128, torch.bfloat16, [0, 100, 1000], 5, 5, True, (-1, -1), 0.0, 0, 64, 425),  # paged
+    (2, 512, 8, 2, 128, torch.bfloat16, [2, 300], 4, 0, True, (7, 0), 0.0, 3, 0, 426),   # tokens before key 0
+]
+
+
+@pytest.mark.parametrize("case", MULTI_CASES, ids=[f"q{c[-1]}" for c in MULTI_CASES])
+def test_decode_multi_query(case):
+    """Several query tokens against the KV cache (FAQ Q17 with causal, bottom-right per
+    FAQ Q6): with an append of s_new tokens, token t sits at position
+    cache_seqlens[b] + s_new - s_q + t; O and LSE against the oracle, appended rows
+    bit-exact, and the pool untouched elsewhere when paged."""
+    b, s_cache, hq, hkv, d, dt, lens, s_q, s_new, causal, window, cap, splits, page, seed = case
+    q, kc, vc = W.kvcache(b, s_cache, hq, hkv, d, seed=seed, dtype=dt)
+    q = W.qkv(b, s_q, 1, hq, 1, d, seed=seed + 2000, dtype=dt)[0]
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    dq, dl = _dev(q, lens_t)
+    kw = {}
+    if s_new:
+        kn, vn = W.kv_new(b, s_new, hkv, d, seed=seed + 1000, dtype=dt)
+        kw = dict(k=kn.to(DEV), v=vn.to(DEV))
+    if page:
+        gen = torch.Generator().manual_seed(seed)
+        kp, bt = _to_pages(kc, page, 2, gen)
+        vp, _ = _to_pages(vc, page, 2, torch.Generator().manual_seed(seed))
+        dkc, dvc, dbt = _dev(kp, vp, bt)
+        kw["block_table"] = dbt
+    else:
+        dkc, dvc = _dev(kc, vc)
+    out = _poison_out(q.shape, dt)
+    lse = _poison_lse((b, hq, s_q))
+    ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, causal=causal, window_size=window, softcap=cap,
+                         num_splits=splits, out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    if s_new:
+        o_ref, l_ref, kc_ref, vc_ref = oracle.attention_kvcache_append(q, kc, vc, kn, vn, lens_t, causal=causal,
+                                                                       window_size=window, softcap=cap)
+        got_k = oracle.paged_to_contiguous(dkc.cpu(), bt, s_cache) if page else dkc.cpu()
+        got_v = oracle.paged_to_contiguous(dvc.cpu(), bt, s_cache) if page else dvc.cpu()
+        assert torch.equal(got_k, kc_ref) and torch.equal(got_v, vc_ref)
+    else:
+        o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens_t, causal=causal, window_size=window, softcap=cap)
+    assert_o_close(out, o_ref, dt, f"multi-query {seed}")
+    assert_lse_close(lse, l_ref, f"multi-query {seed}")
+
+
+def test_decode_multi_query_split_independent():
+    """The same multi-token call with 1, 3 and 16 splits agrees with the oracle each time."""
+    q, kc, vc = W.kvcache(2, 2000, 16, 4, 128, seed=427)
+    q = W.qkv(2, 3, 1, 16, 1, 128, seed=428)[0]
+    lens = torch.tensor([2000, 777], dtype=torch.int32)
+    dq, dkc, dvc, dl = _dev(q, kc, vc, lens)
+    o_ref, l_ref = oracle.attention_kvcache(q, kc, vc, lens, causal=True)
+    for ns in (1, 3, 16):
+        out, lse = ex.attn_with_kvcache(dq, dkc, dvc, cache_seqlens=dl, causal=True, num_splits=ns)
+        torch.cuda.synchronize()
+        assert_o_close(out, o_ref, q.dtype, f"splits {ns}")
+        assert_lse_close(lse, l_ref, f"splits {ns}")
+
+
 def _to_pages(cache, page, spare, gen):
     """Scatter a contiguous cache (b, s, h, d) into a pool of pages at a random
     permutation of page slots; returns (pool, block_table)."""
