@@ -263,17 +263,18 @@ def attention_backward(q, k, v, do, *, softmax_scale=None, causal=False, window_
 
 
 def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=False,
-                                  window_size=(-1, -1)):
-    """The size of the terms each gradient of ``attention_backward`` sums (no
-    softcap), for tolerances: a sum whose terms carry a relative rounding
-    error u is off by at most about u times the sum of its terms' absolute
-    values (the classic forward error bound of a dot product), however much
-    the terms cancel.  Written out through the backward's own sums:
-    dS_ij = P_ij (dP_ij - sum_k dO_ik O_ik) has terms of total size
-    A_ij = P_ij (|dP_ij| + sum_k |dO_ik O_ik|), so the magnitudes returned are
-    scale A |K|, scale A^T |Q| and P^T |dO| (dQ, dK, dV), summed over grouped
-    heads like the gradients.  Each is >= the matching |gradient|, with
-    equality for dV where dO >= 0.
+                                  window_size=(-1, -1), softcap=0.0):
+    """The size of the terms each gradient of ``attention_backward`` sums, for
+    tolerances: a sum whose terms carry a relative rounding error u is off by
+    at most about u times the sum of its terms' absolute values (the classic
+    forward error bound of a dot product), however much the terms cancel.
+    Written out through the backward's own sums: dS_ij = P_ij (dP_ij - sum_k
+    dO_ik O_ik) has terms of total size A_ij = P_ij (|dP_ij| + sum_k |dO_ik
+    O_ik|), times the softcap factor 1 - tanh^2(s_raw / c) when softcap c > 0
+    (P then from the capped scores), so the magnitudes returned are scale A |K|,
+    scale A^T |Q| and P^T |dO| (dQ, dK, dV), summed over grouped heads like the
+    gradients.  Each is >= the matching |gradient|, with equality for dV where
+    dO >= 0.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b, s_q, h_q, d = q.shape
@@ -290,10 +291,13 @@ def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=Fal
             hk = _kv_head(h, h_q, h_kv)
             q2, k2, v2, do2 = q[bi, :, h], k[bi, :, hk], v[bi, :, hk], do[bi, :, h]
             _, _, p = attend_head(q2, k2, v2, scale=scale, causal=causal, window_left=wl,
-                                  window_right=wr, return_probs=True)
+                                  window_right=wr, softcap=softcap, return_probs=True)
             dp = do2 @ v2.T
             o2 = p @ v2
             a = p * (np.abs(dp) + np.abs(do2 * o2).sum(axis=1, keepdims=True))
+            if softcap is not None and softcap > 0.0:
+                t = np.tanh(scores(q2, k2, scale) / softcap)
+                a = a * (1.0 - t * t)
             mv[bi, :, hk] += p.T @ np.abs(do2)
             mq[bi, :, h] = scale * (a @ np.abs(k2))
             mk[bi, :, hk] += scale * (a.T @ np.abs(q2))

@@ -566,6 +566,43 @@ def pin_backward_magnitudes():
                     wv[0, j, 0, t] += pr[j] * abs(do[0, i, h, t])
     assert np.allclose(mq, wq, rtol=1e-12, atol=1e-14)
     assert np.allclose(mk, wk, rtol=1e-12, atol=1e-14)
+    # with softcap c: the bound still holds, and on the same tiny case the terms
+    # enumerated in scalar Python (capped scores c tanh(s / c), dS terms times
+    # 1 - tanh^2) match
+    cap = 1.5
+    for causal, win in ((True, (-1, -1)), (False, (2, 1))):
+        q8 = r.standard_normal((2, 7, 4, 8)) * 2
+        k8 = r.standard_normal((2, 9, 2, 8)) * 2
+        v8 = r.standard_normal((2, 9, 2, 8))
+        do8 = r.standard_normal((2, 7, 4, 8))
+        g = oracle.attention_backward(q8, k8, v8, do8, causal=causal, window_size=win, softcap=cap)
+        m = oracle.attention_backward_magnitudes(q8, k8, v8, do8, causal=causal, window_size=win, softcap=cap)
+        for gi, mi in zip(g, m):
+            assert np.all(mi >= np.abs(gi) - 1e-12)
+    mq, mk, mv = oracle.attention_backward_magnitudes(q, k, v, do, softmax_scale=scale, causal=True, softcap=cap)
+    wq = np.zeros_like(mq)
+    wk = np.zeros_like(mk)
+    wv = np.zeros_like(mv)
+    for h in range(2):
+        for i in range(s_q):
+            keys = [j for j in range(s_k) if j <= i + s_k - s_q]
+            raw = {j: scale * math.fsum(q[0, i, h, t] * k[0, j, 0, t] for t in range(d)) for j in keys}
+            sc = {j: cap * math.tanh(raw[j] / cap) for j in keys}
+            top = max(sc.values())
+            z = math.fsum(math.exp(sc[j] - top) for j in keys)
+            pr = {j: math.exp(sc[j] - top) / z for j in keys}
+            o = [math.fsum(pr[j] * v[0, j, 0, t] for j in keys) for t in range(d)]
+            dterms = math.fsum(abs(do[0, i, h, t] * o[t]) for t in range(d))
+            for j in keys:
+                dp = math.fsum(do[0, i, h, t] * v[0, j, 0, t] for t in range(d))
+                a = pr[j] * (abs(dp) + dterms) * (1.0 - math.tanh(raw[j] / cap) ** 2)
+                for t in range(d):
+                    wq[0, i, h, t] += scale * a * abs(k[0, j, 0, t])
+                    wk[0, j, 0, t] += scale * a * abs(q[0, i, h, t])
+                    wv[0, j, 0, t] += pr[j] * abs(do[0, i, h, t])
+    assert np.allclose(mq, wq, rtol=1e-12, atol=1e-14)
+    assert np.allclose(mk, wk, rtol=1e-12, atol=1e-14)
+    assert np.allclose(mv, wv, rtol=1e-12, atol=1e-14)
     assert np.allclose(mv, wv, rtol=1e-12, atol=1e-14)
 
 
