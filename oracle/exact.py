@@ -273,8 +273,8 @@ def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=Fal
     O_ik|), times the softcap factor 1 - tanh^2(s_raw / c) when softcap c > 0
     (P then from the capped scores), so the magnitudes returned are scale A |K|,
     scale A^T |Q| and P^T |dO| (dQ, dK, dV), summed over grouped heads like the
-    gradients.  Each is >= the matching |gradient|, with equality for dV where
-    dO >= 0.
+    gradients (the scale enters by its absolute value: these are sizes).  Each
+    is >= the matching |gradient|, with equality for dV where dO >= 0.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b, s_q, h_q, d = q.shape
@@ -299,8 +299,8 @@ def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=Fal
                 t = np.tanh(scores(q2, k2, scale) / softcap)
                 a = a * (1.0 - t * t)
             mv[bi, :, hk] += p.T @ np.abs(do2)
-            mq[bi, :, h] = scale * (a @ np.abs(k2))
-            mk[bi, :, hk] += scale * (a.T @ np.abs(q2))
+            mq[bi, :, h] = abs(scale) * (a @ np.abs(k2))
+            mk[bi, :, hk] += abs(scale) * (a.T @ np.abs(q2))
     return mq, mk, mv
 
 

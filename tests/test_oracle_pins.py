@@ -535,6 +535,11 @@ def pin_backward_magnitudes():
         m = oracle.attention_backward_magnitudes(q, k, v, do, causal=causal, window_size=win)
         for gi, mi in zip(g, m):
             assert np.all(mi >= np.abs(gi) - 1e-12)
+        # a negative scale: the terms' sizes are the same, the bound still holds
+        gn = oracle.attention_backward(q, k, v, do, causal=causal, window_size=win, softmax_scale=-0.3)
+        mn = oracle.attention_backward_magnitudes(q, k, v, do, causal=causal, window_size=win, softmax_scale=-0.3)
+        for gi, mi in zip(gn, mn):
+            assert np.all(mi >= 0) and np.all(mi >= np.abs(gi) - 1e-12)
         _, _, dv = oracle.attention_backward(q, k, v, np.abs(do), causal=causal, window_size=win)
         _, _, mv = oracle.attention_backward_magnitudes(q, k, v, np.abs(do), causal=causal, window_size=win)
         assert np.allclose(mv, dv, atol=1e-12)
