@@ -102,6 +102,8 @@ class BwdArgs(C.Structure):
         ("dk_stride", C.c_int64 * 3), ("dv_stride", C.c_int64 * 3), ("lse_stride", C.c_int64 * 2),
         ("softmax_scale", C.c_float), ("softcap", C.c_float), ("causal", C.c_int32),
         ("window_left", C.c_int32), ("window_right", C.c_int32),
+        ("cu_seqlens_q", C.c_void_p), ("cu_seqlens_k", C.c_void_p),
+        ("max_seqlen_q", C.c_int32), ("max_seqlen_k", C.c_int32),
     ]
 
 
@@ -559,17 +561,47 @@ def attn_with_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=None, s
     return out, lse
 
 
+def _bwd_call(dout, q, k, v, out, lse, dq, dk, dv, workspace, *, batch, s_q, s_k, h_q, h_kv, d, strides,
+              lse_st, softmax_scale, causal, window_size, softcap, cu_q=None, cu_k=None, max_q=0, max_k=0):
+    a = BwdArgs()
+    a.dtype = _dtype_code(q)
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = batch, s_q, s_k, h_q, h_kv, d
+    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr()
+    a.lse = lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    for name, st in strides.items():
+        getattr(a, f"{name}_stride")[:] = list(st)
+    a.lse_stride[:] = list(lse_st)
+    a.softmax_scale = _scale(softmax_scale)
+    a.softcap = float(softcap or 0.0)
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = _window(window_size)
+    a.cu_seqlens_q = cu_q.data_ptr() if cu_q is not None else None
+    a.cu_seqlens_k = cu_k.data_ptr() if cu_k is not None else None
+    a.max_seqlen_q, a.max_seqlen_k = int(max_q), int(max_k)
+    L = lib()
+    with torch.cuda.device(q.device):
+        wb = C.c_size_t(0)
+        _raise_for(L.exattn_bwd_plan(C.byref(a), C.byref(wb)), "exattn_bwd_plan")
+        ws_ptr, ws_bytes = None, 0
+        if wb.value > 0:
+            if workspace is None:
+                workspace = _workspace(q.device, wb.value)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = L.exattn_bwd(C.byref(a), C.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes,
+                          C.c_void_p(_stream(q.device)))
+    _raise_for(st, "exattn_bwd")
+
+
 def attn_backward(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
                   softcap=0.0, dq=None, dk=None, dv=None, workspace=None):
     """Gradients of attn_func: (dq, dk, dv) for the upstream gradient dout.
 
     q, out, dout (b, s_q, h_q, d); k, v (b, s_k, h_kv, d); lse (b, h_q, s_q) fp32
-    as attn_func returns it; the same scale, causal and window as the forward
-    call.  A KV head's dk and dv sum over the query heads that read it.
-    head_dim 64 or 128, no softcap, fixed lengths.  Deterministic.
+    as attn_func returns it; the same scale, causal, window and softcap as the
+    forward call.  A KV head's dk and dv sum over the query heads that read it.
+    head_dim 64 or 128.  Deterministic.
     """
-    if softcap not in (0, 0.0, None):
-        raise NotImplementedError("the backward does not provide softcap")
     for name, t in (("q", q), ("out", out), ("dout", dout)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be (batch, seqlen, heads, head_dim)")
@@ -592,32 +624,49 @@ def attn_backward(dout, q, k, v, out, lse, softmax_scale=None, causal=False, win
         raise ValueError("dq, dk and dv must have the shapes of q, k and v")
     if len({q.dtype, dq.dtype, dk.dtype, dv.dtype}) != 1:
         raise ValueError("dq, dk and dv must have the dtype of q")
-    a = BwdArgs()
-    a.dtype = _dtype_code(q)
-    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = b, s_q, s_k, h_q, h_kv, d
-    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr()
-    a.lse = lse.data_ptr()
-    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("dout", dout), ("dq", dq), ("dk", dk),
-                    ("dv", dv)):
-        getattr(a, f"{name}_stride")[:] = list(t.stride()[:3])
-    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
-    a.softmax_scale = _scale(softmax_scale)
-    a.softcap = 0.0
-    a.causal = 1 if causal else 0
-    a.window_left, a.window_right = _window(window_size)
-    L = lib()
-    with torch.cuda.device(q.device):
-        wb = C.c_size_t(0)
-        _raise_for(L.exattn_bwd_plan(C.byref(a), C.byref(wb)), "exattn_bwd_plan")
-        ws_ptr, ws_bytes = None, 0
-        if wb.value > 0:
-            if workspace is None:
-                workspace = _workspace(q.device, wb.value)
-            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        st = L.exattn_bwd(C.byref(a), C.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes,
-                          C.c_void_p(_stream(q.device)))
-    _raise_for(st, "exattn_bwd")
+    strides = {name: t.stride()[:3] for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("dout", dout),
+                                                     ("dq", dq), ("dk", dk), ("dv", dv))}
+    _bwd_call(dout, q, k, v, out, lse, dq, dk, dv, workspace, batch=b, s_q=s_q, s_k=s_k, h_q=h_q, h_kv=h_kv,
+              d=d, strides=strides, lse_st=(lse.stride(0), lse.stride(1)), softmax_scale=softmax_scale,
+              causal=causal, window_size=window_size, softcap=softcap)
+    return dq, dk, dv
+
+
+def attn_varlen_backward(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                         softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, dq=None, dk=None,
+                         dv=None, workspace=None):
+    """Gradients of attn_varlen_func (FAQ Q8 packing): q, out, dout (total_q, h_q, d); k, v
+    (total_k, h_kv, d); lse (h_q, total_q) as attn_varlen_func returns it.  Returns (dq, dk, dv)."""
+    for name, t in (("q", q), ("out", out), ("dout", dout), ("k", k), ("v", v)):
+        if t.dim() != 3:
+            raise ValueError(f"varlen {name} must be (total, heads, head_dim)")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have the shape of q")
+    if v.shape != k.shape or k.shape[-1] != q.shape[-1]:
+        raise ValueError("k and v must be (total_k, heads_kv, head_dim)")
+    if len({q.dtype, k.dtype, v.dtype, out.dtype, dout.dtype}) != 1:
+        raise ValueError("q, k, v, out and dout must share one dtype")
+    total_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    if lse.dtype != torch.float32 or lse.shape != (h_q, total_q):
+        raise ValueError("lse must be fp32 (heads_q, total_q)")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold batch + 1 entries")
+    _on_gpu(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
+    _check_last_dim(dout, q, k, v, out, dq, dk, dv)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk and dv must have the shapes of q, k and v")
+    strides = {name: (0, t.stride(0), t.stride(1)) for name, t in
+               (("q", q), ("k", k), ("v", v), ("o", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv))}
+    _bwd_call(dout, q, k, v, out, lse, dq, dk, dv, workspace, batch=cu_seqlens_q.numel() - 1, s_q=0, s_k=0,
+              h_q=h_q, h_kv=h_kv, d=d, strides=strides, lse_st=(0, lse.stride(0)), softmax_scale=softmax_scale,
+              causal=causal, window_size=window_size, softcap=softcap, cu_q=cu_seqlens_q, cu_k=cu_seqlens_k,
+              max_q=max_seqlen_q, max_k=max_seqlen_k)
     return dq, dk, dv
 
 
@@ -627,4 +676,5 @@ def auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus):
 
 
 __all__ = ["attn_func", "attn_func_fp8", "attn_qkvpacked_func", "attn_kvpacked_func", "attn_varlen_func",
-           "attn_with_kvcache", "attn_backward", "decode_plan", "auto_splits", "lib", "library_path"]
+           "attn_with_kvcache", "attn_backward", "attn_varlen_backward", "decode_plan", "auto_splits", "lib",
+           "library_path"]

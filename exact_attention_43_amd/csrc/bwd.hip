@@ -82,13 +82,21 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
   const int i = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
   const int h = blockIdx.y, b = blockIdx.z;
-  const bool in = i < p.s_q;
+  // row i of sequence b: token offsets (varlen) or batch offsets
+  int sq = p.s_q;
+  int64_t ob = (int64_t)b * p.o_sb, db = (int64_t)b * p.do_sb, lb = (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
+  if (p.cu_q != nullptr) {
+    const int qs = p.cu_q[b];
+    sq = p.cu_q[b + 1] - qs;
+    ob = (int64_t)qs * p.o_ss;
+    db = (int64_t)qs * p.do_ss;
+    lb = (int64_t)h * p.lse_sh + qs;
+  }
+  const bool in = i < sq;
   float acc = 0.f;
   if (in) {
-    const u32x4_t a = *(const u32x4_t*)(p.o + (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh +
-                                        8 * part);
-    const u32x4_t g = *(const u32x4_t*)(p.dout + (int64_t)b * p.do_sb + (int64_t)i * p.do_ss +
-                                        (int64_t)h * p.do_sh + 8 * part);
+    const u32x4_t a = *(const u32x4_t*)(p.o + ob + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh + 8 * part);
+    const u32x4_t g = *(const u32x4_t*)(p.dout + db + (int64_t)i * p.do_ss + (int64_t)h * p.do_sh + 8 * part);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc = __builtin_fmaf(lo_f32<BF16>(a[e]), lo_f32<BF16>(g[e]), acc);
@@ -98,7 +106,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (in && part == 0) {
-    const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i];
+    const float lse = p.lse[lb + i];
     f32x2_t st;
     st[0] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
     st[1] = acc;
@@ -106,8 +114,49 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
   }
 }
 
+// Softcap: P = 2^(c log2 e tanh(s scale / c) - LSE log2 e), and the gradient
+// through c tanh(x / c) multiplies dS by 1 - tanh^2.  p_out: P; f_out: that
+// factor (1 without softcap).
+template <bool SOFTCAP>
+__device__ __forceinline__ void probs(float s, float lse2, const BwdParams& p, float& p_out, float& f_out) {
+  if constexpr (SOFTCAP) {
+    const float t = tanh_exp2(s * p.cap_in);
+    p_out = fast_exp2(__builtin_fmaf(t, p.cap_out_log2, -lse2));
+    f_out = 1.0f - t * t;
+  } else {
+    p_out = fast_exp2(__builtin_fmaf(s, p.scale_log2, -lse2));
+    f_out = 1.0f;
+  }
+}
+
+// Token offsets of sequence b (varlen) or its batch offsets, and its lengths.
+struct SeqSpan {
+  int sq, sk;
+  int64_t q, dout, o, dq;  // element offsets of the sequence's first query row
+  int64_t k, v, dk, dv;    // ... and of its first key row
+};
+__device__ __forceinline__ SeqSpan seq_span(const BwdParams& p, int b) {
+  SeqSpan r;
+  if (p.cu_q != nullptr) {
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    r.sq = p.cu_q[b + 1] - qs;
+    r.sk = p.cu_k[b + 1] - ks;
+    r.q = (int64_t)qs * p.q_ss, r.dout = (int64_t)qs * p.do_ss, r.o = (int64_t)qs * p.o_ss;
+    r.dq = (int64_t)qs * p.dq_ss;
+    r.k = (int64_t)ks * p.k_ss, r.v = (int64_t)ks * p.v_ss, r.dk = (int64_t)ks * p.dk_ss;
+    r.dv = (int64_t)ks * p.dv_ss;
+  } else {
+    r.sq = p.s_q, r.sk = p.s_k;
+    r.q = (int64_t)b * p.q_sb, r.dout = (int64_t)b * p.do_sb, r.o = (int64_t)b * p.o_sb;
+    r.dq = (int64_t)b * p.dq_sb;
+    r.k = (int64_t)b * p.k_sb, r.v = (int64_t)b * p.v_sb, r.dk = (int64_t)b * p.dk_sb;
+    r.dv = (int64_t)b * p.dv_sb;
+  }
+  return r;
+}
+
 // dK, dV for 128 keys of one KV head (4 waves x 32 keys).
-template <bool BF16, int D>
+template <bool BF16, int D, bool SOFTCAP>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   using E = Elem<BF16>;
   constexpr int KS = D / 16;                   // k-steps over head_dim
@@ -130,15 +179,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   const int kt = blockIdx.x % n_kt;
   const int hk = (blockIdx.x / n_kt) % p.h_kv;
   const int b = blockIdx.x / (n_kt * p.h_kv);
-  const int sq = p.s_q, sk = p.s_k, off = sk - sq;
+  const SeqSpan sp = seq_span(p, b);
+  const int sq = sp.sq, sk = sp.sk, off = sk - sq;
+  const int sqm = p.s_q;  // row stride of the statistics (the longest sequence)
   const int k0 = kt * kBwdKeys;
+  if (k0 >= sk) return;  // uniform: a shorter sequence has no keys here
   const int kcol = k0 + 32 * wave + l32;  // this lane's key
 
   // ---- K and V of this lane's key as B operands: K[kcol][16 ks + 8 hsel .. +7].
   u32x4_t kf[KS], vf[KS];
   {
-    const uint16_t* kp = p.k + (int64_t)b * p.k_sb + (int64_t)kcol * p.k_ss + (int64_t)hk * p.k_sh + 8 * hsel;
-    const uint16_t* vp = p.v + (int64_t)b * p.v_sb + (int64_t)kcol * p.v_ss + (int64_t)hk * p.v_sh + 8 * hsel;
+    const uint16_t* kp = p.k + sp.k + (int64_t)kcol * p.k_ss + (int64_t)hk * p.k_sh + 8 * hsel;
+    const uint16_t* vp = p.v + sp.v + (int64_t)kcol * p.v_ss + (int64_t)hk * p.v_sh + 8 * hsel;
     const bool in = kcol < sk;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -167,9 +219,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
     q_ofs[i] = (uint32_t)(row * p.q_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
     d_ofs[i] = (uint32_t)(row * p.do_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
   }
-  const uint16_t* const qb_ptr = p.q + (int64_t)b * p.q_sb;
-  const uint16_t* const db_ptr = p.dout + (int64_t)b * p.do_sb;
-  const float* const sb_ptr = p.ws_stats + (int64_t)b * p.h_q * sq * 2;
+  const uint16_t* const qb_ptr = p.q + sp.q;
+  const uint16_t* const db_ptr = p.dout + sp.dout;
+  const float* const sb_ptr = p.ws_stats + (int64_t)b * p.h_q * sqm * 2;
   auto issue = [&](int st, uint8_t* dst) {
     const int h = hk * g + st / nqb;
     const int q0 = (qb_lo + st % nqb) * kBwdRows;
@@ -177,7 +229,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
     const __amdgpu_buffer_rsrc_t rd = block_rsrc<D>(db_ptr + (int64_t)h * p.do_sh, p.do_ss, q0, sq, kBwdRows);
     // the rows' statistics: 32 (lse2, D) pairs, 256 bytes, by lanes 0-15 of wave 0
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(sb_ptr + ((int64_t)h * sq + q0) * 2), 0, 8 * min(kBwdRows, sq - q0), 0x00020000);
+        (void*)(sb_ptr + ((int64_t)h * sqm + q0) * 2), 0, 8 * min(kBwdRows, sq - q0), 0x00020000);
 #pragma unroll
     for (int i = 0; i < SLICES / 4; ++i) {
       buffer_load_lds16(rq, dst + (4 * i + wave) * 1024, q_ofs[i]);
@@ -237,16 +289,19 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
       f32x4_t rs[4];  // rows qi + 2 j, qi + 2 j + 1: (lse2, D, lse2, D)
 #pragma unroll
       for (int j = 0; j < 4; ++j) rs[j] = *(const f32x4_t*)(stats + 2 * (qi + 2 * j));
-      float pv[8], sv[8];
+      float pv[8], sv[8], fv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = fast_exp2(__builtin_fmaf(s[8 * c + u], p.scale_log2, -rs[u >> 1][2 * (u & 1)]));
+      for (int u = 0; u < 8; ++u) probs<SOFTCAP>(s[8 * c + u], rs[u >> 1][2 * (u & 1)], p, pv[u], fv[u]);
       if (!full) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
           if (!visible_key(q0 + qi + u, kcol, sq, sk, off, p.wl, wr)) pv[u] = 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] = pv[u] * (dp[8 * c + u] - rs[u >> 1][2 * (u & 1) + 1]);
+      for (int u = 0; u < 8; ++u) {
+        sv[u] = pv[u] * (dp[8 * c + u] - rs[u >> 1][2 * (u & 1) + 1]);
+        if constexpr (SOFTCAP) sv[u] *= fv[u];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pb[c][e] = E::pack2(pv[2 * e], pv[2 * e + 1]);
@@ -285,8 +340,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
 
   // ---- dK = scale (dK^T)^T, dV = (dV^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3.
   if (kcol < sk) {
-    uint16_t* kq = p.dk + (int64_t)b * p.dk_sb + (int64_t)kcol * p.dk_ss + (int64_t)hk * p.dk_sh;
-    uint16_t* vq = p.dv + (int64_t)b * p.dv_sb + (int64_t)kcol * p.dv_ss + (int64_t)hk * p.dv_sh;
+    uint16_t* kq = p.dk + sp.dk + (int64_t)kcol * p.dk_ss + (int64_t)hk * p.dk_sh;
+    uint16_t* vq = p.dv + sp.dv + (int64_t)kcol * p.dv_ss + (int64_t)hk * p.dv_sh;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -304,7 +359,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
 
 // dQ for 64 query rows of one query head (2 waves x 32 rows; two work groups
 // share a CU, which measured 3% faster than one of 4 waves).
-template <bool BF16, int D, int NG>
+template <bool BF16, int D, int NG, bool SOFTCAP>
 __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdParams p) {
   using E = Elem<BF16>;
   constexpr int BN = dq_keys<NG>();
@@ -333,8 +388,11 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
   const int u = blockIdx.x % units;
   const int b = u / p.h_q, h = u % p.h_q;
   const int hk = h / p.group;
-  const int sq = p.s_q, sk = p.s_k, off = sk - sq;
+  const SeqSpan sp = seq_span(p, b);
+  const int sq = sp.sq, sk = sp.sk, off = sk - sq;
+  const int sqm = p.s_q;  // row stride of the statistics
   const int q0 = qt * kDqRows;
+  if (q0 >= sq) return;  // uniform: a shorter sequence has no rows here
   const int q0w = q0 + 32 * wave;  // this wave's first row
   const int qrow = q0w + l32;
 
@@ -350,8 +408,8 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
   u32x4_t qf[KS], df[KS];
   {
     const bool in = qrow < sq;
-    const uint16_t* qp = p.q + (int64_t)b * p.q_sb + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 8 * hsel;
-    const uint16_t* dp = p.dout + (int64_t)b * p.do_sb + (int64_t)qrow * p.do_ss + (int64_t)h * p.do_sh + 8 * hsel;
+    const uint16_t* qp = p.q + sp.q + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 8 * hsel;
+    const uint16_t* dp = p.dout + sp.dout + (int64_t)qrow * p.do_ss + (int64_t)h * p.do_sh + 8 * hsel;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = in ? *(const u32x4_t*)(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
@@ -360,11 +418,11 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
   }
   f32x2_t rst;  // (lse2, D) of this lane's row
   rst[0] = __builtin_inff(), rst[1] = 0.f;
-  if (qrow < sq) rst = *(const f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * sq + qrow));
+  if (qrow < sq) rst = *(const f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * sqm + qrow));
   const float lse2 = rst[0], drow = rst[1];
 
-  const uint16_t* kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
-  const uint16_t* vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+  const uint16_t* kg = p.k + sp.k + (int64_t)hk * p.k_sh;
+  const uint16_t* vg = p.v + sp.v + (int64_t)hk * p.v_sh;
   uint32_t kofs[KINST], vofs[KINST];
 #pragma unroll
   for (int i = 0; i < KINST; ++i) {
@@ -426,16 +484,19 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
     for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        float sv[8];
+        float sv[8], fv[8];
 #pragma unroll
-        for (int uu = 0; uu < 8; ++uu) sv[uu] = fast_exp2(__builtin_fmaf(s[t2][8 * c + uu], p.scale_log2, -lse2));
+        for (int uu = 0; uu < 8; ++uu) probs<SOFTCAP>(s[t2][8 * c + uu], lse2, p, sv[uu], fv[uu]);
         if (!full) {
 #pragma unroll
           for (int uu = 0; uu < 8; ++uu)
             if (!visible_key(qrow, kb0 + 32 * t2 + 16 * c + 8 * hsel + uu, sq, sk, off, p.wl, p.wr)) sv[uu] = 0.f;
         }
 #pragma unroll
-        for (int uu = 0; uu < 8; ++uu) sv[uu] *= dp[t2][8 * c + uu] - drow;
+        for (int uu = 0; uu < 8; ++uu) {
+          sv[uu] *= dp[t2][8 * c + uu] - drow;
+          if constexpr (SOFTCAP) sv[uu] *= fv[uu];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb[t2][c][e] = E::pack2(sv[2 * e], sv[2 * e + 1]);
       }
@@ -518,7 +579,7 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
 
   // ---- dQ = scale (dQ^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3 of row qrow.
   if (qrow < sq) {
-    uint16_t* op = p.dq + (int64_t)b * p.dq_sb + (int64_t)qrow * p.dq_ss + (int64_t)h * p.dq_sh;
+    uint16_t* op = p.dq + sp.dq + (int64_t)qrow * p.dq_ss + (int64_t)h * p.dq_sh;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -531,7 +592,7 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
   }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool SOFTCAP>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   // A kernel whose grid would be empty is skipped: with no query rows dK and dV
   // are zero (the dK/dV kernel sees no query block), with no keys dQ is zero
@@ -548,7 +609,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   const int n_kt = (p.s_k + kBwdKeys - 1) / kBwdKeys;
   if (n_kt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(n_kt * p.h_kv * p.batch), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, SOFTCAP>), dim3(n_kt * p.h_kv * p.batch), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -558,9 +619,9 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     // Fewer than 1024 tiles leave under two waves per SIMD on 256 CUs: split each
     // tile's key blocks between two wave groups then.
     if (grid < 1024)
-      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2>), dim3(grid), dim3(64 * kDqWaves * 2), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves * 2), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
@@ -568,9 +629,14 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 64) return p.bf16 ? launch_bwd_t<true, 64>(p, stream) : launch_bwd_t<false, 64>(p, stream);
-  if (head_dim == 128) return p.bf16 ? launch_bwd_t<true, 128>(p, stream) : launch_bwd_t<false, 128>(p, stream);
+template <int D, bool SOFTCAP>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  return p.bf16 ? launch_bwd_t<true, D, SOFTCAP>(p, stream) : launch_bwd_t<false, D, SOFTCAP>(p, stream);
+}
+
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool softcap, hipStream_t stream) {
+  if (head_dim == 64) return softcap ? launch_bwd_d<64, true>(p, stream) : launch_bwd_d<64, false>(p, stream);
+  if (head_dim == 128) return softcap ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<128, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -337,17 +337,21 @@ exattn_status exattn_bwd(const exattn_bwd_args* a, void* workspace, size_t works
     p.dv_sb = a->dv_stride[0], p.dv_ss = a->dv_stride[1], p.dv_sh = a->dv_stride[2];
     p.lse_sb = a->lse_stride[0], p.lse_sh = a->lse_stride[1];
     p.batch = a->batch;
-    p.s_q = a->seqlen_q;
-    p.s_k = a->seqlen_k;
+    p.s_q = pl.s_q;
+    p.s_k = pl.s_k;
     p.h_q = a->heads_q;
     p.h_kv = a->heads_kv;
     p.group = pl.group;
     p.scale = pl.scale;
     p.scale_log2 = pl.scale_log2;
+    p.cap_in = pl.cap_in;
+    p.cap_out_log2 = pl.cap_out_log2;
     p.wl = pl.wl;
     p.wr = pl.wr;
     p.bf16 = pl.bf16 ? 1 : 0;
-    hipError_t e = launch_bwd(p, pl.head_dim, static_cast<hipStream_t>(stream));
+    p.cu_q = pl.varlen ? a->cu_seqlens_q : nullptr;
+    p.cu_k = pl.varlen ? a->cu_seqlens_k : nullptr;
+    hipError_t e = launch_bwd(p, pl.head_dim, pl.softcap, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("backward launch: ") + hipGetErrorString(e));
     return EXATTN_OK;
   } catch (...) {

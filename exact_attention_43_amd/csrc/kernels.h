@@ -113,8 +113,14 @@ struct BwdParams {
   int64_t lse_sb, lse_sh;
   int32_t batch, s_q, s_k, h_q, h_kv, group;
   float scale, scale_log2;
+  float cap_in, cap_out_log2;  // softcap: scale / c and c log2 e (0 without softcap)
   int32_t wl, wr;  // wr = 0 for causal; < 0 unbounded
   int32_t bf16;
+  // Varlen (cu_q != nullptr): sequence b spans rows cu_q[b] .. cu_q[b+1] - 1 of
+  // q / o / dout / dq and cu_k[b] .. cu_k[b+1] - 1 of k / v / dk / dv (batch
+  // strides ignored); s_q / s_k are the largest lengths.  LSE is (h_q, total_q).
+  const int32_t* cu_q;
+  const int32_t* cu_k;
 };
 
 int prefill_rows_per_tile();
@@ -128,6 +134,6 @@ hipError_t launch_decode(const DecParams& p, bool bf16, int head_dim, bool softc
 constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
 // Device address of the current device's scratch array (looked up once per device).
 hipError_t decode_scratch(void** ptr);
-hipError_t launch_bwd(const BwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool softcap, hipStream_t stream);
 
 }  // namespace exattn

@@ -346,12 +346,23 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
   if (st != EXATTN_OK) return st;
   if (a->head_dim == 256)
     return fail(EXATTN_E_UNSUPPORTED, "the backward provides head_dim 64 and 128");
-  if (a->seqlen_q < 0 || a->seqlen_k < 0) return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k is negative");
+  const bool varlen = a->cu_seqlens_q != nullptr;
+  if (varlen != (a->cu_seqlens_k != nullptr))
+    return fail(EXATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+  // lengths (fixed) or the largest sequence (varlen), which size the grids
+  const int32_t s_q = varlen ? a->max_seqlen_q : a->seqlen_q;
+  const int32_t s_k = varlen ? a->max_seqlen_k : a->seqlen_k;
+  if (s_q < 0 || s_k < 0) return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k (or their maxima) is negative");
   float scale_log2, cap_in, cap_out;
   bool cap;
   st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &scale_log2, &cap_in, &cap_out, &cap);
   if (st != EXATTN_OK) return st;
-  if (cap) return fail(EXATTN_E_UNSUPPORTED, "the backward does not provide softcap");
+  pl->softcap = cap;
+  pl->cap_in = cap_in;
+  pl->cap_out_log2 = cap_out;
+  pl->varlen = varlen;
+  pl->s_q = s_q;
+  pl->s_k = s_k;
   pl->bf16 = a->dtype == EXATTN_BF16;
   pl->head_dim = a->head_dim;
   pl->group = a->heads_q / a->heads_kv;
@@ -359,14 +370,12 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
   pl->scale = scale_log2 / kLog2eHost;
   pl->wl = a->window_left < 0 ? -1 : a->window_left;
   pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
-  const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)a->seqlen_q;
+  const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)s_q;
   pl->ws_bytes = (rows * 8 + 255) & ~(size_t)255;  // (LSE log2 e, dO . O) per row
-  pl->empty = a->batch == 0 || (a->seqlen_q == 0 && a->seqlen_k == 0);
+  pl->empty = a->batch == 0 || (s_q == 0 && s_k == 0);
   if (pl->empty) return EXATTN_OK;
   const void* ptrs[9] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse};
-  const bool need[9] = {a->seqlen_q > 0, a->seqlen_k > 0, a->seqlen_k > 0, a->seqlen_q > 0,
-                        a->seqlen_q > 0, a->seqlen_q > 0, a->seqlen_k > 0, a->seqlen_k > 0,
-                        a->seqlen_q > 0};
+  const bool need[9] = {s_q > 0, s_k > 0, s_k > 0, s_q > 0, s_q > 0, s_q > 0, s_k > 0, s_k > 0, s_q > 0};
   for (int i = 0; i < 9; ++i) {
     if (need[i] && ptrs[i] == nullptr)
       return fail(EXATTN_E_INVALID, "q, k, v, o, dout, lse, dq, dk and dv must not be NULL");
@@ -377,10 +386,11 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
   const int64_t* strides[8] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride,
                                a->dout_stride, a->dq_stride, a->dk_stride, a->dv_stride};
   for (int t = 0; t < 8; ++t)
-    for (int i = 0; i < 3; ++i)
+    for (int i = varlen ? 1 : 0; i < 3; ++i)
       if (!stride_ok(strides[t][i]))
         return fail(EXATTN_E_INVALID, "backward strides must be non-negative multiples of 8 elements");
-  if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides are negative");
+  if (a->lse_stride[1] < 0 || (!varlen && a->lse_stride[0] < 0))
+    return fail(EXATTN_E_INVALID, "lse strides are negative");
   // Q and dO tiles of 32 rows, K and V tiles of up to 64 keys, one head each.
   const char* bn[5] = {"q", "k", "v", "o", "dout"};
   for (int t = 0; t < 5; ++t) {

@@ -74,6 +74,9 @@ exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d
 // Checked backward arguments, resolved for the launch.
 struct BwdPlan {
   bool bf16 = false;
+  bool softcap = false, varlen = false;
+  float cap_in = 0.f, cap_out_log2 = 0.f;
+  int s_q = 0, s_k = 0;  // lengths, or the largest ones (varlen)
   bool empty = false;  // nothing to compute (batch 0 or no query rows and no keys)
   int head_dim = 0, group = 1, wl = -1, wr = -1;
   float scale = 0.f, scale_log2 = 0.f;

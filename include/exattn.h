@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define EXATTN_ABI_VERSION 3
+#define EXATTN_ABI_VERSION 4
 
 typedef enum {
   EXATTN_OK = 0,
@@ -260,14 +260,17 @@ exattn_status exattn_decode_paged(const exattn_decode_args *args, const exattn_p
  * Backward of the dense forward: dQ, dK, dV from Q, K,
  * V, the forward's O and LSE, and the upstream gradient dO, recomputing S and
  * P ("FlashAttention完整说明", section 二.2: only O and the softmax statistics
- * are kept).  Same layouts and masks as exattn_fwd for fixed lengths
- * (element strides over batch, token, head; head_dim contiguous); dq like q,
- * dk and dv like k and v; lse as exattn_fwd writes it (fp32, element (b, h, i)
- * at lse[b * lse_stride[0] + h * lse_stride[1] + i]).  A KV head's dK and dV
- * sum over the query heads that read it.  Deterministic (no atomics).
- * Provided: head_dim 64 and 128, no softcap, fixed lengths; other cases return
- * EXATTN_E_UNSUPPORTED.  workspace: batch * heads_q * seqlen_q * 8 bytes rounded
- * up to 256 (exattn_bwd_plan), 256-byte aligned, scratch owned by the caller.
+ * are kept).  Same layouts, masks and softcap as exattn_fwd, fixed length or
+ * varlen (element strides over batch, token, head; head_dim contiguous); dq
+ * like q, dk and dv like k and v; lse as exattn_fwd writes it (fp32, element
+ * (b, h, i) at lse[b * lse_stride[0] + h * lse_stride[1] + i]; varlen i is the
+ * packed token).  With softcap c the gradient flows through c tanh(s / c)
+ * (FAQ Q22), i.e. dS is multiplied by 1 - tanh^2.  A KV head's dK and dV sum
+ * over the query heads that read it.  Deterministic (no atomics).
+ * Provided: head_dim 64 and 128; head_dim 256 returns EXATTN_E_UNSUPPORTED.
+ * workspace: batch * heads_q * seqlen_q (varlen: max_seqlen_q) * 8 bytes
+ * rounded up to 256 (exattn_bwd_plan), 256-byte aligned, scratch owned by the
+ * caller.
  * Errors (nothing launched): EXATTN_E_INVALID for NULL or misaligned pointers,
  * negative sizes or strides that are not non-negative multiples of 8 elements;
  * EXATTN_E_UNSUPPORTED as above; EXATTN_E_WORKSPACE for a missing, short or
@@ -284,9 +287,16 @@ typedef struct {
   int64_t dq_stride[3], dk_stride[3], dv_stride[3];
   int64_t lse_stride[2];
   float softmax_scale; /* NaN: 1/sqrt(head_dim); else as given */
-  float softcap;       /* must be <= 0 (off) */
+  float softcap;       /* <= 0: off; > 0 as in the forward */
   int32_t causal;
   int32_t window_left, window_right;
+  /* Varlen (both non-NULL): int32 device arrays of batch + 1 prefix sums as
+   * for exattn_fwd; q, o, dout, dq are (total_q, heads_q, head_dim), k, v, dk,
+   * dv (total_k, heads_kv, head_dim), the batch strides are ignored, lse is
+   * (heads_q, total_q) as exattn_fwd writes it, and max_seqlen_q /
+   * max_seqlen_k bound every sequence (they size the grids). */
+  const int32_t *cu_seqlens_q, *cu_seqlens_k;
+  int32_t max_seqlen_q, max_seqlen_k;
 } exattn_bwd_args;
 
 /* Host-only: the workspace size (bytes) exattn_bwd needs for these arguments. */

@@ -44,7 +44,7 @@ def test_struct_layout_and_version(L):
     assert L.exattn_args_size(4) == C.sizeof(ex.BwdArgs)
     assert L.exattn_args_size(5) == C.sizeof(ex.Fp8Descale)
     assert L.exattn_args_size(7) == 0
-    assert L.exattn_abi_version() == 3
+    assert L.exattn_abi_version() == 4
     assert L.exattn_status_string(0) == b"EXATTN_OK"
     assert L.exattn_status_string(3) == b"EXATTN_E_WORKSPACE"
 
@@ -317,8 +317,9 @@ BAD_BWD = [
     ("dtype", dict(dtype=3), ex.EXATTN_E_UNSUPPORTED),
     ("head_dim 256", dict(head_dim=256), ex.EXATTN_E_UNSUPPORTED),
     ("head_dim 80", dict(head_dim=80), ex.EXATTN_E_UNSUPPORTED),
-    ("softcap", dict(softcap=30.0), ex.EXATTN_E_UNSUPPORTED),
     ("heads ratio", dict(heads_q=3), ex.EXATTN_E_INVALID),
+    ("half varlen", dict(cu_seqlens_q=FAKE), ex.EXATTN_E_INVALID),
+    ("negative max seqlen", dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=-1), ex.EXATTN_E_INVALID),
     ("negative seqlen", dict(seqlen_q=-1), ex.EXATTN_E_INVALID),
     ("null dout", dict(dout=None), ex.EXATTN_E_INVALID),
     ("null dk", dict(dk=None), ex.EXATTN_E_INVALID),
@@ -452,3 +453,13 @@ def test_decode_plan_counts_query_tokens(L):
     a1 = _dec(num_splits=4, seqlen_q=0)
     assert L.exattn_decode_plan(C.byref(a1), C.byref(ns), C.byref(wb)) == ex.EXATTN_OK
     assert wb.value == ((4 * 8 * 32 * 128 * 4 + 255) // 256 * 256 + 4 * 8 * 32 * 4 + 255) // 256 * 256
+
+
+def test_bwd_accepts_softcap_and_varlen_plans(L):
+    """Softcap and packed sequences are provided: their plans succeed; the varlen workspace
+    is sized by the longest sequence."""
+    wb = C.c_size_t(0)
+    assert L.exattn_bwd_plan(C.byref(_bwd(softcap=30.0)), C.byref(wb)) == ex.EXATTN_OK, L.exattn_last_error()
+    a = _bwd(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=77, max_seqlen_k=300)
+    assert L.exattn_bwd_plan(C.byref(a), C.byref(wb)) == ex.EXATTN_OK, L.exattn_last_error()
+    assert wb.value == (2 * 4 * 77 * 8 + 255) // 256 * 256

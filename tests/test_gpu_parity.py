@@ -631,6 +631,68 @@ def test_backward(case):
     assert_grad_close(gv, rv, mv, dt, "dv")
 
 
+BWD_CAP_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, dtype, causal, window, softcap, scale, seed
+    (2, 200, 200, 4, 4, 128, torch.bfloat16, True, (-1, -1), 30.0, None, 230),
+    (1, 130, 300, 8, 2, 64, torch.float16, False, (-1, -1), 5.0, None, 231),
+    (1, 300, 300, 2, 2, 128, torch.bfloat16, False, (50, 10), 2.0, None, 232),   # saturating cap
+    (2, 257, 100, 4, 1, 128, torch.float16, True, (-1, -1), 20.0, -0.09, 233),   # negative scale, empty rows
+    (1, 1024, 1024, 16, 16, 128, torch.bfloat16, True, (-1, -1), 50.0, None, 234),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CAP_CASES, ids=[f"c{c[-1]}" for c in BWD_CAP_CASES])
+def test_backward_softcap(case):
+    """The backward through the softcap (FAQ Q22: c tanh(s / c) before the mask) against the
+    oracle's gradients, which differentiate through the cap."""
+    b, sq, sk, hq, hkv, d, dt, causal, window, cap, scale, seed = case
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=seed, dtype=dt)
+    if cap <= 2.0:
+        q, k = (q.float() * 3).to(dt), (k.float() * 3).to(dt)
+    dout = W.qkv(b, sq, 1, hq, 1, d, seed=seed + 1000, dtype=dt)[0]
+    dq_, dk_, dv_, ddo = _dev(q, k, v, dout)
+    kw = dict(causal=causal, window_size=window, softcap=cap, softmax_scale=scale)
+    out, lse = ex.attn_func(dq_, dk_, dv_, **kw)
+    gq, gk, gv = ex.attn_backward(ddo, dq_, dk_, dv_, out, lse, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, dout, **kw)
+    mq, mk, mv = oracle.attention_backward_magnitudes(q, k, v, dout, **kw)
+    assert_grad_close(gq, rq, mq, dt, "dq")
+    assert_grad_close(gk, rk, mk, dt, "dk")
+    assert_grad_close(gv, rv, mv, dt, "dv")
+
+
+@pytest.mark.parametrize("causal,window,cap", [(True, (-1, -1), 0.0), (False, (40, 7), 0.0),
+                                               (True, (256, 0), 50.0)])
+def test_backward_varlen(causal, window, cap):
+    """Packed sequences (FAQ Q8), ragged and empty ones included: each sequence's gradients
+    against the oracle's on that sequence alone."""
+    lens_q = [1, 0, 300, 129, 64, 77]
+    lens_k = [5, 3, 300, 1, 300, 77]
+    hq, hkv, d = 8, 2, 128
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, hq, hkv, d, seed=235)
+    dout = W.varlen_qkv(lens_q, [1] * len(lens_q), hq, 1, d, seed=236)[0]
+    dq_, dk_, dv_, dcq, dck, ddo = _dev(q, k, v, cu_q, cu_k, dout)
+    kw = dict(causal=causal, window_size=window, softcap=cap)
+    out, lse = ex.attn_varlen_func(dq_, dk_, dv_, dcq, dck, max(lens_q), max(lens_k), **kw)
+    gq = torch.full_like(dq_, float("nan"))
+    gk = torch.full_like(dk_, float("nan"))
+    gv = torch.full_like(dv_, float("nan"))
+    ex.attn_varlen_backward(ddo, dq_, dk_, dv_, out, lse, dcq, dck, max(lens_q), max(lens_k), dq=gq, dk=gk,
+                            dv=gv, **kw)
+    torch.cuda.synchronize()
+    gq, gk, gv = gq.cpu(), gk.cpu(), gv.cpu()
+    for i in range(len(lens_q)):
+        a, e = int(cu_q[i]), int(cu_q[i + 1])
+        ka, ke = int(cu_k[i]), int(cu_k[i + 1])
+        qs, ks, vs, ds = q[None, a:e], k[None, ka:ke], v[None, ka:ke], dout[None, a:e]
+        rq, rk, rv = oracle.attention_backward(qs, ks, vs, ds, **kw)
+        mq, mk, mv = oracle.attention_backward_magnitudes(qs, ks, vs, ds, **kw)
+        assert_grad_close(gq[None, a:e], rq, mq, q.dtype, f"seq {i} dq")
+        assert_grad_close(gk[None, ka:ke], rk, mk, q.dtype, f"seq {i} dk")
+        assert_grad_close(gv[None, ka:ke], rv, mv, q.dtype, f"seq {i} dv")
+
+
 @pytest.mark.parametrize("s_q,s_k", [(0, 50), (40, 0)])
 def test_backward_empty_side(s_q, s_k):
     """No query rows: dK = dV = 0; no keys: dQ = 0 (the buffers start as NaN)."""
