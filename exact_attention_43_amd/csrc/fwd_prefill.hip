@@ -113,31 +113,42 @@ prefill_kernel(const FwdParams p) {
   // Packed GQA (p.pack): a unit is one KV head, and its tiles hold the rows of
   // all `group` query heads that read it, head fastest: virtual row R is
   // position R / group of query head hk * group + R % group.  Unpacked, a unit
-  // is one query head and virtual row R is position R.
+  // is one query head and virtual row R is position R.  Work groups are
+  // dispatched (and spread over the XCDs, work group id modulo 8) in linear
+  // order, x fastest; a three-dimensional grid (unit, batch, tile) gives that
+  // same order without the integer divisions of a linear id, which cost a few
+  // hundred scalar instructions ahead of the first load.
   const bool pack = p.pack != 0;
   const int G = pack ? p.group : 1;
-  const int units = p.batch * (pack ? p.h_kv : p.h_q);
-  const int bid = blockIdx.x;
-  const int qt = p.n_qt - 1 - bid / units;
-  const int u = bid % units;
-  int b, h;
-  if (pack) {
-    b = u / p.h_kv;
-    h = (u % p.h_kv) * p.group;  // the group's first query head
-  } else if (p.xcd_group) {
-    // u % 8 picks the XCD; it depends only on the KV unit, so the query heads
-    // sharing one K/V also share one L2.
-    const int x = u & 7;
-    const int rest = u >> 3;
-    const int j = rest % p.group;
-    const int kvu = (rest / p.group) * 8 + x;
-    b = kvu / p.h_kv;
-    h = (kvu % p.h_kv) * p.group + j;
+  int qt, b, h, hk;
+  if (p.grid3 != 0) {
+    qt = p.n_qt - 1 - (int)blockIdx.z;
+    b = blockIdx.y;
+    h = pack ? (int)blockIdx.x * p.group : (int)blockIdx.x;  // packed: the group's first query head
+    hk = pack || p.group == 1 ? (int)blockIdx.x : h / p.group;
   } else {
-    b = u / p.h_q;
-    h = u % p.h_q;
+    const int units = p.batch * (pack ? p.h_kv : p.h_q);
+    const int bid = blockIdx.x;
+    qt = p.n_qt - 1 - bid / units;
+    const int u = bid % units;
+    if (pack) {
+      b = u / p.h_kv;
+      h = (u % p.h_kv) * p.group;
+    } else if (p.xcd_group) {
+      // u % 8 picks the XCD; it depends only on the KV unit, so the query heads
+      // sharing one K/V also share one L2.
+      const int x = u & 7;
+      const int rest = u >> 3;
+      const int j = rest % p.group;
+      const int kvu = (rest / p.group) * 8 + x;
+      b = kvu / p.h_kv;
+      h = (kvu % p.h_kv) * p.group + j;
+    } else {
+      b = u / p.h_q;
+      h = u % p.h_q;
+    }
+    hk = h / p.group;
   }
-  const int hk = h / p.group;
   // Virtual row -> position and head offset.  Rows divide through a float
   // reciprocal, exact after the +-1 correction for rows below 2^22 (the host
   // limits packed launches to that); unpacked rows are positions.
@@ -188,6 +199,22 @@ prefill_kernel(const FwdParams p) {
   const int q0 = 64 * (my_a ? tile_a : tile_b);   // first row of this wave's tile
   const int q_last = min(q0 + 64, sqv) - 1;
 
+  // ---- Q^T fragments: lane holds Q[row][16 ks + 8 hsel .. +7] for every ks.
+  // Issued first: the burst of Q reads from memory is the longest wait of the
+  // prologue, and everything up to the loop except the first KV DMA can be
+  // computed under it.
+  const int qrow = q0 + 32 * (wg & 1) + l32;  // virtual row of this lane
+  const int qpos = vpos(qrow);                 // its position
+  const int qhead = h + vhead(qrow);           // its query head
+  u32x4_t qf[KS];
+  if (my_valid && qrow < sqv) {
+    const uint16_t* qp = p.q + qoff + (int64_t)qhead * p.q_sh + (int64_t)qpos * p.q_ss + 8 * hsel;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
+  }
   const uint16_t* kg = p.k + koff + (int64_t)hk * p.k_sh;
   const uint16_t* vg = p.v + voff + (int64_t)hk * p.v_sh;
 
@@ -222,22 +249,38 @@ prefill_kernel(const FwdParams p) {
   const int w_lo = my_a ? a_lo : b_lo;                    // this wave's blocks
   const int w_hi = my_valid ? (my_a ? a_hi : b_hi) : 0;
 
-  // ---- Q^T fragments: lane holds Q[row][16 ks + 8 hsel .. +7] for every ks.
-  const int qrow = q0 + 32 * (wg & 1) + l32;  // virtual row of this lane
-  const int qpos = vpos(qrow);                 // its position
-  const int qhead = h + vhead(qrow);           // its query head
-  u32x4_t qf[KS];
-  if (my_valid && qrow < sqv) {
-    const uint16_t* qp = p.q + qoff + (int64_t)qhead * p.q_sh + (int64_t)qpos * p.q_ss + 8 * hsel;
+  // ---- K and V straight into LDS by DMA: wave wg of the group, instruction i
+  // fills 1 KiB slice 4 i + wg; lane l writes slot l = (row l / DCH of the
+  // slice, stored chunk l % DCH), so it fetches global chunk (l % DCH) ^
+  // swizzle(row).  Lane offsets are loop-invariant bytes (token strides are
+  // checked on the host).
+  uint32_t kofs_ld[KINST], vofs_ld[KINST];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
+  for (int i = 0; i < KINST; ++i) {
+    const int row = (4 * i + wg) * ROWS_PER_KB + lane / DCH;
+    kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
+    vofs_ld[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ vswz<D>(row))) * 2u;
   }
-  if (p.q_sign != 0u) {  // negative softmax scale: negate Q exactly, use |scale|
+  auto issue_k = [&](int n, uint8_t* kdst) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] ^= u32x4_t{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
+    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rk, kdst + (4 * i + wg) * 1024, kofs_ld[i]);
+  };
+  auto issue_v = [&](int n, uint8_t* vdst) {
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
+#pragma unroll
+    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rv, vdst + (4 * i + wg) * 1024, vofs_ld[i]);
+  };
+  uint8_t* const k0 = gsm;
+  uint8_t* const k1 = gsm + KTILE;
+  uint8_t* const v0 = gsm + 2 * KTILE;
+  uint8_t* const v1 = gsm + 2 * KTILE + VTILE;
+  // The first block of the group: K and V (plain loop) or K only (the
+  // software-pipelined loop loads V(b_i) in step i).
+  constexpr bool kPipelined = NG == 1 && D == 128 && !SOFTCAP;
+  if (n_lo + grp < n_hi) {
+    issue_k(n_lo + grp, k0);
+    if constexpr (!kPipelined) issue_v(n_lo + grp, v0);
   }
 
   // ---- loop-invariant LDS addresses.
@@ -271,28 +314,6 @@ prefill_kernel(const FwdParams p) {
       vtr[half][dt] = key * (D * 2) + 16 * ((dcol >> 3) ^ vswz<D>(key)) + 2 * (dcol & 7);
     }
 
-  // ---- K and V straight into LDS by DMA: wave wg of the group, instruction i
-  // fills 1 KiB slice 4 i + wg; lane l writes slot l = (row l / DCH of the
-  // slice, stored chunk l % DCH), so it fetches global chunk (l % DCH) ^
-  // swizzle(row).  Lane offsets are loop-invariant bytes (token strides are
-  // checked on the host).
-  uint32_t kofs_ld[KINST], vofs_ld[KINST];
-#pragma unroll
-  for (int i = 0; i < KINST; ++i) {
-    const int row = (4 * i + wg) * ROWS_PER_KB + lane / DCH;
-    kofs_ld[i] = (uint32_t)(row * p.k_ss + 8 * ((lane % DCH) ^ kswz<D>(row))) * 2u;
-    vofs_ld[i] = (uint32_t)(row * p.v_ss + 8 * ((lane % DCH) ^ vswz<D>(row))) * 2u;
-  }
-  auto issue_k = [&](int n, uint8_t* kdst) {
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kg, p.k_ss, n * BN, sk, BN);
-#pragma unroll
-    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rk, kdst + (4 * i + wg) * 1024, kofs_ld[i]);
-  };
-  auto issue_v = [&](int n, uint8_t* vdst) {
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vg, p.v_ss, n * BN, sk, BN);
-#pragma unroll
-    for (int i = 0; i < KINST; ++i) buffer_load_lds16(rv, vdst + (4 * i + wg) * 1024, vofs_ld[i]);
-  };
   // The partner wave's share (slices 4 i + (wg ^ 2): the other tile's wave of
   // the group), issued together with this wave's own share in steps where
   // only the partner has a block to compute.
@@ -467,27 +488,27 @@ prefill_kernel(const FwdParams p) {
                                      pf[t2][c], oacc[dt]);
   };
 
-  uint8_t* const k0 = gsm;
-  uint8_t* const k1 = gsm + KTILE;
-  uint8_t* const v0 = gsm + 2 * KTILE;
-  uint8_t* const v1 = gsm + 2 * KTILE + VTILE;
   const int nblk = n_hi - n_lo;
   const int steps = (nblk + NG - 1) / NG;
   // group g works on blocks b_i = n_lo + g + NG i, i < nb
   const int nb = nblk > grp ? (nblk - grp + NG - 1) / NG : 0;
   auto blk = [&](int i) { return n_lo + grp + NG * i; };
   auto active = [&](int i) { return blk(i) >= w_lo && blk(i) < w_hi; };  // uniform per wave
-  // Consume Q after the first DMA is on its way (in each branch, so that each
-  // path waits only for the Q loads): the compiler then waits for them before
-  // the loop.  Otherwise it cannot tell that the loop's own waits covered them
-  // and waits inside every step for all newer loads, the next block's
+  // Consume Q (and apply the sign of a negative scale) just before the loop,
+  // after the first DMA is on its way: the compiler then waits for the Q loads
+  // only, once.  Otherwise it cannot tell that the loop's own waits covered
+  // them and waits inside every step for all newer loads, the next block's
   // prefetch included.
   auto pin_q = [&] {
+    if (p.q_sign != 0u) {  // negative softmax scale: negate Q exactly, use |scale|
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] ^= u32x4_t{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   };
 
-  if constexpr (NG == 1 && D == 128 && !SOFTCAP) {
+  if constexpr (kPipelined) {
     // ---- software-pipelined loop (one group: large grids).  Step i computes
     // S(b_i) = K(b_i) Q^T and, with the exponentials of S(b_{i-1}) issued
     // between those MFMAs, the softmax and O += P V of b_{i-1}.  One SIMD
@@ -566,12 +587,7 @@ prefill_kernel(const FwdParams p) {
         if (kb + BN - 1 > full_r || kb < full_l) mask_keys(sn, mhi - kb, mlo - kb);
       }
     };
-    if (nb > 0) {
-      issue_k(blk(0), k0);
-      pin_q();
-    } else {
-      pin_q();
-    }
+    pin_q();
     f32x16_t sa[NT2], sb[NT2];
     // Unrolled by two so each call sees fixed stages and score registers.
     // Before each step: K(b_i) and V(b_{i-1}) have landed, and every wave is
@@ -634,13 +650,7 @@ prefill_kernel(const FwdParams p) {
         issue_v(n + NG, vn);
       }
     };
-    if (n_lo + grp < n_hi) {
-      issue_k(n_lo + grp, k0);
-      issue_v(n_lo + grp, v0);
-      pin_q();
-    } else {
-      pin_q();
-    }
+    pin_q();
     int i = 0;
     for (; i + 1 < steps; i += 2) {
       const int n = n_lo + NG * i + grp;
@@ -764,19 +774,19 @@ prefill_kernel(const FwdParams p) {
 }
 
 template <bool BF16, int D, bool SOFTCAP, int NG>
-void launch_s(const FwdParams& p, int grid, hipStream_t stream) {
+void launch_s(const FwdParams& p, dim3 grid, hipStream_t stream) {
   const dim3 block(256 * NG);
   if constexpr (NG == 2) {
     if (p.pair_tiles != 0) {
-      hipLaunchKernelGGL((prefill_kernel<BF16, D, SOFTCAP, 2, true>), dim3(grid), block, 0, stream, p);
+      hipLaunchKernelGGL((prefill_kernel<BF16, D, SOFTCAP, 2, true>), grid, block, 0, stream, p);
       return;
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<BF16, D, SOFTCAP, NG, false>), dim3(grid), block, 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<BF16, D, SOFTCAP, NG, false>), grid, block, 0, stream, p);
 }
 
 template <bool BF16, int D, int NG>
-hipError_t launch_g(const FwdParams& p, bool softcap, int grid, hipStream_t stream) {
+hipError_t launch_g(const FwdParams& p, bool softcap, dim3 grid, hipStream_t stream) {
   if (softcap)
     launch_s<BF16, D, true, NG>(p, grid, stream);
   else
@@ -785,7 +795,7 @@ hipError_t launch_g(const FwdParams& p, bool softcap, int grid, hipStream_t stre
 }
 
 template <bool BF16>
-hipError_t launch_t(const FwdParams& p, int head_dim, bool softcap, int grid, int groups,
+hipError_t launch_t(const FwdParams& p, int head_dim, bool softcap, dim3 grid, int groups,
                     hipStream_t stream) {
   switch (head_dim) {
     case 64:
@@ -803,10 +813,16 @@ hipError_t launch_t(const FwdParams& p, int head_dim, bool softcap, int grid, in
 
 int prefill_rows_per_tile() { return kBM; }
 
-hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,
+hipError_t launch_prefill(const FwdParams& p_in, bool bf16, int head_dim, bool softcap, int grid,
                           int groups, hipStream_t stream) {
-  return bf16 ? launch_t<true>(p, head_dim, softcap, grid, groups, stream)
-              : launch_t<false>(p, head_dim, softcap, grid, groups, stream);
+  // (unit, batch, tile) grid where the dimensions allow it; the XCD-grouped
+  // GQA order and grids past the y / z limits index a linear grid.
+  FwdParams p = p_in;
+  const int upb = p.pack ? p.h_kv : p.h_q;  // units per batch entry
+  p.grid3 = !p.xcd_group && p.batch <= 65535 && p.n_qt <= 65535 ? 1 : 0;
+  const dim3 g = p.grid3 ? dim3(upb, p.batch, p.n_qt) : dim3(grid);
+  return bf16 ? launch_t<true>(p, head_dim, softcap, g, groups, stream)
+              : launch_t<false>(p, head_dim, softcap, g, groups, stream);
 }
 
 }  // namespace exattn

@@ -32,6 +32,7 @@ struct FwdParams {
   int32_t wl, wr;      // window; wr = 0 for causal; < 0 unbounded
   uint32_t q_sign;     // 0x80008000 when the scale is negative: Q is negated, scale_log2 = |.|
   int32_t pack;        // 1: a tile packs the rows of the `group` query heads of one KV head
+  int32_t grid3;       // set by the launcher: 1 for a (unit, batch, tile) grid, 0 for a linear one
 };
 
 // Split-KV decode: one work group per (split, KV head x query-head group, batch).
