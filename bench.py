@@ -406,12 +406,11 @@ def run_backward(ex, W, args):
     }
 
 
-def run_fp8(ex, W, args):
-    """The FP8 forward on the causal prefill shape: q, k, v (2, 1024, 16, 128) E4M3 codes of a
-    seeded N(0,1) draw, descales 1, bf16 output; one step is one exattn_fwd_fp8 call."""
+def fp8_timing(ex, W, w, steps, warmup):
+    """One exattn_fwd_fp8 call per step on workload w: q, k, v E4M3 codes of the seeded N(0,1)
+    draw of its shape, descales 1, bf16 output.  Returns (time_steps result, flops)."""
     import ctypes as C
     import torch
-    w = W.WORKLOADS["causal_prefill"]
     q, k, v = (t.cuda() for t in W.qkv(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv, w.head_dim,
                                        seed=w.seed, dtype=torch.float8_e4m3fn))
     out = torch.empty((w.batch, w.seqlen_q, w.heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
@@ -426,7 +425,7 @@ def run_fp8(ex, W, args):
     a.v_stride[:] = list(v.stride()[:3])
     a.o_stride[:] = list(out.stride()[:3])
     a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
-    a.causal = 1
+    a.causal = 1 if w.causal else 0
     a.window_left = a.window_right = -1
     ds = ex.Fp8Descale(1.0, 1.0, 1.0)
     L = ex.lib()
@@ -438,10 +437,21 @@ def run_fp8(ex, W, args):
         if rc != 0:
             ex._raise_for(rc, "exattn_fwd_fp8")
 
+    t = time_steps(step, steps, warmup)
+    del q, k, v, out, lse
+    return t, W.flops(w)
+
+
+def run_fp8(ex, W, args):
+    """The FP8 forward on the causal prefill shape (2, 1024, 16, 128) and on the 16k-token causal
+    prefill (1, 16384, 16, 128); one step is one exattn_fwd_fp8 call."""
+    import torch
     steps = max(10, min(args.steps, 100))
-    t = time_steps(step, steps, max(2, args.warmup // 2))
-    fl = W.flops(w)
+    t, fl = fp8_timing(ex, W, W.WORKLOADS["causal_prefill"], steps, max(2, args.warmup // 2))
     tflops = fl / (t["region"] * 1e-3) / 1e12
+    tl, fll = fp8_timing(ex, W, W.WORKLOADS["long_prefill"], 10, 3)
+    torch.cuda.empty_cache()
+    tfl = fll / (tl["region"] * 1e-3) / 1e12
     return {
         "workload": "FP8 forward of the causal prefill shape: q, k, v (2, 1024, 16, 128) E4M3, descales 1, "
                     "bf16 out",
@@ -449,6 +459,9 @@ def run_fp8(ex, W, args):
         "ms_per_call_avg": round(t["region"], 6), "ms_per_call_median": round(t["pair_median"], 6),
         "ms_per_call_min": round(t["pair_min"], 6), "calls": steps,
         "frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "long": {"workload": "FP8 forward, b 1, s 16384, h 16, d 128, causal, E4M3, descales 1, bf16 out",
+                 "us_per_call": round(tl["region"] * 1e3, 2), "tflops": round(tfl, 2),
+                 "frac_of_fp8_peak": round(tfl / PEAK_FP8_TFLOPS, 4), "calls": 10},
         "note": "S on the FP8 MFMA, PV on the bf16 MFMA (P rounded to bf16)",
     }
 

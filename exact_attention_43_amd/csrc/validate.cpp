@@ -25,11 +25,13 @@ std::string str(int64_t v) { return std::to_string(v); }
 // byte to the end of its last row must stay below 2^31 bytes.
 exattn_status check_span(const char* name, int64_t rows, int64_t token_stride, int64_t heads,
                          int64_t head_stride, int64_t head_dim, int64_t elem_bytes) {
-  const int64_t span = ((rows - 1) * token_stride + (heads - 1) * head_stride + head_dim) * elem_bytes;
-  if (span >= ((int64_t)1 << 31))
+  // 128-bit: the strides are only known to be non-negative multiples of 8
+  const __int128 span =
+      ((__int128)(rows - 1) * token_stride + (__int128)(heads - 1) * head_stride + head_dim) * elem_bytes;
+  if (span >= ((__int128)1 << 31))
     return fail(EXATTN_E_UNSUPPORTED,
-                std::string(name) + ": a tile of " + str(rows) + " tokens spans " + str(span) +
-                    " bytes with these strides, beyond the kernels' 32-bit offsets (2^31 bytes)");
+                std::string(name) + ": a tile of " + str(rows) +
+                    " tokens spans 2^31 bytes or more with these strides, beyond the kernels' 32-bit offsets");
   return EXATTN_OK;
 }
 
@@ -158,8 +160,8 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   if (a->pack_gqa < -1 || a->pack_gqa > 1)
     return fail(EXATTN_E_INVALID, "pack_gqa must be -1 (automatic), 0 or 1");
   const int64_t g = pl->group;
-  const int64_t tiles_plain = (int64_t)a->heads_q * ((s_q + rows_per_tile - 1) / rows_per_tile);
-  const int64_t tiles_packed = (int64_t)a->heads_kv * ((s_q * g + rows_per_tile - 1) / rows_per_tile);
+  const int64_t tiles_plain = (int64_t)a->heads_q * (((int64_t)s_q + rows_per_tile - 1) / rows_per_tile);
+  const int64_t tiles_packed = (int64_t)a->heads_kv * (((int64_t)s_q * g + rows_per_tile - 1) / rows_per_tile);
   pl->pack = a->pack_gqa == 1 || (a->pack_gqa == -1 && g > 1 && tiles_packed < tiles_plain);
   const bool pack_fits = (int64_t)s_q * g < ((int64_t)1 << 22);  // the kernel's row division
   if (a->pack_gqa == 1 && !pack_fits)
@@ -227,7 +229,7 @@ exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d
     if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
     if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides must be non-negative");
   }
-  const int64_t grid = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64);
+  const int64_t grid = (int64_t)a->batch * a->heads_q * (((int64_t)a->seqlen_q + 63) / 64);
   if (grid > 0x7fffffffLL) return fail(EXATTN_E_INVALID, "problem too large for one launch");
   return EXATTN_OK;
 }
@@ -243,9 +245,16 @@ int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t se
   if (batch <= 0 || seqlen_k <= 0 || heads_kv <= 0 || heads_q <= 0 || num_cus <= 0) return 1;
   const int64_t cols = (int64_t)(heads_q / heads_kv) * (seqlen_q > 1 ? seqlen_q : 1);
   const int64_t hpw = decode_heads_per_group(head_dim, heads_kv);
-  const int64_t units = (int64_t)batch * ((heads_kv + hpw - 1) / hpw) * ((cols + 15) / 16);
   const int64_t target_wgs = num_cus;  // one work group (two 64 KiB LDS stages) per compute unit
-  if (units >= target_wgs) return 1;
+  // work groups without splitting: batch x KV-head groups x 16-column groups
+  // (each factor is at least 1; stop as soon as the product reaches the target)
+  const int64_t factors[3] = {batch, ((int64_t)heads_kv + hpw - 1) / hpw, (cols + 15) / 16};
+  int64_t units = 1;
+  for (const int64_t f : factors) {
+    if (f < 1) return 1;
+    if (units >= (target_wgs + f - 1) / f) return 1;  // units * f >= target_wgs
+    units *= f;
+  }
   int64_t splits = (target_wgs + units - 1) / units;
   const int64_t by_len = seqlen_k / 256 > 1 ? seqlen_k / 256 : 1;  // >= 256 keys per split
   if (splits > by_len) splits = by_len;
@@ -274,14 +283,14 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
   if (cols > 16 * 4096) return fail(EXATTN_E_UNSUPPORTED, "seqlen_q x (heads_q / heads_kv) above 65536");
   pl->n_hg = (int)((cols + 15) / 16);
   pl->hpw = decode_heads_per_group(a->head_dim, a->heads_kv);
-  pl->n_hk = (a->heads_kv + pl->hpw - 1) / pl->hpw;
+  pl->n_hk = (int)(((int64_t)a->heads_kv + pl->hpw - 1) / pl->hpw);
   pl->wl = a->window_left < 0 ? -1 : a->window_left;
   pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
   int64_t ns = a->num_splits == 0
                    ? auto_splits(a->batch, a->heads_q, a->heads_kv, a->seqlen_cache, a->head_dim,
                                  num_cus, pl->s_q)
                    : a->num_splits;
-  const int64_t chunks = (a->seqlen_cache + 31) / 32;
+  const int64_t chunks = ((int64_t)a->seqlen_cache + 31) / 32;
   if (ns > chunks) ns = chunks;
   if (ns > 256) ns = 256;
   if (ns < 1) ns = 1;
