@@ -20,6 +20,11 @@ MFMA busy time and executed MFMA FLOPs from one counter pass
 (``--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16``)::
 
     python -m exact_attention_43_amd.counters mfma DIR --kernel REGEX --flops F --out FILE.txt --cmd "..."
+
+MFMA, VALU and LDS activity per kernel against the clock actually run (one pass of
+the counters listed in ``cmd_busy``)::
+
+    python -m exact_attention_43_amd.counters busy DIR --kernel REGEX --out FILE.txt --cmd "..."
 """
 from __future__ import annotations
 
@@ -188,6 +193,57 @@ def cmd_mfma(a):
     print(text)
 
 
+def cmd_busy(a):
+    """Per kernel matching a.kernel (one line each): medians over its dispatches of the
+    duration, the GPU clock actually run (GRBM_GUI_ACTIVE cycles / duration), the MFMA busy
+    fraction against those cycles, the executed MFMA FLOPs (bf16 and FP8 MOPs x 512), the
+    VALU-active cycles per SIMD and the LDS-active fraction per CU, from one counter pass:
+    --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8
+    SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE."""
+    rx = re.compile(a.kernel)
+    per = {}
+    for r in _csvs(a.dir, "counter_collection.csv"):
+        if not rx.search(r["Kernel_Name"]):
+            continue
+        d = per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})
+        c, v = r["Counter_Name"], float(r["Counter_Value"])
+        d[c] = d.get(c, 0.0) + v
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    kernels = sorted({k[0] for k in per})
+    if not kernels:
+        raise SystemExit(f"no kernel matching {a.kernel!r}")
+    med = lambda xs: statistics.median(xs)
+    lines = [f"# MFMA, VALU and LDS activity per dispatch (medians); clock from GRBM_GUI_ACTIVE",
+             f"# command: {a.cmd}", "",
+             f"{'kernel':<64} {'disp':>4} {'us':>8} {'GHz':>5} {'mfma%':>6} {'TFLOP':>8} {'valu%':>6} "
+             f"{'lds%':>5} {'bank%':>5}"]
+    for k in kernels:
+        ds = [v for (n, _), v in per.items() if n == k]
+        ns = med([d["ns"] for d in ds])
+        # GRBM_GUI_ACTIVE comes summed over the XCDs, which all count the same
+        # cycles; over a short dispatch it also counts the collection window
+        cyc = med([d["GRBM_GUI_ACTIVE"] for d in ds]) / a.xcds
+        ghz = cyc / ns
+        mfma = med([d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds]) / a.simds / cyc
+        fl = med([(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)) * 512
+                  for d in ds])
+        valu = med([d["SQ_ACTIVE_INST_VALU"] for d in ds]) / a.simds / cyc
+        lds = med([d["SQ_LDS_IDX_ACTIVE"] for d in ds]) / a.cus / cyc
+        bank = med([d["SQ_LDS_BANK_CONFLICT"] for d in ds]) / max(1.0, med([d["SQ_LDS_IDX_ACTIVE"] for d in ds]))
+        lines.append(f"{k[:64]:<64} {len(ds):>4} {ns / 1e3:>8.2f} {ghz:>5.2f} {100 * mfma:>6.1f} {fl / 1e12:>8.4f} "
+                     f"{100 * valu:>6.1f} {100 * lds:>5.1f} {100 * bank:>5.1f}")
+    lines += ["", "mfma%: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE); valu%: SQ_ACTIVE_INST_VALU",
+              "per SIMD over the same cycles (it counts every wave's VALU cycles, so two waves can exceed 100);",
+              "lds%: SQ_LDS_IDX_ACTIVE per CU; bank%: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.",
+              "GRBM_GUI_ACTIVE / 8 XCDs gives the cycles; over dispatches of a few tens of microseconds it also",
+              "counts the collection window (the GHz column then reads high and the fractions low).",
+              "Durations run longer under counter collection than in a plain run."]
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -219,6 +275,15 @@ def main(argv=None):
     m.add_argument("--out", required=True)
     m.add_argument("--cmd", required=True)
     m.set_defaults(fn=cmd_mfma)
+    u = sub.add_parser("busy")
+    u.add_argument("dir")
+    u.add_argument("--kernel", required=True)
+    u.add_argument("--simds", type=int, default=1024)
+    u.add_argument("--cus", type=int, default=256)
+    u.add_argument("--xcds", type=int, default=8)
+    u.add_argument("--out", required=True)
+    u.add_argument("--cmd", required=True)
+    u.set_defaults(fn=cmd_busy)
     a = ap.parse_args(argv)
     a.fn(a)
 
