@@ -600,7 +600,7 @@ def attn_backward(dout, q, k, v, out, lse, softmax_scale=None, causal=False, win
     q, out, dout (b, s_q, h_q, d); k, v (b, s_k, h_kv, d); lse (b, h_q, s_q) fp32
     as attn_func returns it; the same scale, causal, window and softcap as the
     forward call.  A KV head's dk and dv sum over the query heads that read it.
-    head_dim 64 or 128.  Deterministic.
+    head_dim 64, 128 or 256.  Deterministic.
     """
     for name, t in (("q", q), ("out", out), ("dout", dout)):
         if t.dim() != 4:

@@ -156,11 +156,15 @@ __device__ __forceinline__ SeqSpan seq_span(const BwdParams& p, int b) {
 }
 
 // dK, dV for 128 keys of one KV head (4 waves x 32 keys).
-template <bool BF16, int D, bool SOFTCAP>
+// DS: head-dim slices.  At d = 256 a wave's K and V (128 registers) and its
+// dK and dV accumulators (256) leave too few of its 512 for the rest, so the
+// work groups of a key tile split dK and dV into two halves of the head dims
+// (DS = 2), each recomputing S and dP (a third more products).
+template <bool BF16, int D, bool SOFTCAP, int DS>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   using E = Elem<BF16>;
   constexpr int KS = D / 16;                   // k-steps over head_dim
-  constexpr int DT = D / 32;                   // 32-wide head_dim tiles
+  constexpr int DT = D / 32 / DS;              // 32-wide head_dim tiles of this work group's slice
   constexpr int DCH = D / 8;                   // 16-byte chunks per row
   constexpr int TILE = kBwdRows * D * 2;       // bytes of a Q (or dO) tile
   constexpr int ROWS_PER_KB = 1024 / (D * 2);  // rows per 1 KiB DMA slice
@@ -176,9 +180,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   const int l32 = lane & 31;
 
   const int n_kt = (p.s_k + kBwdKeys - 1) / kBwdKeys;
-  const int kt = blockIdx.x % n_kt;
-  const int hk = (blockIdx.x / n_kt) % p.h_kv;
-  const int b = blockIdx.x / (n_kt * p.h_kv);
+  const int dsl = (int)blockIdx.x % DS;   // head-dim slice: dims 32 DT dsl ..
+  const int bid = (int)blockIdx.x / DS;
+  const int kt = bid % n_kt;
+  const int hk = (bid / n_kt) % p.h_kv;
+  const int b = bid / (n_kt * p.h_kv);
   const SeqSpan sp = seq_span(p, b);
   const int sq = sp.sq, sk = sp.sk, off = sk - sq;
   const int sqm = p.s_q;  // row stride of the statistics (the longest sequence)
@@ -254,7 +260,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int row = 8 * (gi >> 1) + 4 * half + (li >> 2);
-      const int dcol = 32 * dt + 16 * (gi & 1) + 4 * (li & 3);
+      const int dcol = 32 * (DT * dsl + dt) + 16 * (gi & 1) + 4 * (li & 3);
       tr[half][dt] = row * (D * 2) + 16 * ((dcol >> 3) ^ qswz<D>(row)) + 2 * (dcol & 7);
     }
 
@@ -351,8 +357,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
         wk[1] = E::pack2(dk[dt][4 * J + 2] * p.scale, dk[dt][4 * J + 3] * p.scale);
         wv[0] = E::pack2(dv[dt][4 * J], dv[dt][4 * J + 1]);
         wv[1] = E::pack2(dv[dt][4 * J + 2], dv[dt][4 * J + 3]);
-        *(u32x2_t*)(kq + 32 * dt + 8 * J + 4 * hsel) = wk;
-        *(u32x2_t*)(vq + 32 * dt + 8 * J + 4 * hsel) = wv;
+        *(u32x2_t*)(kq + 32 * (DT * dsl + dt) + 8 * J + 4 * hsel) = wk;
+        *(u32x2_t*)(vq + 32 * (DT * dsl + dt) + 8 * J + 4 * hsel) = wv;
       }
   }
 }
@@ -609,7 +615,9 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   const int n_kt = (p.s_k + kBwdKeys - 1) / kBwdKeys;
   if (n_kt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, SOFTCAP>), dim3(n_kt * p.h_kv * p.batch), dim3(256), 0, stream, p);
+    constexpr int DS = D == 256 ? 2 : 1;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, SOFTCAP, DS>), dim3(n_kt * p.h_kv * p.batch * DS), dim3(256), 0,
+                       stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -617,11 +625,17 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   if (n_qt > 0) {
     const int grid = n_qt * p.h_q * p.batch;
     // Fewer than 1024 tiles leave under two waves per SIMD on 256 CUs: split each
-    // tile's key blocks between two wave groups then.
-    if (grid < 1024)
+    // tile's key blocks between two wave groups then.  At d = 256 the one-group
+    // kernel's 64-key blocks need more registers than a wave has: two groups of
+    // 32-key blocks always.
+    bool two = true;
+    if constexpr (D != 256) two = grid < 1024;
+    if (two) {
       hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves * 2), 0, stream, p);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
+    } else {
+      if constexpr (D != 256)
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
+    }
     e = hipGetLastError();
   }
   return e;
@@ -637,6 +651,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool softcap, hipStream_t stream) {
   if (head_dim == 64) return softcap ? launch_bwd_d<64, true>(p, stream) : launch_bwd_d<64, false>(p, stream);
   if (head_dim == 128) return softcap ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<128, false>(p, stream);
+  if (head_dim == 256) return softcap ? launch_bwd_d<256, true>(p, stream) : launch_bwd_d<256, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

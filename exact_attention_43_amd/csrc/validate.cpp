@@ -353,8 +353,6 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
   *pl = BwdPlan{};
   exattn_status st = check_common(a->dtype, a->head_dim, a->heads_q, a->heads_kv, a->batch);
   if (st != EXATTN_OK) return st;
-  if (a->head_dim == 256)
-    return fail(EXATTN_E_UNSUPPORTED, "the backward provides head_dim 64 and 128");
   const bool varlen = a->cu_seqlens_q != nullptr;
   if (varlen != (a->cu_seqlens_k != nullptr))
     return fail(EXATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");

@@ -312,7 +312,7 @@ void bwd_case(long it, Count& c) {
     ++c.ok;
     if (!pl.empty) {
       expect(pl.group >= 1 && (int64_t)pl.group * a.heads_kv == a.heads_q, "bwd group", it);
-      expect(pl.head_dim == 64 || pl.head_dim == 128, "bwd head_dim", it);
+      expect(pl.head_dim == 64 || pl.head_dim == 128 || pl.head_dim == 256, "bwd head_dim", it);
       expect(isfinite(pl.scale) && isfinite(pl.scale_log2), "bwd scales finite", it);
       const int64_t sq = a.cu_seqlens_q != nullptr ? a.max_seqlen_q : a.seqlen_q;
       expect(pl.ws_bytes % 256 == 0 && (int64_t)pl.ws_bytes >= 8 * (int64_t)a.batch * a.heads_q * sq,

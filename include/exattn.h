@@ -267,7 +267,7 @@ exattn_status exattn_decode_paged(const exattn_decode_args *args, const exattn_p
  * packed token).  With softcap c the gradient flows through c tanh(s / c)
  * (FAQ Q22), i.e. dS is multiplied by 1 - tanh^2.  A KV head's dK and dV sum
  * over the query heads that read it.  Deterministic (no atomics).
- * Provided: head_dim 64 and 128; head_dim 256 returns EXATTN_E_UNSUPPORTED.
+ * head_dim 64, 128 or 256.
  * workspace: batch * heads_q * seqlen_q (varlen: max_seqlen_q) * 8 bytes
  * rounded up to 256 (exattn_bwd_plan), 256-byte aligned, scratch owned by the
  * caller.

@@ -315,7 +315,6 @@ def _bwd(**kw):
 
 BAD_BWD = [
     ("dtype", dict(dtype=3), ex.EXATTN_E_UNSUPPORTED),
-    ("head_dim 256", dict(head_dim=256), ex.EXATTN_E_UNSUPPORTED),
     ("head_dim 80", dict(head_dim=80), ex.EXATTN_E_UNSUPPORTED),
     ("heads ratio", dict(heads_q=3), ex.EXATTN_E_INVALID),
     ("half varlen", dict(cu_seqlens_q=FAKE), ex.EXATTN_E_INVALID),
@@ -456,9 +455,14 @@ def test_decode_plan_counts_query_tokens(L):
 
 
 def test_bwd_accepts_softcap_and_varlen_plans(L):
-    """Softcap and packed sequences are provided: their plans succeed; the varlen workspace
-    is sized by the longest sequence."""
+    """Softcap, packed sequences and head_dim 256 are provided: their plans succeed; the
+    varlen workspace is sized by the longest sequence."""
     wb = C.c_size_t(0)
+    d256 = _bwd(head_dim=256)
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
+        st = getattr(d256, f"{name}_stride")
+        st[:] = [st[0] * 2, st[1] * 2, st[2] * 2]
+    assert L.exattn_bwd_plan(C.byref(d256), C.byref(wb)) == ex.EXATTN_OK, L.exattn_last_error()
     assert L.exattn_bwd_plan(C.byref(_bwd(softcap=30.0)), C.byref(wb)) == ex.EXATTN_OK, L.exattn_last_error()
     a = _bwd(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=77, max_seqlen_k=300)
     assert L.exattn_bwd_plan(C.byref(a), C.byref(wb)) == ex.EXATTN_OK, L.exattn_last_error()

@@ -608,6 +608,11 @@ BWD_CASES = [
     # 1024 query tiles and more: the dQ kernel without the key split
     (1, 2048, 2048, 32, 8, 64, torch.bfloat16, True, (-1, -1), 209),
     (1, 1024, 1024, 64, 16, 128, torch.float16, False, (-1, -1), 210),
+    # head_dim 256: dK and dV in two head-dim slices, dQ always with the key split
+    (2, 200, 200, 4, 2, 256, torch.bfloat16, True, (-1, -1), 211),
+    (1, 130, 300, 4, 4, 256, torch.float16, False, (-1, -1), 212),
+    (1, 257, 100, 2, 1, 256, torch.bfloat16, True, (-1, -1), 213),    # rows without keys
+    (1, 512, 512, 8, 8, 256, torch.float16, False, (100, 20), 214),
 ]
 
 
@@ -638,6 +643,8 @@ BWD_CAP_CASES = [
     (1, 300, 300, 2, 2, 128, torch.bfloat16, False, (50, 10), 2.0, None, 232),   # saturating cap
     (2, 257, 100, 4, 1, 128, torch.float16, True, (-1, -1), 20.0, -0.09, 233),   # negative scale, empty rows
     (1, 1024, 1024, 16, 16, 128, torch.bfloat16, True, (-1, -1), 50.0, None, 234),
+    (1, 200, 200, 4, 2, 256, torch.bfloat16, True, (-1, -1), 30.0, None, 237),
+    (1, 150, 150, 2, 2, 256, torch.float16, False, (-1, -1), 2.0, -0.07, 238),  # saturating, negative scale
 ]
 
 
@@ -662,14 +669,14 @@ def test_backward_softcap(case):
     assert_grad_close(gv, rv, mv, dt, "dv")
 
 
-@pytest.mark.parametrize("causal,window,cap", [(True, (-1, -1), 0.0), (False, (40, 7), 0.0),
-                                               (True, (256, 0), 50.0)])
-def test_backward_varlen(causal, window, cap):
+@pytest.mark.parametrize("causal,window,cap,d", [(True, (-1, -1), 0.0, 128), (False, (40, 7), 0.0, 128),
+                                                 (True, (256, 0), 50.0, 128), (True, (-1, -1), 0.0, 256)])
+def test_backward_varlen(causal, window, cap, d):
     """Packed sequences (FAQ Q8), ragged and empty ones included: each sequence's gradients
     against the oracle's on that sequence alone."""
     lens_q = [1, 0, 300, 129, 64, 77]
     lens_k = [5, 3, 300, 1, 300, 77]
-    hq, hkv, d = 8, 2, 128
+    hq, hkv = 8, 2
     q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, hq, hkv, d, seed=235)
     dout = W.varlen_qkv(lens_q, [1] * len(lens_q), hq, 1, d, seed=236)[0]
     dq_, dk_, dv_, dcq, dck, ddo = _dev(q, k, v, cu_q, cu_k, dout)
