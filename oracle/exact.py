@@ -323,15 +323,16 @@ def decode_e4m3(codes):
 
 
 def attention_fp8(q, k, v, *, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_scale=None,
-                  causal=False, window_size=(-1, -1), rows=None, heads=None):
+                  causal=False, window_size=(-1, -1), softcap=0.0, rows=None, heads=None):
     """The FP8 forward (FAQ Q20): Q, K, V are E4M3 codes whose real values are
     code x descale (one factor per tensor); the result is exact attention of
-    those real values (default scale 1/sqrt(d)).  The output precision (bf16)
-    and the internal FP8 products are the kernel's business: the reference is
-    the definition in float64."""
+    those real values (default scale 1/sqrt(d)), with the same softcap and
+    masks as the 16-bit forward (FAQ Q22: the cap on the scaled scores, before
+    the mask).  The output precision (bf16) and the internal FP8 products are
+    the kernel's business: the reference is the definition in float64."""
     return attention(decode_e4m3(q) * float(q_descale), decode_e4m3(k) * float(k_descale),
                      decode_e4m3(v) * float(v_descale), softmax_scale=softmax_scale, causal=causal,
-                     window_size=window_size, rows=rows, heads=heads)
+                     window_size=window_size, softcap=softcap, rows=rows, heads=heads)
 
 
 def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new):

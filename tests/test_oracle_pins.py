@@ -647,6 +647,41 @@ def pin_fp8():
     assert np.allclose(o6, o7, atol=1e-12) and np.allclose(l6, l7, atol=1e-12)
 
 
+def pin_fp8_softcap():
+    """The FP8 forward with softcap (FAQ Q20 with Q22): the cap acts on the scaled
+    scores of the real values.  With one key, LSE is c tanh(s / c) of the row's
+    single score and O is that key's V row (real values: codes from torch's own
+    E4M3 conversion times the descales), and the Q and K descales still enter
+    only through their product with the scale."""
+    import torch
+    r = _rng(27)
+    q = torch.from_numpy(r.standard_normal((1, 7, 2, 32)) * 3).to(torch.float8_e4m3fn)
+    k = torch.from_numpy(r.standard_normal((1, 1, 2, 32)) * 3).to(torch.float8_e4m3fn)
+    v = torch.from_numpy(r.standard_normal((1, 1, 2, 32))).to(torch.float8_e4m3fn)
+    cap, dq, dk, dv = 5.0, 0.5, 1.5, 2.0
+    o, lse = oracle.attention_fp8(q, k, v, q_descale=dq, k_descale=dk, v_descale=dv, softcap=cap)
+    qf, kf, vf = (t.to(torch.float64).numpy() for t in (q, k, v))
+    scale = 1.0 / math.sqrt(32)
+    for h in range(2):
+        for i in range(7):
+            raw = scale * dq * dk * math.fsum(qf[0, i, h] * kf[0, 0, h])
+            assert abs(lse[0, h, i] - cap * math.tanh(raw / cap)) < 1e-12
+            assert np.allclose(o[0, i, h], vf[0, 0, h] * dv, atol=1e-12)
+    # the cap bites: the capped LSE is not the uncapped one
+    _, lse_nc = oracle.attention_fp8(q, k, v, q_descale=dq, k_descale=dk, v_descale=dv)
+    assert np.abs(lse - lse_nc).max() > 0.1
+    # descales and scale through their product, with the cap on
+    q2 = torch.from_numpy(r.standard_normal((2, 9, 4, 16))).to(torch.float8_e4m3fn)
+    k2 = torch.from_numpy(r.standard_normal((2, 11, 2, 16))).to(torch.float8_e4m3fn)
+    v2 = torch.from_numpy(r.standard_normal((2, 11, 2, 16))).to(torch.float8_e4m3fn)
+    o1, l1 = oracle.attention_fp8(q2, k2, v2, causal=True, softcap=1.5)
+    o2, l2 = oracle.attention_fp8(q2, k2, v2, q_descale=4.0, k_descale=0.25, causal=True, softcap=1.5)
+    o3, l3 = oracle.attention_fp8(q2, k2, v2, q_descale=2.0, softmax_scale=0.125, causal=True, softcap=1.5)
+    o4, l4 = oracle.attention_fp8(q2, k2, v2, softmax_scale=0.25, causal=True, softcap=1.5)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    assert np.allclose(o3, o4, atol=1e-12) and np.allclose(l3, l4, atol=1e-12)
+
+
 def pin_softcap():
     r = _rng(19)
     q = r.standard_normal((1, 6, 2, 16)) * 4
@@ -688,7 +723,7 @@ def pin_default_scale():
 
 PINS = [pin_bruteforce, pin_sdpa, pin_softmax_rows, pin_sk1, pin_identical_v_rows,
         pin_zero_q_counts, pin_bottom_right_causal, pin_window_fixture, pin_shift_invariance,
-        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_decode_multi_query, pin_paged, pin_backward, pin_backward_magnitudes, pin_fp8, pin_softcap,
+        pin_merge_identity, pin_gqa_repeat, pin_varlen, pin_decode, pin_decode_append, pin_decode_multi_query, pin_paged, pin_backward, pin_backward_magnitudes, pin_fp8, pin_fp8_softcap, pin_softcap,
         pin_default_scale]
 
 
