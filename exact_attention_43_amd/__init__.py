@@ -308,11 +308,36 @@ def attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_s
     return out, lse
 
 
+def _fp8_call(q, k, v, out, lse, *, batch, s_q, s_k, h_q, h_kv, d, q_st, k_st, v_st, o_st, lse_st, descales,
+              softmax_scale, causal, window_size, softcap, cu_q=None, cu_k=None, max_q=0, max_k=0):
+    a = FwdArgs()
+    a.dtype = EXATTN_FP8_E4M3
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = batch, s_q, s_k, h_q, h_kv, d
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    a.q_stride[:] = list(q_st)
+    a.k_stride[:] = list(k_st)
+    a.v_stride[:] = list(v_st)
+    a.o_stride[:] = list(o_st)
+    a.lse_stride[:] = list(lse_st)
+    if cu_q is not None:
+        a.cu_seqlens_q, a.cu_seqlens_k = cu_q.data_ptr(), cu_k.data_ptr()
+        a.max_seqlen_q, a.max_seqlen_k = int(max_q), int(max_k)
+    a.softmax_scale = _scale(softmax_scale)
+    a.softcap = float(softcap or 0.0)
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = _window(window_size)
+    ds = Fp8Descale(*(float(x) for x in descales))
+    with torch.cuda.device(q.device):
+        st = lib().exattn_fwd_fp8(C.byref(a), C.byref(ds), C.c_void_p(_stream(q.device)))
+    _raise_for(st, "exattn_fwd_fp8")
+
+
 def attn_func_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_scale=None, causal=False,
-                  window_size=(-1, -1), out=None, lse=None):
+                  window_size=(-1, -1), softcap=0.0, out=None, lse=None):
     """FP8 forward with a bf16 output (FAQ Q20).  q (b, s_q, h_q, d), k, v (b, s_k, h_kv, d) as
     torch.float8_e4m3fn; the real inputs are the values times the descale factors.  Returns
-    (out bf16 (b, s_q, h_q, d), lse fp32 (b, h_q, s_q)).  head_dim 64 or 128, fixed lengths."""
+    (out bf16 (b, s_q, h_q, d), lse fp32 (b, h_q, s_q)).  head_dim 64 or 128; softcap as for
+    attn_func (applied to the scaled real scores)."""
     _on_gpu(q, k, v, out, lse)
     _check_last_dim(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -331,23 +356,49 @@ def attn_func_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, softmax_
     if lse is None:
         lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
     _check_lse(lse, (b, h_q, s_q))
-    a = FwdArgs()
-    a.dtype = EXATTN_FP8_E4M3
-    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = b, s_q, s_k, h_q, h_kv, d
-    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
-    a.q_stride[:] = list(q.stride()[:3])
-    a.k_stride[:] = list(k.stride()[:3])
-    a.v_stride[:] = list(v.stride()[:3])
-    a.o_stride[:] = list(out.stride()[:3])
-    a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
-    a.softmax_scale = _scale(softmax_scale)
-    a.softcap = 0.0
-    a.causal = 1 if causal else 0
-    a.window_left, a.window_right = _window(window_size)
-    ds = Fp8Descale(float(q_descale), float(k_descale), float(v_descale))
-    with torch.cuda.device(q.device):
-        st = lib().exattn_fwd_fp8(C.byref(a), C.byref(ds), C.c_void_p(_stream(q.device)))
-    _raise_for(st, "exattn_fwd_fp8")
+    _fp8_call(q, k, v, out, lse, batch=b, s_q=s_q, s_k=s_k, h_q=h_q, h_kv=h_kv, d=d, q_st=q.stride()[:3],
+              k_st=k.stride()[:3], v_st=v.stride()[:3], o_st=out.stride()[:3],
+              lse_st=(lse.stride(0), lse.stride(1)), descales=(q_descale, k_descale, v_descale),
+              softmax_scale=softmax_scale, causal=causal, window_size=window_size, softcap=softcap)
+    return out, lse
+
+
+def attn_varlen_func_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, q_descale=1.0,
+                         k_descale=1.0, v_descale=1.0, softmax_scale=None, causal=False, window_size=(-1, -1),
+                         softcap=0.0, out=None, lse=None):
+    """The FP8 forward over packed sequences (FAQ Q8, Q20): q (total_q, h_q, d), k, v
+    (total_k, h_kv, d) as torch.float8_e4m3fn, int32 cu_seqlens.  Returns out bf16
+    (total_q, h_q, d) and lse (h_q, total_q)."""
+    _on_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("varlen q, k, v must be 3-D (total, heads, head_dim)")
+    if not (q.dtype == k.dtype == v.dtype == torch.float8_e4m3fn):
+        raise ValueError("q, k and v must be torch.float8_e4m3fn")
+    if k.shape != v.shape or k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    _check_last_dim(q, k, v)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold batch + 1 entries")
+    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()):
+        raise ValueError("cu_seqlens must be contiguous")
+    total_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    if out is None:
+        out = torch.empty((total_q, h_q, d), dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != (total_q, h_q, d):
+        raise ValueError("out must be bf16 (total_q, heads_q, head_dim)")
+    _check_last_dim(out)
+    if lse is None:
+        lse = torch.empty((h_q, total_q), dtype=torch.float32, device=q.device)
+    _check_lse(lse, (h_q, total_q))
+    _fp8_call(q, k, v, out, lse, batch=cu_seqlens_q.numel() - 1, s_q=0, s_k=0, h_q=h_q, h_kv=h_kv, d=d,
+              q_st=(0, q.stride(0), q.stride(1)), k_st=(0, k.stride(0), k.stride(1)),
+              v_st=(0, v.stride(0), v.stride(1)), o_st=(0, out.stride(0), out.stride(1)),
+              lse_st=(0, lse.stride(0)), descales=(q_descale, k_descale, v_descale),
+              softmax_scale=softmax_scale, causal=causal, window_size=window_size, softcap=softcap,
+              cu_q=cu_seqlens_q, cu_k=cu_seqlens_k, max_q=max_seqlen_q, max_k=max_seqlen_k)
     return out, lse
 
 
@@ -675,6 +726,6 @@ def auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus):
     return int(lib().exattn_decode_auto_splits(batch, heads_q, heads_kv, seqlen_k, head_dim, num_cus))
 
 
-__all__ = ["attn_func", "attn_func_fp8", "attn_qkvpacked_func", "attn_kvpacked_func", "attn_varlen_func",
+__all__ = ["attn_func", "attn_func_fp8", "attn_varlen_func_fp8", "attn_qkvpacked_func", "attn_kvpacked_func", "attn_varlen_func",
            "attn_with_kvcache", "attn_backward", "attn_varlen_backward", "decode_plan", "auto_splits", "lib",
            "library_path"]

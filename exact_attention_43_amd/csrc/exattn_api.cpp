@@ -272,8 +272,8 @@ exattn_status exattn_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale*
     p.o_sb = a->o_stride[0], p.o_ss = a->o_stride[1], p.o_sh = a->o_stride[2];
     p.lse_sb = a->lse_stride[0], p.lse_sh = a->lse_stride[1];
     p.batch = a->batch;
-    p.s_q = a->seqlen_q;
-    p.s_k = a->seqlen_k;
+    p.s_q = pl.s_q;
+    p.s_k = pl.s_k;
     p.h_q = a->heads_q;
     p.h_kv = a->heads_kv;
     p.group = pl.group;
@@ -281,7 +281,11 @@ exattn_status exattn_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale*
     p.v_descale = pl.v_descale;
     p.wl = pl.wl;
     p.wr = pl.wr;
-    hipError_t e = launch_fwd_fp8(p, pl.head_dim, static_cast<hipStream_t>(stream));
+    p.cap_in = pl.cap_in;
+    p.cap_out_log2 = pl.cap_out_log2;
+    p.cu_q = pl.varlen ? a->cu_seqlens_q : nullptr;
+    p.cu_k = pl.varlen ? a->cu_seqlens_k : nullptr;
+    hipError_t e = launch_fwd_fp8(p, pl.head_dim, pl.softcap, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(EXATTN_E_HIP, std::string("fp8 forward launch: ") + hipGetErrorString(e));
     return EXATTN_OK;
   } catch (...) {

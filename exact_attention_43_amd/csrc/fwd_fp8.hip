@@ -81,7 +81,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p)));
 }
 
-template <int D, int NW, int NG>
+template <int D, int NW, int NG, bool SOFTCAP>
 __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Params p) {
   constexpr int BN = kF8Keys;
   constexpr int NT2 = BN / 32;       // 32-key tiles per block
@@ -110,8 +110,29 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
   const int u = blockIdx.x % units;
   const int b = u / p.h_q, h = u % p.h_q;
   const int hk = h / p.group;
-  const int sq = p.s_q, sk = p.s_k, off = sk - sq;
+  // a batch entry's rows: from the batch strides, or (varlen, FAQ Q8) the token
+  // span cu[b] .. cu[b + 1] - 1 of the packed tensors
+  int sq = p.s_q, sk = p.s_k;
+  int64_t qoff, koff, voff, ooff, lseoff;
+  if (p.cu_q != nullptr) {
+    const int qs = p.cu_q[b], ks = p.cu_k[b];
+    sq = p.cu_q[b + 1] - qs;
+    sk = p.cu_k[b + 1] - ks;
+    qoff = (int64_t)qs * p.q_ss;
+    koff = (int64_t)ks * p.k_ss;
+    voff = (int64_t)ks * p.v_ss;
+    ooff = (int64_t)qs * p.o_ss;
+    lseoff = qs;
+  } else {
+    qoff = (int64_t)b * p.q_sb;
+    koff = (int64_t)b * p.k_sb;
+    voff = (int64_t)b * p.v_sb;
+    ooff = (int64_t)b * p.o_sb;
+    lseoff = (int64_t)b * p.lse_sb;
+  }
+  const int off = sk - sq;
   const int q0 = qt * rows_wg;
+  if (q0 >= sq) return;  // uniform: a shorter sequence has no rows here
   const int q0w = q0 + 32 * wave;
   const int qrow = q0w + l32;
 
@@ -129,7 +150,7 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
   i32x8_t qf[KS];
   {
     const bool in = qrow < sq;
-    const uint8_t* qp = p.q + (int64_t)b * p.q_sb + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 32 * hsel;
+    const uint8_t* qp = p.q + qoff + (int64_t)qrow * p.q_ss + (int64_t)h * p.q_sh + 32 * hsel;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4_t lo = in ? *(const u32x4_t*)(qp + 64 * ks) : u32x4_t{0, 0, 0, 0};
@@ -139,8 +160,8 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
   }
 
   // ---- DMA of the FP8 K and V tiles: row r, chunk c at r * D + 16 * (c ^ swz(r)).
-  const uint8_t* kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
-  const uint8_t* vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+  const uint8_t* kg = p.k + koff + (int64_t)hk * p.k_sh;
+  const uint8_t* vg = p.v + voff + (int64_t)hk * p.v_sh;
   uint32_t kofs[SLICES / NW], vofs[SLICES / NW];
 #pragma unroll
   for (int i = 0; i < SLICES / NW; ++i) {
@@ -217,7 +238,11 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
     for (int t2 = 0; t2 < NT2; ++t2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = s[t2][r] * p.scale_log2;
+        float x;
+        if constexpr (SOFTCAP)  // c tanh(s / c) before the mask (FAQ Q22), in the log2 domain
+          x = p.cap_out_log2 * tanh_exp2(s[t2][r] * p.cap_in);
+        else
+          x = s[t2][r] * p.scale_log2;
         if (!full) {
           const int key = kb0 + 32 * t2 + 16 * (r >> 3) + 8 * hsel + (r & 7);
           if (!f8_visible(qrow, key, sk, off, p.wl, p.wr)) x = -__builtin_inff();
@@ -336,7 +361,7 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
   // ---- O = (O^T)^T v_descale / l as bf16; lane holds head dims 32 dt + 8 J + 4 H + 0..3 of row qrow.
   if (qrow < sq) {
     const float inv = l > 0.f ? p.v_descale / l : 0.f;
-    uint16_t* op = p.o + (int64_t)b * p.o_sb + (int64_t)qrow * p.o_ss + (int64_t)h * p.o_sh;
+    uint16_t* op = p.o + ooff + (int64_t)qrow * p.o_ss + (int64_t)h * p.o_sh;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -347,12 +372,12 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
         *(u32x2_t*)(op + 32 * dt + 8 * J + 4 * hsel) = w;
       }
     if (hsel == 0 && p.lse != nullptr)
-      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow] =
+      p.lse[lseoff + (int64_t)h * p.lse_sh + qrow] =
           l > 0.f ? (m + fast_log2(l)) * kLn2 : kNegInf;
   }
 }
 
-template <int D>
+template <int D, bool SOFTCAP>
 hipError_t launch_fp8_t(const Fp8Params& p, hipStream_t stream) {
   constexpr int NW = 2;
   const int n_qt = (p.s_q + 32 * NW - 1) / (32 * NW);
@@ -363,17 +388,17 @@ hipError_t launch_fp8_t(const Fp8Params& p, hipStream_t stream) {
   // causal b2 s1024 h16 d128 shape); with more tiles the split only adds the merge
   // (1114 us against 1032 at s16384).
   if (grid < 1024)
-    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 2>), dim3((unsigned)grid), dim3(64 * NW * 2), 0, stream, p);
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 2, SOFTCAP>), dim3((unsigned)grid), dim3(64 * NW * 2), 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 1>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 1, SOFTCAP>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_fp8(const Fp8Params& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 64) return launch_fp8_t<64>(p, stream);
-  if (head_dim == 128) return launch_fp8_t<128>(p, stream);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int head_dim, bool softcap, hipStream_t stream) {
+  if (head_dim == 64) return softcap ? launch_fp8_t<64, true>(p, stream) : launch_fp8_t<64, false>(p, stream);
+  if (head_dim == 128) return softcap ? launch_fp8_t<128, true>(p, stream) : launch_fp8_t<128, false>(p, stream);
   return hipErrorInvalidValue;
 }
 

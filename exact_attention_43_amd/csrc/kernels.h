@@ -89,12 +89,15 @@ struct Fp8Params {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   int64_t lse_sb, lse_sh;
-  int batch, s_q, s_k, h_q, h_kv, group;
+  int batch, s_q, s_k, h_q, h_kv, group;  // s_q / s_k: lengths (fixed) or maxima (varlen)
   float scale_log2, v_descale;
   int wl, wr;  // window edges, -1 = unbounded (wr = 0 for causal)
+  float cap_in, cap_out_log2;  // softcap: scale x descales / c and c log2 e
+  const int32_t* cu_q;  // varlen prefix sums (token offsets, batch strides ignored), or nullptr
+  const int32_t* cu_k;
 };
 
-hipError_t launch_fwd_fp8(const Fp8Params& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int head_dim, bool softcap, hipStream_t stream);
 
 // Backward (dense layouts): dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
 struct BwdParams {

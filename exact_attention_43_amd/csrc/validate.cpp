@@ -187,29 +187,43 @@ exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d
   if (a->batch < 0) return fail(EXATTN_E_INVALID, "batch is negative");
   if (a->heads_q < 1 || a->heads_kv < 1) return fail(EXATTN_E_INVALID, "heads must be >= 1");
   if (a->heads_q % a->heads_kv != 0) return fail(EXATTN_E_INVALID, "heads_q is not a multiple of heads_kv");
-  if (a->cu_seqlens_q != nullptr || a->cu_seqlens_k != nullptr)
-    return fail(EXATTN_E_UNSUPPORTED, "the FP8 forward provides fixed lengths only");
-  if (a->seqlen_q < 0 || a->seqlen_k < 0) return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k is negative");
+  pl->varlen = a->cu_seqlens_q != nullptr;
+  if (pl->varlen != (a->cu_seqlens_k != nullptr))
+    return fail(EXATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_k must both be set or both NULL");
+  if (pl->varlen) {
+    if (a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
+      return fail(EXATTN_E_INVALID, "max_seqlen_q / max_seqlen_k is negative");
+    pl->s_q = a->max_seqlen_q;
+    pl->s_k = a->max_seqlen_k;
+  } else {
+    if (a->seqlen_q < 0 || a->seqlen_k < 0) return fail(EXATTN_E_INVALID, "seqlen_q / seqlen_k is negative");
+    pl->s_q = a->seqlen_q;
+    pl->s_k = a->seqlen_k;
+  }
   float scale_log2, cap_in, cap_out;
   bool cap;
   exattn_status st = resolve_scales(a->softmax_scale, a->softcap, a->head_dim, &scale_log2, &cap_in, &cap_out, &cap);
   if (st != EXATTN_OK) return st;
-  if (cap) return fail(EXATTN_E_UNSUPPORTED, "the FP8 forward does not provide softcap");
   float dq = 1.f, dk = 1.f, dv = 1.f;
   if (d != nullptr) dq = d->q, dk = d->k, dv = d->v;
   if (!isfinite(dq) || !isfinite(dk) || !isfinite(dv))
     return fail(EXATTN_E_INVALID, "descale factors must be finite");
+  // the kernel's scores are products of the codes: the descales fold into the scale
   pl->scale_log2 = scale_log2 * dq * dk;
   if (!isfinite(pl->scale_log2)) return fail(EXATTN_E_INVALID, "softmax_scale x descales overflows");
+  pl->softcap = cap;
+  pl->cap_in = cap_in * dq * dk;
+  pl->cap_out_log2 = cap_out;
+  if (!isfinite(pl->cap_in)) return fail(EXATTN_E_INVALID, "softmax_scale x descales / softcap overflows");
   pl->v_descale = dv;
   pl->head_dim = a->head_dim;
   pl->group = a->heads_q / a->heads_kv;
   pl->wl = a->window_left < 0 ? -1 : a->window_left;
   pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
-  pl->empty = a->batch == 0 || a->seqlen_q == 0;
+  pl->empty = a->batch == 0 || pl->s_q == 0;
   if (pl->empty) return EXATTN_OK;
   if (a->q == nullptr || a->o == nullptr) return fail(EXATTN_E_INVALID, "q or o is NULL");
-  if (a->seqlen_k > 0 && (a->k == nullptr || a->v == nullptr)) return fail(EXATTN_E_INVALID, "k or v is NULL");
+  if (pl->s_k > 0 && (a->k == nullptr || a->v == nullptr)) return fail(EXATTN_E_INVALID, "k or v is NULL");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return fail(EXATTN_E_INVALID, "q, k, v and o must be 16-byte aligned");
   const int64_t* s8[3] = {a->q_stride, a->k_stride, a->v_stride};
@@ -229,7 +243,7 @@ exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d
     if ((reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0) return fail(EXATTN_E_INVALID, "lse must be 4-byte aligned");
     if (a->lse_stride[0] < 0 || a->lse_stride[1] < 0) return fail(EXATTN_E_INVALID, "lse strides must be non-negative");
   }
-  const int64_t grid = (int64_t)a->batch * a->heads_q * (((int64_t)a->seqlen_q + 63) / 64);
+  const int64_t grid = (int64_t)a->batch * a->heads_q * (((int64_t)pl->s_q + 63) / 64);
   if (grid > 0x7fffffffLL) return fail(EXATTN_E_INVALID, "problem too large for one launch");
   return EXATTN_OK;
 }

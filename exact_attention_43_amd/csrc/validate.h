@@ -66,8 +66,11 @@ exattn_status check_append(const exattn_decode_args* a, const exattn_kv_new* n);
 // Checked FP8 forward arguments, resolved for the launch.
 struct Fp8Plan {
   bool empty = false;
+  bool softcap = false, varlen = false;
   int head_dim = 0, group = 1, wl = -1, wr = -1;
+  int s_q = 0, s_k = 0;  // lengths (fixed) or maxima (varlen)
   float scale_log2 = 0.f, v_descale = 1.f;
+  float cap_in = 0.f, cap_out_log2 = 0.f;  // softcap: scale x descales / c, and c log2 e
 };
 exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d, Fp8Plan* pl);
 

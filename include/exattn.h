@@ -314,8 +314,9 @@ exattn_status exattn_bwd(const exattn_bwd_args *args, void *workspace, size_t wo
  * lse as for exattn_fwd (or NULL).  The real inputs are code x descale, one
  * fp32 factor per tensor; S = softmax_scale q_descale k_descale (Q K^T) runs
  * on the FP8 MFMA, P V on the bf16 MFMA against V widened exactly from FP8,
- * and O is multiplied by v_descale.  Provided: fixed lengths, head_dim 64 and
- * 128, causal and window masks, GQA, no softcap (else EXATTN_E_UNSUPPORTED).
+ * and O is multiplied by v_descale.  Provided: head_dim 64 and 128 (else
+ * EXATTN_E_UNSUPPORTED), fixed lengths or varlen (cu_seqlens as for exattn_fwd),
+ * causal and window masks, GQA, softcap (on the scaled real scores, FAQ Q22).
  * Errors as for exattn_fwd; in addition q, k, v strides must be non-negative
  * multiples of 16 elements, o strides multiples of 8, and descale NULL or its
  * factors finite (EXATTN_E_INVALID).  descale NULL means all factors 1.

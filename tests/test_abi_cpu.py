@@ -265,8 +265,10 @@ def _f8(**kw):
 BAD_FP8 = [
     ("dtype bf16", dict(dtype=1), None, ex.EXATTN_E_UNSUPPORTED),
     ("head_dim 256", dict(head_dim=256), None, ex.EXATTN_E_UNSUPPORTED),
-    ("softcap", dict(softcap=20.0), None, ex.EXATTN_E_UNSUPPORTED),
-    ("varlen", dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE), None, ex.EXATTN_E_UNSUPPORTED),
+    ("nan softcap", dict(softcap=float("nan")), None, ex.EXATTN_E_INVALID),
+    ("varlen half", dict(cu_seqlens_q=FAKE), None, ex.EXATTN_E_INVALID),
+    ("varlen negative max", dict(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=-1), None,
+     ex.EXATTN_E_INVALID),
     ("stride not 16", dict(k_stride=[64 * 4 * 128, 4 * 128 + 8, 128]), None, ex.EXATTN_E_INVALID),
     ("odd o stride", dict(o_stride=[64 * 4 * 128, 4 * 128 + 4, 128]), None, ex.EXATTN_E_INVALID),
     ("null q", dict(q=None), None, ex.EXATTN_E_INVALID),
@@ -290,6 +292,11 @@ def test_fp8_rejects(L, name, kw, ds, status):
 def test_fp8_empty_and_fwd_refuses_fp8(L):
     assert L.exattn_fwd_fp8(C.byref(_f8(batch=0, q=None, o=None)), None, None) == ex.EXATTN_OK
     assert L.exattn_fwd_fp8(C.byref(_f8(seqlen_q=0)), None, None) == ex.EXATTN_OK
+    # softcap and packed sequences are provided: with nothing to compute the calls pass every
+    # check and launch nothing
+    assert L.exattn_fwd_fp8(C.byref(_f8(seqlen_q=0, softcap=30.0)), None, None) == ex.EXATTN_OK
+    assert L.exattn_fwd_fp8(C.byref(_f8(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, max_seqlen_q=0, max_seqlen_k=9)),
+                            None, None) == ex.EXATTN_OK
     assert L.exattn_fwd_fp8(None, None, None) == ex.EXATTN_E_INVALID
     assert L.exattn_fwd(C.byref(_f8()), None) == ex.EXATTN_E_UNSUPPORTED  # the 16-bit path takes no FP8
 

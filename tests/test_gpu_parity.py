@@ -728,6 +728,42 @@ FP8_CASES = [
 ]
 
 
+def _check_fp8(out, lse, q, k, v, ds, causal, window, cap, where):
+    """O and LSE of one FP8 call (4-D tensors, one batch entry or more) against the oracle on
+    the decoded inputs."""
+    dsq, dsk, dsv = ds
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    ro, rl = oracle.attention_fp8(q, k, v, q_descale=dsq, k_descale=dsk, v_descale=dsv, causal=causal,
+                                  window_size=window, softcap=cap)
+    # FAQ Q10's FP8 tolerance is for values at the codes' own scale: O is compared after
+    # dividing by v_descale (the real V is code x v_descale, so P's rounding moves O by
+    # amounts proportional to it).
+    assert_o_close(out.float() / dsv, np.nan_to_num(ro) / dsv, "fp8", f"{where} O")
+    # LSE: the FP8 MFMA sums its 16 products with a shorter mantissa than fp32 (a probe
+    # of 16-term dot products measured errors near 2^-15 of the sum of |products|), and a
+    # score takes d / 16 such sums, so a score may move by about (d / 16) 2^-15 of
+    # scale * sum_i |q_i k_i|; the LSE moves by at most the largest such move (the softcap
+    # c tanh(s / c) has slope at most 1, so it moves no more).  Bound per row:
+    # 1e-4 + 2^-11 * scale_eff * max_j sum_i |q_i k_i| (d = 128 gives 2^-12 per sum,
+    # times 2 in reserve).
+    qa = np.abs(oracle.decode_e4m3(q))
+    ka = np.abs(oracle.decode_e4m3(k))
+    g = hq // hkv
+    mag = np.stack([np.stack([(qa[bi, :, h] @ ka[bi, :, h // g].T).max(axis=1) if sk else np.zeros(sq)
+                              for h in range(hq)]) for bi in range(b)])  # (b, h, s_q)
+    scale_eff = abs(dsq * dsk) / math.sqrt(d)
+    lg = lse.detach().cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl)), f"{where} LSE: -inf pattern differs"
+    fin = ~np.isneginf(rl)
+    bound = 1e-4 + 2.0 ** -11 * scale_eff * mag
+    assert not np.isnan(lg).any()
+    err = np.zeros_like(rl)
+    err[fin] = np.abs(lg[fin] - rl[fin])  # -inf rows already matched exactly above
+    assert np.all(err[fin] <= bound[fin]), (f"{where} LSE: max err {err[fin].max():.3e}, "
+                                            f"worst err/bound {(err[fin] / bound[fin]).max():.3f}")
+
+
 @pytest.mark.parametrize("case", FP8_CASES, ids=[f"f{c[-1]}" for c in FP8_CASES])
 def test_fp8_forward(case):
     """The FP8 forward (bf16 out) against the oracle on the decoded inputs, FAQ Q10's FP8
@@ -742,32 +778,50 @@ def test_fp8_forward(case):
     torch.cuda.synchronize()
     assert out.dtype == torch.bfloat16
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
-    ro, rl = oracle.attention_fp8(q, k, v, q_descale=dsq, k_descale=dsk, v_descale=dsv, causal=causal,
-                                  window_size=window)
-    # FAQ Q10's FP8 tolerance is for values at the codes' own scale: O is compared after
-    # dividing by v_descale (the real V is code x v_descale, so P's rounding moves O by
-    # amounts proportional to it).
-    assert_o_close(out.float() / dsv, np.nan_to_num(ro) / dsv, "fp8", "fp8 O")
-    # LSE: the FP8 MFMA sums its 16 products with a shorter mantissa than fp32 (a probe
-    # of 16-term dot products measured errors near 2^-15 of the sum of |products|), and a
-    # score takes d / 16 such sums, so a score may move by about (d / 16) 2^-15 of
-    # scale * sum_i |q_i k_i|; the LSE moves by at most the largest such move.  Bound per
-    # row: 1e-4 + 2^-11 * scale_eff * max_j sum_i |q_i k_i| (d = 128 gives 2^-12 per
-    # sum, times 2 in reserve).
-    qa = np.abs(oracle.decode_e4m3(q))
-    ka = np.abs(oracle.decode_e4m3(k))
-    g = hq // hkv
-    mag = np.stack([np.stack([(qa[bi, :, h] @ ka[bi, :, h // g].T).max(axis=1) if sk else np.zeros(sq)
-                              for h in range(hq)]) for bi in range(b)])  # (b, h, s_q)
-    scale_eff = abs(dsq * dsk) / math.sqrt(d)
-    lg = lse.detach().cpu().numpy().astype(np.float64)
-    assert np.array_equal(np.isneginf(lg), np.isneginf(rl)), "fp8 LSE: -inf pattern differs"
-    fin = ~np.isneginf(rl)
-    bound = 1e-4 + 2.0 ** -11 * scale_eff * mag
-    assert not np.isnan(lg).any()
-    err = np.zeros_like(rl)
-    err[fin] = np.abs(lg[fin] - rl[fin])  # -inf rows already matched exactly above
-    assert np.all(err[fin] <= bound[fin]), f"fp8 LSE: max err {err[fin].max():.3e}, worst err/bound {(err[fin] / bound[fin]).max():.3f}"
+    _check_fp8(out, lse, q, k, v, (dsq, dsk, dsv), causal, window, 0.0, "fp8")
+
+
+FP8_CAP_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, causal, window, (q, k, v descale), softcap, seed
+    (2, 200, 200, 4, 4, 128, True, (-1, -1), (0.5, 2.0, 1.5), 30.0, 240),
+    (1, 130, 300, 8, 2, 64, False, (-1, -1), (1.0, 1.0, 1.0), 5.0, 241),
+    (1, 300, 300, 2, 2, 128, False, (50, 10), (2.0, 2.0, 0.5), 2.0, 242),       # saturating
+    (1, 2048, 2048, 32, 8, 128, True, (-1, -1), (0.5, 1.0, 2.0), 50.0, 243),  # kernel without the key split
+]
+
+
+@pytest.mark.parametrize("case", FP8_CAP_CASES, ids=[f"f{c[-1]}" for c in FP8_CAP_CASES])
+def test_fp8_softcap(case):
+    """The FP8 forward with softcap (FAQ Q20 with Q22) against the oracle on the decoded inputs."""
+    b, sq, sk, hq, hkv, d, causal, window, ds, cap, seed = case
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=seed, dtype=torch.float8_e4m3fn)
+    gq, gk, gv = _dev(q, k, v)
+    out, lse = ex.attn_func_fp8(gq, gk, gv, q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], causal=causal,
+                                window_size=window, softcap=cap)
+    torch.cuda.synchronize()
+    _check_fp8(out, lse, q, k, v, ds, causal, window, cap, "fp8 softcap")
+
+
+@pytest.mark.parametrize("causal,window,cap", [(True, (-1, -1), 0.0), (False, (40, 7), 0.0), (True, (256, 0), 50.0)])
+def test_fp8_varlen(causal, window, cap):
+    """The FP8 forward over packed sequences (FAQ Q8), ragged and empty ones included: each
+    sequence against the oracle on that sequence alone; rows past the packed total untouched."""
+    lens_q = [1, 0, 300, 129, 64, 77]
+    lens_k = [5, 3, 300, 1, 300, 77]
+    hq, hkv, d, ds = 8, 2, 128, (0.5, 2.0, 1.5)
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, hq, hkv, d, seed=244, dtype=torch.float8_e4m3fn)
+    gq, gk, gv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    out = torch.full((q.shape[0], hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((hq, q.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+    ex.attn_varlen_func_fp8(gq, gk, gv, dcq, dck, max(lens_q), max(lens_k), q_descale=ds[0], k_descale=ds[1],
+                            v_descale=ds[2], causal=causal, window_size=window, softcap=cap, out=out, lse=lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    for i in range(len(lens_q)):
+        a, e = int(cu_q[i]), int(cu_q[i + 1])
+        ka, ke = int(cu_k[i]), int(cu_k[i + 1])
+        _check_fp8(out[None, a:e], lse[None, :, a:e], q[None, a:e], k[None, ka:ke], v[None, ka:ke], ds, causal,
+                   window, cap, f"fp8 varlen seq {i}")
 
 
 def test_fp8_rejects_on_gpu():
