@@ -226,6 +226,26 @@ def test_pack_gqa(case):
         assert torch.equal(res[True][0], res[False][0]) and torch.equal(res[True][1], res[False][1])
 
 
+@pytest.mark.parametrize("hq,hkv,causal", [(2, 2, False), (4, 1, True)])
+def test_prefill_batch_past_grid_y_limit(hq, hkv, causal):
+    """More batch entries than a grid's y dimension holds (65535): the prefill indexes a
+    linear grid and decodes (batch, head) from the work-group id, plain or with packed GQA
+    (4 query heads of one KV head in one tile).  Sampled entries against the oracle."""
+    b, sq, sk, d = 65541, 3, 5, 64
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=215, dtype=torch.float16)
+    gq, gk, gv = _dev(q, k, v)
+    out = torch.full((b, sq, hq, d), float("nan"), dtype=torch.float16, device="cuda")
+    lse = torch.full((b, hq, sq), float("nan"), dtype=torch.float32, device="cuda")
+    ex.attn_func(gq, gk, gv, causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    idx = sorted({0, 1, 2, 65534, 65535, 65536, b - 1} | set(range(40000, 40040)))
+    ro, rl = oracle.attention(q[idx], k[idx], v[idx], causal=causal)
+    assert_o_close(out[idx].float().cpu(), ro, "fp16", "O")
+    assert_lse_close(lse[idx].cpu(), rl, "LSE")
+
+
+
 def test_pack_gqa_varlen():
     lens_q = [5, 0, 17, 64, 1]
     lens_k = [40, 3, 17, 300, 1]
