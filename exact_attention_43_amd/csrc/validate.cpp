@@ -412,10 +412,10 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
         return fail(EXATTN_E_INVALID, "backward strides must be non-negative multiples of 8 elements");
   if (a->lse_stride[1] < 0 || (!varlen && a->lse_stride[0] < 0))
     return fail(EXATTN_E_INVALID, "lse strides are negative");
-  // Q and dO tiles of 32 rows, K and V tiles of up to 64 keys, one head each.
+  // Q and dO tiles of 32 rows, K and V tiles of up to 128 keys, one head each.
   const char* bn[5] = {"q", "k", "v", "o", "dout"};
   for (int t = 0; t < 5; ++t) {
-    st = check_span(bn[t], 64, strides[t][1], 1, 0, a->head_dim, 2);
+    st = check_span(bn[t], t == 1 || t == 2 ? 128 : 64, strides[t][1], 1, 0, a->head_dim, 2);
     if (st != EXATTN_OK) return st;
   }
   if (rows > ((size_t)1 << 31) / 2) return fail(EXATTN_E_INVALID, "too many rows for one backward");

@@ -665,6 +665,10 @@ BWD_CAP_CASES = [
     (1, 1024, 1024, 16, 16, 128, torch.bfloat16, True, (-1, -1), 50.0, None, 234),
     (1, 200, 200, 4, 2, 256, torch.bfloat16, True, (-1, -1), 30.0, None, 237),
     (1, 150, 150, 2, 2, 256, torch.float16, False, (-1, -1), 2.0, -0.07, 238),  # saturating, negative scale
+    (1, 100, 150, 4, 2, 64, torch.bfloat16, True, (-1, -1), 10.0, None, 239),
+    # 1024 query tiles and more: the dQ kernel without the key split, with softcap
+    (1, 1024, 1024, 64, 16, 128, torch.bfloat16, True, (-1, -1), 30.0, None, 245),
+    (1, 2048, 2048, 32, 8, 64, torch.float16, False, (-1, -1), 20.0, None, 246),
 ]
 
 
