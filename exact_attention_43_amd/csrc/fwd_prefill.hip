@@ -104,7 +104,6 @@ prefill_kernel(const FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;   // KV-block group
   const int wg = wave & 3;     // wave within the group
-  const int gtid = tid & 255;  // thread index within the group
   const int hsel = lane >> 5;  // which 32-lane half
   const int l32 = lane & 31;
   uint8_t* gsm = smem + grp * GROUP_LDS;

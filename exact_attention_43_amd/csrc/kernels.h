@@ -127,6 +127,20 @@ struct BwdParams {
   const int32_t* cu_k;
 };
 
+// Key-split prefill (head_dim 128, fixed lengths): n_units = batch x h_q units
+// run n_wg work groups each; work group w of every unit runs the 4 slots
+// slot[4 w .. 4 w + 3].  A slot entry holds a 64-row query tile (bits 0-15),
+// its key group kg (bits 16-18) of kgn (bits 19-21) and a used bit (24); key
+// group kg takes the tile's 32-key blocks lo + kg, lo + kg + kgn, ...  The
+// kgn slots of a tile sit in one work group at consecutive positions, kg 0
+// first.  per_xcd = ceil(n_units n_wg / 8).
+struct SlotParams {
+  FwdParams f;
+  int32_t n_units, n_wg, per_xcd;
+  uint32_t slot[256];
+};
+hipError_t launch_prefill_slots(const SlotParams& sp, bool bf16, bool softcap, hipStream_t stream);
+
 int prefill_rows_per_tile();
 // groups: 1 or 2 groups of 4 waves per work group (d = 256 always uses 1).
 hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,

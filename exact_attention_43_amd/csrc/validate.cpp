@@ -4,7 +4,9 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 namespace exattn {
 namespace {
@@ -69,6 +71,16 @@ exattn_status resolve_scales(float softmax_scale, float softcap, int head_dim, f
 
 }  // namespace
 
+// Window edges as the kernels take them: < 0 unbounded, causal forces the
+// right edge to 0.  An edge that reaches past every key of every row (left >=
+// keys, right >= query rows) bounds nothing and is taken as unbounded: the
+// kernels add the edges to row and key positions in 32 bits.
+void window_edges(int32_t left, int32_t right, int32_t causal, int64_t rows, int64_t keys, int* wl,
+                  int* wr) {
+  *wl = left < 0 || left >= keys ? -1 : left;
+  *wr = causal ? 0 : (right < 0 || right >= rows ? -1 : right);
+}
+
 exattn_status fail(exattn_status st, const std::string& msg) {
   g_error = msg;
   return st;
@@ -120,8 +132,7 @@ exattn_status plan_fwd(const exattn_fwd_args* a, int rows_per_tile, FwdPlan* pl)
   pl->s_q = s_q;
   pl->s_k = s_k;
   pl->group = a->heads_q / a->heads_kv;
-  pl->wl = a->window_left < 0 ? -1 : a->window_left;
-  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  window_edges(a->window_left, a->window_right, a->causal, s_q, s_k, &pl->wl, &pl->wr);
   pl->empty = a->batch == 0 || s_q == 0;
   if (pl->empty) return EXATTN_OK;
 
@@ -218,8 +229,7 @@ exattn_status plan_fwd_fp8(const exattn_fwd_args* a, const exattn_fp8_descale* d
   pl->v_descale = dv;
   pl->head_dim = a->head_dim;
   pl->group = a->heads_q / a->heads_kv;
-  pl->wl = a->window_left < 0 ? -1 : a->window_left;
-  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  window_edges(a->window_left, a->window_right, a->causal, pl->s_q, pl->s_k, &pl->wl, &pl->wr);
   pl->empty = a->batch == 0 || pl->s_q == 0;
   if (pl->empty) return EXATTN_OK;
   if (a->q == nullptr || a->o == nullptr) return fail(EXATTN_E_INVALID, "q or o is NULL");
@@ -276,6 +286,74 @@ int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t se
   return (int32_t)(splits < 1 ? 1 : splits);
 }
 
+void tile_key_blocks(int t, int s_q, int s_k, int wl, int wr, int* lo, int* hi) {
+  const int64_t r0 = (int64_t)64 * t, r1 = std::min<int64_t>(r0 + 64, s_q) - 1;
+  const int64_t off = (int64_t)s_k - s_q;
+  int64_t kmin = 0, kmax = (int64_t)s_k - 1;
+  if (wl >= 0) kmin = std::max<int64_t>(0, r0 + off - wl);
+  if (wr >= 0) kmax = std::min<int64_t>(kmax, r1 + off + wr);
+  *lo = 0;
+  *hi = 0;
+  if (kmax >= kmin) {
+    *lo = (int)(kmin / 32);
+    *hi = (int)(kmax / 32 + 1);
+  }
+}
+
+bool build_slot_schedule(const int* w, int n64, int wg_max, SlotSchedule* out) {
+  *out = SlotSchedule{};
+  if (n64 < 1 || wg_max < 1) return false;
+  const int max_wg = std::min(wg_max, kMaxSlots / 4);
+  if (n64 > 4 * max_wg) return false;
+  std::vector<int> kg(n64);
+  auto load = [&](int t) { return (w[t] + kg[t] - 1) / kg[t]; };
+  // bins of 4 slots, first fit by decreasing kgn (ties: heavier first); returns
+  // the bin count and fills bin / position per tile
+  std::vector<int> order(n64), bin(n64), pos(n64);
+  auto pack = [&]() {
+    for (int t = 0; t < n64; ++t) order[t] = t;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return kg[x] != kg[y] ? kg[x] > kg[y] : w[x] > w[y]; });
+    std::vector<int> fill;
+    for (int t : order) {
+      int b = 0;
+      while (b < (int)fill.size() && fill[b] + kg[t] > 4) ++b;
+      if (b == (int)fill.size()) fill.push_back(0);
+      bin[t] = b;
+      pos[t] = fill[b];
+      fill[b] += kg[t];
+    }
+    return (int)fill.size();
+  };
+  // greedy: give a slot to the tile with the largest per-slot load while the
+  // slots last, then shrink the budget until the tiles pack into max_wg groups
+  for (int budget = 4 * max_wg; budget >= n64; --budget) {
+    for (int t = 0; t < n64; ++t) kg[t] = 1;
+    int used = n64;
+    while (used < budget) {
+      int best = -1;
+      for (int t = 0; t < n64; ++t)
+        if (kg[t] < 4 && w[t] > kg[t] && (best < 0 || load(t) > load(best))) best = t;
+      if (best < 0) break;
+      ++kg[best];
+      ++used;
+    }
+    const int n_wg = pack();
+    if (n_wg > max_wg) continue;
+    out->n_wg = n_wg;
+    int steps = 0;
+    for (int t = 0; t < n64; ++t) {
+      steps = std::max(steps, load(t));
+      for (int k = 0; k < kg[t]; ++k)
+        out->slot[4 * bin[t] + pos[t] + k] =
+            (uint32_t)t | ((uint32_t)k << 16) | ((uint32_t)kg[t] << 19) | (1u << 24);
+    }
+    out->steps = steps;
+    return true;
+  }
+  return false;
+}
+
 exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* pl) {
   if (a == nullptr || pl == nullptr) return fail(EXATTN_E_INVALID, "args is NULL");
   *pl = DecodePlan{};
@@ -298,8 +376,9 @@ exattn_status plan_decode(const exattn_decode_args* a, int num_cus, DecodePlan* 
   pl->n_hg = (int)((cols + 15) / 16);
   pl->hpw = decode_heads_per_group(a->head_dim, a->heads_kv);
   pl->n_hk = (int)(((int64_t)a->heads_kv + pl->hpw - 1) / pl->hpw);
-  pl->wl = a->window_left < 0 ? -1 : a->window_left;
-  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  // keys per batch entry are known on the device only: the left edge is kept
+  // (the kernel subtracts it), the right edge is bounded by the query tokens
+  window_edges(a->window_left, a->window_right, a->causal, pl->s_q, INT64_MAX, &pl->wl, &pl->wr);
   int64_t ns = a->num_splits == 0
                    ? auto_splits(a->batch, a->heads_q, a->heads_kv, a->seqlen_cache, a->head_dim,
                                  num_cus, pl->s_q)
@@ -389,8 +468,7 @@ exattn_status plan_bwd(const exattn_bwd_args* a, BwdPlan* pl) {
   pl->group = a->heads_q / a->heads_kv;
   pl->scale_log2 = scale_log2;
   pl->scale = scale_log2 / kLog2eHost;
-  pl->wl = a->window_left < 0 ? -1 : a->window_left;
-  pl->wr = a->causal ? 0 : (a->window_right < 0 ? -1 : a->window_right);
+  window_edges(a->window_left, a->window_right, a->causal, s_q, s_k, &pl->wl, &pl->wr);
   const size_t rows = (size_t)a->batch * (size_t)a->heads_q * (size_t)s_q;
   pl->ws_bytes = (rows * 8 + 255) & ~(size_t)255;  // (LSE log2 e, dO . O) per row
   pl->empty = a->batch == 0 || (s_q == 0 && s_k == 0);

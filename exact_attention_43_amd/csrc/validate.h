@@ -104,4 +104,22 @@ int decode_heads_per_group(int head_dim, int heads_kv);
 int32_t auto_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_k,
                     int32_t head_dim, int32_t num_cus, int32_t seqlen_q = 1);
 
+// Key-split prefill schedule (one (batch, head) unit; every unit runs the same).
+// A work group has 4 slots of 2 waves; a slot covers one 64-row query tile and
+// the key blocks kg, kg + kgn, kg + 2 kgn, ... of that tile's visible range
+// (kgn slots per tile, consecutive within one work group, 1 <= kgn <= 4).
+constexpr int kMaxSlots = 256;
+struct SlotSchedule {
+  int n_wg = 0;   // work groups per unit
+  int steps = 0;  // the largest per-slot block count
+  // per slot: tile (bits 0-15), kg (16-18), kgn (19-21), used (bit 24)
+  uint32_t slot[kMaxSlots] = {};
+};
+// Visible 32-key blocks [lo, hi) of 64-row query tile t (bottom-right causal /
+// window offsets; window edges < 0 unbounded).
+void tile_key_blocks(int t, int s_q, int s_k, int wl, int wr, int* lo, int* hi);
+// Builds the schedule for n64 tiles with w[t] visible blocks each, in at most
+// wg_max work groups per unit.  Returns false when the tiles do not fit.
+bool build_slot_schedule(const int* w, int n64, int wg_max, SlotSchedule* out);
+
 }  // namespace exattn

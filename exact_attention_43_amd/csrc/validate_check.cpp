@@ -16,6 +16,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
+#include <string>
+
 #include "validate.h"
 
 using namespace exattn;
@@ -120,6 +123,20 @@ void fill_dense_strides(int64_t st[3], int32_t s, int32_t h, int32_t d) {
   st[0] = stride_val(capped(capped(s, h), d));
 }
 
+// Window edges as planned: an edge inside the rows / keys is kept as given,
+// one that reaches past all of them is unbounded (-1), so that row + key
+// offset + edge stays within 32 bits in the kernels.
+template <class Args>
+void window_checks(const Args& a, int64_t s_q, int64_t s_k, int wl, int wr, const char* who, long it) {
+  const std::string w = who;
+  expect(wl < 0 || wl < s_k, (w + " left edge inside the keys").c_str(), it);
+  expect(wr < 0 || wr < std::max<int64_t>(s_q, 1), (w + " right edge inside the rows").c_str(), it);
+  if (a.window_left >= 0 && a.window_left < s_k) expect(wl == a.window_left, (w + " left edge kept").c_str(), it);
+  if (a.causal) expect(wr == 0, (w + " causal right edge").c_str(), it);
+  else if (a.window_right >= 0 && a.window_right < s_q)
+    expect(wr == a.window_right, (w + " right edge kept").c_str(), it);
+}
+
 void fwd_case(long it, Count& c, Count& c8) {
   exattn_fwd_args a{};
   a.dtype = dtype_val();
@@ -168,6 +185,7 @@ void fwd_case(long it, Count& c, Count& c8) {
       expect(!pl.pack || (int64_t)pl.s_q * pl.group < ((int64_t)1 << 22), "fwd pack bound", it);
       const int64_t units = (int64_t)a.batch * (pl.pack ? a.heads_kv : a.heads_q);
       expect(units * pl.n_qt == pl.grid, "fwd grid = units x tiles", it);
+      window_checks(a, pl.s_q, pl.s_k, pl.wl, pl.wr, "fwd", it);
     }
   } else {
     ++c.rejected;
@@ -184,6 +202,7 @@ void fwd_case(long it, Count& c, Count& c8) {
     if (!p8.empty) {
       expect(p8.group >= 1 && (int64_t)p8.group * a.heads_kv == a.heads_q, "fp8 group", it);
       expect(isfinite(p8.scale_log2) && isfinite(p8.v_descale), "fp8 scales finite", it);
+      window_checks(a, p8.s_q, p8.s_k, p8.wl, p8.wr, "fp8", it);
     }
   } else {
     ++c8.rejected;
@@ -317,6 +336,7 @@ void bwd_case(long it, Count& c) {
       const int64_t sq = a.cu_seqlens_q != nullptr ? a.max_seqlen_q : a.seqlen_q;
       expect(pl.ws_bytes % 256 == 0 && (int64_t)pl.ws_bytes >= 8 * (int64_t)a.batch * a.heads_q * sq,
              "bwd workspace holds 8 bytes per row", it);
+      window_checks(a, pl.s_q, pl.s_k, pl.wl, pl.wr, "bwd", it);
     }
   } else {
     ++c.rejected;
@@ -335,6 +355,51 @@ void splits_case(long it, Count& c) {
   ++c.ok;
 }
 
+void slots_case(long it, Count& c) {
+  const int n64 = chance(80) ? 1 + pick(64) : size_val(300);
+  const int wg_max = chance(80) ? 1 + pick(80) : size_val(100);
+  if (n64 < 1 || n64 > 1024) {
+    ++c.rejected;
+    return;
+  }
+  static int w[1024];
+  for (int t = 0; t < n64; ++t) w[t] = chance(10) ? 0 : pick(chance(50) ? 2 * (t + 1) + 1 : 300);
+  SlotSchedule sc;
+  if (!build_slot_schedule(w, n64, wg_max, &sc)) {
+    ++c.rejected;
+    expect(wg_max < 1 || n64 > 4 * std::min(wg_max, kMaxSlots / 4), "schedule refused a fitting case", it);
+    return;
+  }
+  ++c.ok;
+  expect(sc.n_wg >= 1 && sc.n_wg <= wg_max && sc.n_wg <= kMaxSlots / 4, "schedule work groups", it);
+  static int seen[1024];
+  for (int t = 0; t < n64; ++t) seen[t] = 0;
+  int steps = 0;
+  for (int s = 0; s < 4 * sc.n_wg; ++s) {
+    const uint32_t e = sc.slot[s];
+    if (!(e >> 24)) continue;
+    const int t = (int)(e & 0xffff), k = (int)((e >> 16) & 7), kn = (int)((e >> 19) & 7);
+    if (t >= n64 || kn < 1 || kn > 4 || k >= kn) {
+      expect(false, "schedule entry out of range", it);
+      continue;
+    }
+    // the tile's slots are consecutive and inside one work group
+    const int first = s - k;
+    expect(first >= 0 && first / 4 == (first + kn - 1) / 4, "tile slots share one work group", it);
+    ++seen[t];
+    steps = std::max(steps, (w[t] + kn - 1) / kn);
+  }
+  for (int t = 0; t < n64; ++t) {
+    const uint32_t e0 = [&] {
+      for (int s = 0; s < 4 * sc.n_wg; ++s)
+        if ((sc.slot[s] >> 24) && (int)(sc.slot[s] & 0xffff) == t && ((sc.slot[s] >> 16) & 7) == 0) return sc.slot[s];
+      return 0u;
+    }();
+    expect(e0 != 0 && seen[t] == (int)((e0 >> 19) & 7), "every tile has its kgn slots", it);
+  }
+  expect(steps == sc.steps, "schedule steps", it);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -346,16 +411,17 @@ int main(int argc, char** argv) {
     g_state = (z ^ (z >> 31)) | 1u;
   }
   Count fwd{"plan_fwd"}, fp8{"plan_fwd_fp8"}, dec{"plan_decode"}, app{"check_append"}, pg{"check_paged"},
-      bwd{"plan_bwd"}, spl{"auto_splits"};
+      bwd{"plan_bwd"}, spl{"auto_splits"}, slo{"slot_schedule"};
   for (long it = 0; it < iters; ++it) {
-    switch (it % 4) {
+    switch (it % 5) {
       case 0: fwd_case(it, fwd, fp8); break;
       case 1: decode_case(it, dec, app, pg); break;
       case 2: bwd_case(it, bwd); break;
+      case 3: slots_case(it, slo); break;
       default: splits_case(it, spl); break;
     }
   }
-  for (const Count* c : {&fwd, &fp8, &dec, &app, &pg, &bwd, &spl})
+  for (const Count* c : {&fwd, &fp8, &dec, &app, &pg, &bwd, &spl, &slo})
     printf("%-14s accepted %8ld rejected %8ld\n", c->name, c->ok, c->rejected);
   if (g_broken) printf("%d broken invariants\n", g_broken);
   return g_broken ? 1 : 0;

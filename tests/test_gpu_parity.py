@@ -122,11 +122,18 @@ def _dense_grid(b, s_q, h_q):
 
 
 def _launch(b, s_q, h_q, h_kv, d, masked, pack=False):
-    """The prefill launch the library picks (exattn_api.cpp): (groups, paired)."""
+    """The prefill launch the library picks (exattn_api.cpp) for fixed lengths:
+    (groups, paired, key-split).  The key-split kernel replaces the paired launch at
+    d = 128 without packing when that launch fills at most half of the CUs and the
+    schedule fits (at most one unit per CU and 4 slots per work group)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid = b * h_kv * math.ceil(s_q * (h_q // h_kv) / 128) if pack else _dense_grid(b, s_q, h_q)
     groups = 1 if d == 256 or grid >= 2 * cus else 2
-    return groups, groups == 2 and masked and grid <= cus
+    paired = groups == 2 and masked and grid <= cus
+    units = b * h_q
+    slots = (paired and 2 * grid <= cus and d == 128 and not pack and units <= cus
+             and math.ceil(s_q / 64) <= 4 * min(cus // units, 64))
+    return groups, paired and not slots, slots
 
 
 # Every instance of the prefill kernel template, each at a shape that makes the
@@ -137,7 +144,7 @@ INSTANCE_CASES = []
 for _dt in (torch.float16, torch.bfloat16):
     for _d in (64, 128, 256):
         for _cap in (0.0, 30.0):
-            for _kind in (("one",) if _d == 256 else ("one", "two", "paired")):
+            for _kind in (("one",) if _d == 256 else ("one", "two", "paired") + (("slots",) if _d == 128 else ())):
                 INSTANCE_CASES.append((_dt, _d, _cap, _kind))
 
 
@@ -159,19 +166,23 @@ def test_prefill_instances(case):
     idx = INSTANCE_CASES.index(case)
     # a negative scale: causal one-group and paired launches at d = 128, and the
     # two-group launches with softcap
-    neg = (d == 128 and kind in ("one", "paired")) or (kind == "two" and cap > 0)
+    neg = (d == 128 and kind in ("one", "paired", "slots")) or (kind == "two" and cap > 0)
     scale = -0.7 / math.sqrt(d) if neg else None
-    groups, paired = _launch(b, sq, hq, hkv, d, causal or window != (-1, -1))
-    want = {"one": (1, False), "two": (2, False), "paired": (2, True)}[kind]
+    # at d = 128 the paired kernel is reached through packed GQA (dense
+    # shapes take the key-split kernel there)
+    pack = kind == "paired" and d == 128
+    got = _launch(b, sq, hq, hkv, d, causal or window != (-1, -1), pack)
+    want = {"one": (1, False, False), "two": (2, False, False), "paired": (2, True, False),
+            "slots": (2, False, True)}[kind]
     if kind == "one" and d != 256:
         assert _dense_grid(b, sq, hq) >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
-    assert (groups, paired) == want, f"shape picks {(groups, paired)}, not {kind}"
+    assert got == want, f"shape picks {got}, not {kind}"
     q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=300 + idx, dtype=dt)
     dq, dk, dv = _dev(q, k, v)
     out = _poison_out(q.shape, dt)
     lse = _poison_lse((b, hq, sq))
     ex.attn_func(dq, dk, dv, causal=causal, window_size=window, softcap=cap, softmax_scale=scale,
-                 out=out, lse=lse)
+                 pack_gqa=1 if pack else 0, out=out, lse=lse)
     torch.cuda.synchronize()
     heads = sorted({0, hq // 2 + 1, hq - 1})
     o_ref, l_ref = oracle.attention(q, k, v, causal=causal, window_size=window, softcap=cap,
@@ -181,6 +192,55 @@ def test_prefill_instances(case):
     for h in heads:
         assert_o_close(o_cpu[:, :, h], o_ref[:, :, h], dt, f"{kind} d{d} cap{cap} h{h}")
         assert_lse_close(l_cpu[:, h], l_ref[:, h], f"{kind} d{d} cap{cap} h{h}")
+
+
+# Key-split launches (fwd_prefill_slots.hip): heavy query tiles are cut into up
+# to 4 slots of one work group that take every kgn-th 32-key block and merge at
+# the end.  The shapes vary the slot counts (few units: 4 slots per heavy tile;
+# many units: few slots per tile), the key ranges (ragged tails, s_q above and
+# below s_k, tiles that see no key, windows on either side, no keys at all) and
+# the arithmetic (fp16 / bf16, softcap, a negative scale, GQA).
+SLOT_CASES = [
+    # b, s_q, s_k, h_q, h_kv, dtype, causal, window, softcap, negative scale, seed
+    (1, 1000, 1000, 8, 8, torch.bfloat16, True, (-1, -1), 0.0, False, 600),    # ragged last tile
+    (2, 700, 300, 4, 2, torch.float16, True, (-1, -1), 0.0, False, 601),       # 400 rows see no key
+    (1, 300, 1000, 8, 4, torch.bfloat16, True, (-1, -1), 0.0, True, 602),      # s_q < s_k
+    (1, 1024, 1024, 8, 8, torch.float16, False, (100, 50), 0.0, False, 603),   # two-sided window
+    (2, 2048, 2048, 4, 4, torch.bfloat16, True, (300, -1), 0.0, False, 604),   # causal + left window
+    (1, 4096, 4096, 2, 1, torch.bfloat16, True, (-1, -1), 0.0, False, 605),    # 4 slots on heavy tiles
+    (8, 128, 128, 16, 4, torch.float16, True, (-1, -1), 0.0, False, 606),      # two work groups per unit
+    (4, 256, 256, 16, 4, torch.bfloat16, True, (20, -1), 0.0, False, 610),     # four per unit, window
+    (1, 1536, 1536, 4, 1, torch.bfloat16, True, (-1, -1), 20.0, True, 607),    # softcap, MQA
+    (3, 5, 5, 2, 2, torch.float16, True, (-1, -1), 0.0, False, 608),           # one tile, one block
+    (1, 100, 0, 2, 2, torch.bfloat16, True, (-1, -1), 0.0, False, 609),        # no keys
+]
+
+
+@pytest.mark.parametrize("case", SLOT_CASES, ids=[f"s{c[-1]}" for c in SLOT_CASES])
+def test_prefill_key_split(case):
+    """The key-split kernel against the oracle (every row of sampled heads), with
+    LSE and without, and bitwise equal over two runs (no atomics)."""
+    b, sq, sk, hq, hkv, dt, causal, window, cap, neg, seed = case
+    assert _launch(b, sq, hq, hkv, 128, True)[2], "shape does not take the key-split kernel"
+    scale = -0.9 / math.sqrt(128) if neg else None
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, 128, seed=seed, dtype=dt)
+    dq, dk, dv = _dev(q, k, v)
+    kw = dict(causal=causal, window_size=window, softcap=cap, softmax_scale=scale, pack_gqa=0)
+    out = _poison_out(q.shape, dt)
+    lse = _poison_lse((b, hq, sq))
+    ex.attn_func(dq, dk, dv, out=out, lse=lse, **kw)
+    out2 = _poison_out(q.shape, dt)
+    ex.attn_func(dq, dk, dv, out=out2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    heads = None if b * hq <= 16 else sorted({0, hq // 2 + 1, hq - 1})
+    kw.pop("pack_gqa")
+    o_ref, l_ref = oracle.attention(q, k, v, heads=heads, **kw)
+    o_cpu, l_cpu = out.cpu(), lse.cpu()
+    assert not torch.isnan(o_cpu).any()
+    for h in (range(hq) if heads is None else heads):
+        assert_o_close(o_cpu[:, :, h], o_ref[:, :, h], dt, f"key-split s{seed} h{h}")
+        assert_lse_close(l_cpu[:, h], l_ref[:, h], f"key-split s{seed} h{h}")
 
 
 # Packed GQA (FAQ Q15): the rows of all query heads of a KV head share the tiles.
@@ -222,7 +282,8 @@ def test_pack_gqa(case):
                 assert_o_close(o[:, :, h], o_ref[:, :, h], dt, f"pack={pack} h{h}")
                 assert_lse_close(l[:, h], l_ref[:, h], f"pack={pack} h{h}")
     masked = causal or window != (-1, -1)
-    if _launch(b, sq, hq, hkv, d, masked, True)[0] == _launch(b, sq, hq, hkv, d, masked, False)[0]:
+    on, off = _launch(b, sq, hq, hkv, d, masked, True), _launch(b, sq, hq, hkv, d, masked, False)
+    if on[0] == off[0] and not on[2] and not off[2]:
         assert torch.equal(res[True][0], res[False][0]) and torch.equal(res[True][1], res[False][1])
 
 
@@ -260,6 +321,35 @@ def test_pack_gqa_varlen():
     o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal=True)
     assert_o_close(out, o_ref, q.dtype, "pack varlen")
     assert_lse_close(lse, l_ref, "pack varlen")
+
+
+def test_window_edges_past_int32():
+    """Window edges that reach past every key (up to 2^31 - 1) bound nothing: every
+    entry point gives bitwise what the unbounded window gives (the kernels add
+    the edges to positions in 32 bits, so the planner takes such edges as
+    unbounded)."""
+    big = 2 ** 31 - 1
+    q, k, v = W.qkv(1, 300, 200, 4, 2, 128, seed=620, dtype=torch.bfloat16)
+    dq, dk, dv = _dev(q, k, v)
+    for win, ref in (((big, big), (-1, -1)), ((5, big), (5, -1)), ((big, 7), (-1, 7))):
+        o1, l1 = ex.attn_func(dq, dk, dv, window_size=win)
+        o2, l2 = ex.attn_func(dq, dk, dv, window_size=ref)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"fwd {win}"
+        do = torch.randn_like(o1)
+        g1 = ex.attn_backward(do, dq, dk, dv, o1, l1, window_size=win)
+        g2 = ex.attn_backward(do, dq, dk, dv, o2, l2, window_size=ref)
+        assert all(torch.equal(a, b) for a, b in zip(g1, g2)), f"bwd {win}"
+    f8 = [t.to(torch.float8_e4m3fn) for t in (dq, dk, dv)]
+    o1, l1 = ex.attn_func_fp8(*f8, window_size=(big, big))
+    o2, l2 = ex.attn_func_fp8(*f8, window_size=(-1, -1))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "fp8"
+    kc, vc = _dev(*W.qkv(2, 300, 300, 2, 2, 128, seed=621, dtype=torch.bfloat16)[1:])
+    qd = dq[:, :2].expand(2, 2, 4, 128).contiguous()
+    kc, vc = kc[:, :, :2].contiguous(), vc[:, :, :2].contiguous()
+    o1, l1 = ex.attn_with_kvcache(qd, kc, vc, window_size=(big, big))
+    o2, l2 = ex.attn_with_kvcache(qd, kc, vc, window_size=(-1, -1))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "decode"
 
 
 def test_zero_scale_is_uniform():

@@ -29,7 +29,7 @@ def test_plans_under_sanitizers(checker, seed):
     counts = {m.group(1): (int(m.group(2)), int(m.group(3)))
               for m in re.finditer(r"^(\w+)\s+accepted\s+(\d+)\s+rejected\s+(\d+)$", r.stdout, re.M)}
     assert set(counts) == {"plan_fwd", "plan_fwd_fp8", "plan_decode", "check_append", "check_paged",
-                           "plan_bwd", "auto_splits"}
+                           "plan_bwd", "auto_splits", "slot_schedule"}
     for name, (ok, rejected) in counts.items():
         # the draws reach both outcomes of every check
         assert ok > 100 and rejected > 100, (name, ok, rejected)
