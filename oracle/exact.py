@@ -268,13 +268,17 @@ def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=Fal
     tolerances: a sum whose terms carry a relative rounding error u is off by
     at most about u times the sum of its terms' absolute values (the classic
     forward error bound of a dot product), however much the terms cancel.
-    Written out through the backward's own sums: dS_ij = P_ij (dP_ij - sum_k
-    dO_ik O_ik) has terms of total size A_ij = P_ij (|dP_ij| + sum_k |dO_ik
-    O_ik|), times the softcap factor 1 - tanh^2(s_raw / c) when softcap c > 0
-    (P then from the capped scores), so the magnitudes returned are scale A |K|,
-    scale A^T |Q| and P^T |dO| (dQ, dK, dV), summed over grouped heads like the
-    gradients (the scale enters by its absolute value: these are sizes).  Each
-    is >= the matching |gradient|, with equality for dV where dO >= 0.
+    Written out through the backward's own sums, with every nested sum expanded
+    into its terms: dS_ij = P_ij (dP_ij - D_i), and D_i = sum_k dO_ik O_ik is
+    itself a sum over O_ik = sum_j' P_ij' V_j'k (the forward's output, which a
+    backward takes from the forward with the forward's rounding), so its terms
+    are dO_ik P_ij' V_j'k and dS_ij's terms have total size A_ij = P_ij (|dP_ij|
+    + sum_k |dO_ik| sum_j' P_ij' |V_j'k|), times the softcap factor
+    1 - tanh^2(s_raw / c) when softcap c > 0 (P then from the capped scores).
+    The magnitudes returned are scale A |K|, scale A^T |Q| and P^T |dO| (dQ, dK,
+    dV), summed over grouped heads like the gradients (the scale enters by its
+    absolute value: these are sizes).  Each is >= the matching |gradient|, with
+    equality for dV where dO >= 0.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b, s_q, h_q, d = q.shape
@@ -293,8 +297,8 @@ def attention_backward_magnitudes(q, k, v, do, *, softmax_scale=None, causal=Fal
             _, _, p = attend_head(q2, k2, v2, scale=scale, causal=causal, window_left=wl,
                                   window_right=wr, softcap=softcap, return_probs=True)
             dp = do2 @ v2.T
-            o2 = p @ v2
-            a = p * (np.abs(dp) + np.abs(do2 * o2).sum(axis=1, keepdims=True))
+            ov = p @ np.abs(v2)  # sum_j' P_ij' |V_j'k|: the size of O_ik's terms
+            a = p * (np.abs(dp) + (np.abs(do2) * ov).sum(axis=1, keepdims=True))
             if softcap is not None and softcap > 0.0:
                 t = np.tanh(scores(q2, k2, scale) / softcap)
                 a = a * (1.0 - t * t)

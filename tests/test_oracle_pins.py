@@ -523,8 +523,9 @@ def pin_backward():
 def pin_backward_magnitudes():
     """The term magnitudes bound the gradients from above; dV's equals dV where
     dO >= 0 (P >= 0); and on a tiny case they match the terms enumerated one by
-    one in scalar Python (probabilities from exp and fsum, every term of D, dP
-    and the three products listed and summed in absolute value)."""
+    one in scalar Python (probabilities from exp and fsum, every term of D with
+    O expanded into its terms P V, of dP and of the three products listed and
+    summed in absolute value)."""
     r = _rng(25)
     for s_q, s_k, h_q, h_kv, causal, win in ((7, 9, 4, 2, True, (-1, -1)), (6, 6, 2, 2, False, (2, 0))):
         q = r.standard_normal((2, s_q, h_q, 8))
@@ -560,8 +561,8 @@ def pin_backward_magnitudes():
             top = max(sc.values())
             z = math.fsum(math.exp(sc[j] - top) for j in keys)
             pr = {j: math.exp(sc[j] - top) / z for j in keys}
-            o = [math.fsum(pr[j] * v[0, j, 0, t] for j in keys) for t in range(d)]
-            dterms = math.fsum(abs(do[0, i, h, t] * o[t]) for t in range(d))
+            # D's terms dO_t P_j' V_j't, each listed
+            dterms = math.fsum(abs(do[0, i, h, t] * pr[jj] * v[0, jj, 0, t]) for t in range(d) for jj in keys)
             for j in keys:
                 dp = math.fsum(do[0, i, h, t] * v[0, j, 0, t] for t in range(d))
                 a = pr[j] * (abs(dp) + dterms)
@@ -596,8 +597,8 @@ def pin_backward_magnitudes():
             top = max(sc.values())
             z = math.fsum(math.exp(sc[j] - top) for j in keys)
             pr = {j: math.exp(sc[j] - top) / z for j in keys}
-            o = [math.fsum(pr[j] * v[0, j, 0, t] for j in keys) for t in range(d)]
-            dterms = math.fsum(abs(do[0, i, h, t] * o[t]) for t in range(d))
+            # D's terms dO_t P_j' V_j't, each listed
+            dterms = math.fsum(abs(do[0, i, h, t] * pr[jj] * v[0, jj, 0, t]) for t in range(d) for jj in keys)
             for j in keys:
                 dp = math.fsum(do[0, i, h, t] * v[0, j, 0, t] for t in range(d))
                 a = pr[j] * (abs(dp) + dterms) * (1.0 - math.tanh(raw[j] / cap) ** 2)
