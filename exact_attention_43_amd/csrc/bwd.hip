@@ -363,14 +363,22 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdParams p) {
   }
 }
 
-// dK, dV for 128 keys of one KV head with 8 waves (d = 128): two sets of 4
-// waves (32 keys each) take alternate (query head, query block) steps, each set
-// with its own double-buffered Q / dO stage.  K and V of the 128 keys are
-// loaded once into LDS and read there as the B operands, which leaves a wave
-// about 230 registers, so two waves share each SIMD: one wave's LDS reads and
-// exponentials run under the other's products.  The sets' partial dK, dV are
-// added through LDS at the end in a fixed order (deterministic).
-template <bool BF16, int D, bool SOFTCAP>
+// dK, dV for 32 x (8 / NSET) keys of one KV head with 8 waves (d = 128):
+// NSET sets of 8 / NSET waves (32 keys each) take turns over the (query head,
+// query block) steps, each set with its own double-buffered Q / dO stage.  K
+// and V of the keys are loaded once into LDS and read there as the B operands,
+// which leaves a wave about 230 registers, so two waves share each SIMD: one
+// wave's LDS reads and exponentials run under the other's products.  The sets'
+// partial dK, dV are added through LDS at the end in a fixed order
+// (deterministic).
+// NSET = 2: 128 keys per work group, the rows' statistics ride with the Q / dO
+// DMA.  NSET = 4: 64 keys, twice the work groups, issued heaviest first: under
+// a causal mask the first key tiles see the most query rows, and with more
+// work groups than CUs the dispatcher hands the light tiles to the CUs that
+// finish first (with 128-key tiles the grid is often one work group per CU and
+// the heaviest tile alone sets the time).  The 4 sets' stages fill the 160 KiB
+// of LDS, so the statistics come from memory into registers instead.
+template <bool BF16, int D, bool SOFTCAP, int NSET>
 __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
   using E = Elem<BF16>;
   constexpr int KS = D / 16;                   // k-steps over head_dim
@@ -379,12 +387,16 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
   constexpr int TILE = kBwdRows * D * 2;       // bytes of a Q (or dO) tile
   constexpr int ROWS_PER_KB = 1024 / (D * 2);  // rows per 1 KiB DMA slice
   constexpr int SLICES = TILE / 1024;          // DMA slices per Q tile
-  constexpr int STAGE = 2 * TILE + 2 * 128;    // Q, dO, lse2[32], D[32]
-  constexpr int KVT = kBwdKeys * D * 2;        // bytes of the K (or V) tile
+  static_assert(NSET == 2 || NSET == 4, "2 or 4 sets");
+  constexpr int WPS = 8 / NSET;                // waves per set
+  constexpr int KEYS = 32 * WPS;               // keys per work group
+  constexpr bool kStatsLds = NSET == 2;        // statistics through LDS (else from memory)
+  constexpr int STAGE = 2 * TILE + (kStatsLds ? 2 * 128 : 0);  // Q, dO (, lse2[32], D[32])
+  constexpr int KVT = KEYS * D * 2;            // bytes of the K (or V) tile
   constexpr int KVSL = KVT / 1024;             // DMA slices per K tile
-  static_assert(SLICES % 4 == 0 && KVSL % 8 == 0, "slices per wave");
-  constexpr int LDS_MAIN = 2 * KVT + 2 * 2 * STAGE;
-  constexpr int LDS_RED = 4 * 2 * DT * 16 * 64 * 4;  // set 1's dK and dV partials
+  static_assert(SLICES % WPS == 0 && KVSL % 8 == 0, "slices per wave");
+  constexpr int LDS_MAIN = 2 * KVT + NSET * 2 * STAGE;
+  constexpr int LDS_RED = 4 * 2 * DT * 16 * 64 * 4;  // 4 waves' dK and dV partials
   constexpr int LDS = LDS_MAIN > LDS_RED ? LDS_MAIN : LDS_RED;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
@@ -392,32 +404,40 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int set = wave >> 2;  // which alternate steps
-  const int w4 = wave & 3;    // which 32 keys
+  const int set = wave / WPS;  // which steps: set, set + NSET, ...
+  const int w4 = wave % WPS;   // which 32 keys
   const int hsel = lane >> 5;
   const int l32 = lane & 31;
 
-  const int n_kt = (p.s_k + kBwdKeys - 1) / kBwdKeys;
+  const int n_kt = (p.s_k + KEYS - 1) / KEYS;
   const int bid = blockIdx.x;
-  const int kt = bid % n_kt;
-  const int hk = (bid / n_kt) % p.h_kv;
-  const int b = bid / (n_kt * p.h_kv);
+  int kt, hk, b;
+  if constexpr (NSET == 2) {
+    kt = bid % n_kt;
+    hk = (bid / n_kt) % p.h_kv;
+    b = bid / (n_kt * p.h_kv);
+  } else {  // key tiles major: tile 0 of every (batch, KV head) first
+    const int units = p.batch * p.h_kv;
+    kt = bid / units;
+    hk = bid % units % p.h_kv;
+    b = bid % units / p.h_kv;
+  }
   const SeqSpan sp = seq_span(p, b);
   const int sq = sp.sq, sk = sp.sk, off = sk - sq;
   const int sqm = p.s_q;  // row stride of the statistics (the longest sequence)
-  const int k0 = kt * kBwdKeys;
+  const int k0 = kt * KEYS;
   if (k0 >= sk) return;  // uniform: a shorter sequence has no keys here
   const int kcol = k0 + 32 * w4 + l32;  // this lane's key
 
-  // ---- K and V of the 128 keys into LDS (row = key, chunk c at c ^ kswz(key)),
+  // ---- K and V of the keys into LDS (row = key, chunk c at c ^ kswz(key)),
   // 1 KiB slices, slice wave + 8 i by each wave; keys past the end read as 0.
   uint8_t* const kt_lds = smem;
   uint8_t* const vt_lds = smem + KVT;
   {
     const __amdgpu_buffer_rsrc_t rk =
-        block_rsrc<D>(p.k + sp.k + (int64_t)hk * p.k_sh, p.k_ss, k0, sk, kBwdKeys);
+        block_rsrc<D>(p.k + sp.k + (int64_t)hk * p.k_sh, p.k_ss, k0, sk, KEYS);
     const __amdgpu_buffer_rsrc_t rv =
-        block_rsrc<D>(p.v + sp.v + (int64_t)hk * p.v_sh, p.v_ss, k0, sk, kBwdKeys);
+        block_rsrc<D>(p.v + sp.v + (int64_t)hk * p.v_sh, p.v_ss, k0, sk, KEYS);
 #pragma unroll
     for (int i = 0; i < KVSL / 8; ++i) {
       const int sl = wave + 8 * i;
@@ -428,8 +448,8 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
     }
   }
 
-  // ---- query rows that see any of keys k0 .. k0 + 127 (per head the same).
-  const int k1 = min(k0 + kBwdKeys, sk) - 1;
+  // ---- query rows that see any of keys k0 .. k0 + KEYS - 1 (per head the same).
+  const int k1 = min(k0 + KEYS, sk) - 1;
   const int wr = p.wr;
   int i_lo = 0, i_hi = sq - 1;
   if (wr >= 0) i_lo = max(0, k0 - off - wr);
@@ -438,33 +458,40 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
   const int qb_hi = i_hi >= i_lo ? i_hi / kBwdRows + 1 : qb_lo;  // exclusive
   const int nqb = qb_hi - qb_lo;
   const int g = p.group;
-  const int steps = nqb * g;  // (head, query block) pairs; set s takes s, s + 2, ...
+  const int steps = nqb * g;  // (head, query block) pairs; set s takes s, s + NSET, ...
 
   // ---- Q / dO DMA of this set: tile row r, stored chunk (lane % DCH) at
-  // r * D * 2 + 16 * ((lane % DCH) ^ qswz(r)); slices w4 + 4 i.
-  uint32_t q_ofs[SLICES / 4], d_ofs[SLICES / 4];
+  // r * D * 2 + 16 * ((lane % DCH) ^ qswz(r)); slices w4 + WPS i.
+  uint32_t q_ofs[SLICES / WPS], d_ofs[SLICES / WPS];
 #pragma unroll
-  for (int i = 0; i < SLICES / 4; ++i) {
-    const int row = (4 * i + w4) * ROWS_PER_KB + lane / DCH;
+  for (int i = 0; i < SLICES / WPS; ++i) {
+    const int row = (WPS * i + w4) * ROWS_PER_KB + lane / DCH;
     q_ofs[i] = (uint32_t)(row * p.q_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
     d_ofs[i] = (uint32_t)(row * p.do_ss + 8 * ((lane % DCH) ^ qswz<D>(row))) * 2u;
   }
   const uint16_t* const qb_ptr = p.q + sp.q;
   const uint16_t* const db_ptr = p.dout + sp.dout;
   const float* const sb_ptr = p.ws_stats + (int64_t)b * p.h_q * sqm * 2;
+  // the (lse2, D) pairs of step st's 32 rows; rows past the end read as 0
+  auto stats_rsrc = [&](int st) {
+    const int h = hk * g + st / nqb;
+    const int q0 = (qb_lo + st % nqb) * kBwdRows;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(sb_ptr + ((int64_t)h * sqm + q0) * 2), 0,
+                                             8 * min(kBwdRows, sq - q0), 0x00020000);
+  };
   auto issue = [&](int st, uint8_t* dst) {
     const int h = hk * g + st / nqb;
     const int q0 = (qb_lo + st % nqb) * kBwdRows;
     const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qb_ptr + (int64_t)h * p.q_sh, p.q_ss, q0, sq, kBwdRows);
     const __amdgpu_buffer_rsrc_t rd = block_rsrc<D>(db_ptr + (int64_t)h * p.do_sh, p.do_ss, q0, sq, kBwdRows);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(sb_ptr + ((int64_t)h * sqm + q0) * 2), 0, 8 * min(kBwdRows, sq - q0), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < SLICES / 4; ++i) {
-      buffer_load_lds16(rq, dst + (4 * i + w4) * 1024, q_ofs[i]);
-      buffer_load_lds16(rd, dst + TILE + (4 * i + w4) * 1024, d_ofs[i]);
+    for (int i = 0; i < SLICES / WPS; ++i) {
+      buffer_load_lds16(rq, dst + (WPS * i + w4) * 1024, q_ofs[i]);
+      buffer_load_lds16(rd, dst + TILE + (WPS * i + w4) * 1024, d_ofs[i]);
     }
-    if (w4 == 0 && lane < 16) buffer_load_lds16(rs, dst + 2 * TILE, 16u * lane);
+    if constexpr (kStatsLds) {
+      if (w4 == 0 && lane < 16) buffer_load_lds16(stats_rsrc(st), dst + 2 * TILE, 16u * lane);
+    }
   };
 
   // ---- loop-invariant LDS addresses.
@@ -503,13 +530,24 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
     const uint8_t* dt_ = stg + TILE;
     const float* stats = reinterpret_cast<const float*>(stg + 2 * TILE);  // (lse2, D) per row
     const int q0 = (qb_lo + st % nqb) * kBwdRows;
+    // from memory: rows 16 c + 8 hsel + 2 j, + 1 as (lse2, D, lse2, D), issued
+    // now and first needed after the products
+    f32x4_t rsm[2][4];
+    if constexpr (!kStatsLds) {
+      const __amdgpu_buffer_rsrc_t rsr = stats_rsrc(st);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          rsm[c][j] = __builtin_bit_cast(f32x4_t, buffer_load16(rsr, (uint32_t)(8 * (16 * c + 8 * hsel + 2 * j))));
+    }
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = E::mfma32x32x16(*(const u32x4_t*)(qt + aaddr[ks]), *(const u32x4_t*)(kt_lds + baddr[ks]), s);
       dp = E::mfma32x32x16(*(const u32x4_t*)(dt_ + aaddr[ks]), *(const u32x4_t*)(vt_lds + baddr[ks]), dp);
     }
-    if (st + 2 < steps) issue(st + 2, nxt);
+    if (st + NSET < steps) issue(st + NSET, nxt);
     const int kc0 = k0 + 32 * w4;
     const bool full = q0 + kBwdRows <= sq && kc0 + 32 <= sk && (wr < 0 || kc0 + 31 <= q0 + off + wr) &&
                       (p.wl < 0 || kc0 >= q0 + kBwdRows - 1 + off - p.wl);
@@ -519,7 +557,12 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
       const int qi = 16 * c + 8 * hsel;
       f32x4_t rs[4];  // rows qi + 2 j, qi + 2 j + 1: (lse2, D, lse2, D)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rs[j] = *(const f32x4_t*)(stats + 2 * (qi + 2 * j));
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (kStatsLds)
+          rs[j] = *(const f32x4_t*)(stats + 2 * (qi + 2 * j));
+        else
+          rs[j] = rsm[c][j];
+      }
       float pv[8], sv[8], fv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) probs<SOFTCAP>(s[8 * c + u], rs[u >> 1][2 * (u & 1)], p, pv[u], fv[u]);
@@ -560,47 +603,66 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
   if (set < steps) issue(set, st0);
   // every wave runs the same number of iterations and meets every barrier;
   // the first barrier also publishes the K and V tiles
-  const int iters = (steps + 1) / 2;
+  const int iters = (steps + NSET - 1) / NSET;
   for (int t = 0; t < iters; t += 2) {
     wait_vmem_all();
     __syncthreads();
-    if (set + 2 * t < steps) block(set + 2 * t, st0, st1);
+    if (set + NSET * t < steps) block(set + NSET * t, st0, st1);
     if (t + 1 < iters) {
       wait_vmem_all();
       __syncthreads();
-      if (set + 2 * (t + 1) < steps) block(set + 2 * (t + 1), st1, st0);
+      if (set + NSET * (t + 1) < steps) block(set + NSET * (t + 1), st1, st0);
     }
   }
   wait_vmem_all();  // the K / V DMA when there was no step
 
-  // ---- set 1 hands its partial dK^T, dV^T to set 0 through LDS (everything
-  // in LDS is free once every wave has passed the barrier).
+  // ---- the sets hand their partial dK^T, dV^T on through LDS (everything in
+  // LDS is free once every wave has passed the barrier): with 2 sets set 1 to
+  // set 0; with 4 sets 2 -> 0 and 3 -> 1, then 1 -> 0, so the sum is always
+  // (s0 + s2) + (s1 + s3).
   __syncthreads();
-  float* const red = reinterpret_cast<float*>(smem);  // [w4][dk, dv][dt][j][lane][4]
-  auto slot = [&](int which, int dt, int j) { return red + ((((w4 * 2 + which) * DT + dt) * 4 + j) * 64 + lane) * 4; };
-  if (set == 1) {
+  float* const red = reinterpret_cast<float*>(smem);  // [publishing wave][dk, dv][dt][j][lane][4]
+  auto slot = [&](int pw, int which, int dt, int j) {
+    return red + ((((pw * 2 + which) * DT + dt) * 4 + j) * 64 + lane) * 4;
+  };
+  auto publish = [&](int pw) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        *(f32x4_t*)slot(0, dt, j) = f32x4_t{dk[dt][4 * j], dk[dt][4 * j + 1], dk[dt][4 * j + 2], dk[dt][4 * j + 3]};
-        *(f32x4_t*)slot(1, dt, j) = f32x4_t{dv[dt][4 * j], dv[dt][4 * j + 1], dv[dt][4 * j + 2], dv[dt][4 * j + 3]};
+        *(f32x4_t*)slot(pw, 0, dt, j) = f32x4_t{dk[dt][4 * j], dk[dt][4 * j + 1], dk[dt][4 * j + 2], dk[dt][4 * j + 3]};
+        *(f32x4_t*)slot(pw, 1, dt, j) = f32x4_t{dv[dt][4 * j], dv[dt][4 * j + 1], dv[dt][4 * j + 2], dv[dt][4 * j + 3]};
       }
+  };
+  auto absorb = [&](int pw) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t a = *(const f32x4_t*)slot(pw, 0, dt, j);
+        const f32x4_t c = *(const f32x4_t*)slot(pw, 1, dt, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[dt][4 * j + e] += a[e];
+          dv[dt][4 * j + e] += c[e];
+        }
+      }
+  };
+  if constexpr (NSET == 4) {
+    if (set >= 2) publish(wave - 4);  // waves 4-7: slots 0-3
+    __syncthreads();
+    if (set < 2) absorb(wave);  // wave w (set 0 or 1) takes wave w + 4's partial
+    __syncthreads();
+    if (set == 1) publish(w4);
+    __syncthreads();
+    if (set != 0) return;
+    absorb(w4);
+  } else {
+    if (set == 1) publish(w4);
+    __syncthreads();
+    if (set != 0) return;
+    absorb(w4);
   }
-  __syncthreads();
-  if (set != 0) return;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4_t a = *(const f32x4_t*)slot(0, dt, j);
-      const f32x4_t c = *(const f32x4_t*)slot(1, dt, j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dk[dt][4 * j + e] += a[e];
-        dv[dt][4 * j + e] += c[e];
-      }
-    }
 
   // ---- dK = scale (dK^T)^T, dV = (dV^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3.
   if (kcol < sk) {
@@ -877,12 +939,22 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     // at the causal training shape and longer sequences); d = 64: the 4-wave one,
     // whose work groups already share a CU two at a time (the 8-wave kernel
     // measured 6% slower there); d = 256: the 4-wave one in two head-dim slices.
+    // At d = 128 a mask bounded on one side only (causal, or one window edge)
+    // makes the key tiles' work uneven: 64-key tiles in 4 sets then (whole
+    // backward 10-18% faster at causal shapes); otherwise 128-key tiles in 2
+    // sets, which read each Q / dO block for twice the keys (the 64-key tiles
+    // measured 7% slower without a mask).
     if constexpr (D == 256)
       hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, SOFTCAP, 2>), dim3(n_kt * p.h_kv * p.batch * 2), dim3(256), 0,
                          stream, p);
-    else if constexpr (D == 128)
-      hipLaunchKernelGGL((bwd_dkdv2_kernel<BF16, D, SOFTCAP>), dim3(n_kt * p.h_kv * p.batch), dim3(512), 0,
-                         stream, p);
+    else if constexpr (D == 128) {
+      if ((p.wr >= 0) != (p.wl >= 0))
+        hipLaunchKernelGGL((bwd_dkdv2_kernel<BF16, D, SOFTCAP, 4>), dim3(((p.s_k + 63) / 64) * p.h_kv * p.batch),
+                           dim3(512), 0, stream, p);
+      else
+        hipLaunchKernelGGL((bwd_dkdv2_kernel<BF16, D, SOFTCAP, 2>), dim3(n_kt * p.h_kv * p.batch), dim3(512), 0,
+                           stream, p);
+    }
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, SOFTCAP, 1>), dim3(n_kt * p.h_kv * p.batch), dim3(256), 0,
                          stream, p);

@@ -47,10 +47,8 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
   constexpr int XM = 8 * 2 * 64 * 4;         // every wave's (m, l)
   constexpr int LDS = 4 * SLOT_LDS > XO + XM ? 4 * SLOT_LDS : XO + XM;
   static_assert(LDS <= 160 * 1024 && 4 * 64 * D * 2 <= LDS, "LDS budget (stages, partials, O tile)");
-  static_assert(sizeof(SlotParams) % 4 == 0, "kernel-argument dwords");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
-  // every kernel-argument line (the schedule included) in one batch of scalar loads
-  prefetch_kernargs<sizeof(SlotParams)>();
+  static_assert(offsetof(SlotParams, slot) % 16 == 0, "a work group's 4 entries are one 16-byte load");
   const FwdParams p = sp.f;
 
   const int tid = threadIdx.x;
@@ -95,14 +93,14 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
     kgn = max(1, (int)((e >> 19) & 7u));
     return ((e >> 24) & 1u) && hi - lo > kg ? (hi - lo - kg + kgn - 1) / kgn : 0;
   };
-  const uint32_t* const wg_slots = sp.slot + 4 * wgi;
+  const u32x4_t wg_slots = *reinterpret_cast<const u32x4_t*>(sp.slot + 4 * wgi);
   int steps = 0;  // the work group's longest slot (uniform)
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     int lo_, kg_, kgn_;
     steps = max(steps, slot_blocks(wg_slots[s], lo_, kg_, kgn_));
   }
-  const uint32_t e = wg_slots[slot];
+  const uint32_t e = slot == 0 ? wg_slots[0] : slot == 1 ? wg_slots[1] : slot == 2 ? wg_slots[2] : wg_slots[3];
   const bool used = (e >> 24) & 1u;
   const int tile = (int)(e & 0xffffu);
   int lo, kg, kgn;
@@ -390,7 +388,8 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
   for (int it = 0; it < 4 * 64 * DCH / 512; ++it) {
     const int idx = it * 512 + tid;
     const int row = idx / DCH, chunk = idx % DCH;
-    const uint32_t es = wg_slots[row >> 6];
+    const int rs = row >> 6;
+    const uint32_t es = rs == 0 ? wg_slots[0] : rs == 1 ? wg_slots[1] : rs == 2 ? wg_slots[2] : wg_slots[3];
     const int grow = 64 * (int)(es & 0xffffu) + (row & 63);
     if (((es >> 24) & 1u) && ((es >> 16) & 7u) == 0 && grow < sq) {
       const u32x4_t v = *(const u32x4_t*)(smem + row * OROW + 16 * (chunk ^ kswz<D>(row)));

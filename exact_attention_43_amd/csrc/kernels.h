@@ -136,8 +136,8 @@ struct BwdParams {
 // first.  per_xcd = ceil(n_units n_wg / 8).
 struct SlotParams {
   FwdParams f;
-  int32_t n_units, n_wg, per_xcd;
-  uint32_t slot[256];
+  int32_t n_units, n_wg, per_xcd, pad;
+  alignas(16) uint32_t slot[256];  // starts at byte 256: a work group's 4 entries are one 16-byte load
 };
 hipError_t launch_prefill_slots(const SlotParams& sp, bool bf16, bool softcap, hipStream_t stream);
 

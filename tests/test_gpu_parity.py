@@ -715,6 +715,9 @@ BWD_CASES = [
     (1, 1, 513, 4, 2, 128, torch.bfloat16, True, (-1, -1), 205),      # one row
     (1, 77, 40, 4, 2, 64, torch.float16, False, (5, -1), 206),        # left window only
     (2, 1024, 1024, 16, 16, 128, torch.bfloat16, True, (-1, -1), 207),  # the causal training shape
+    # d = 128 with a mask bounded on one side: 64-key dK/dV tiles in 4 sets
+    (1, 300, 700, 8, 2, 128, torch.bfloat16, False, (120, -1), 215),   # left window only
+    (2, 333, 900, 6, 3, 128, torch.float16, True, (-1, -1), 216),      # s_q < s_k, ragged last tile
     # 1024 query tiles and more: the dQ kernel without the key split
     (1, 2048, 2048, 32, 8, 64, torch.bfloat16, True, (-1, -1), 209),
     (1, 1024, 1024, 64, 16, 128, torch.float16, False, (-1, -1), 210),
