@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
-#include <string.h>
 
 #include <mutex>
 #include <set>
@@ -137,13 +136,14 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     // Where the paired launch would fill at most half of the CUs at d = 128
     // (fixed lengths, one tile per query head), the key-split kernel runs
     // instead: it spreads the heavy tiles' key blocks over the idle CUs and
-    // keeps two busy waves on every SIMD (measured 6-13% faster there; at
-    // about one work group per CU the paired launch measured faster).
+    // keeps two busy waves on every SIMD (measured 12-16% faster there).  At
+    // about one work group per CU the paired launch measured faster, also
+    // against a key-split schedule of the paired launch's size.
     SlotSchedule sch;
     bool slots = false;
     const int64_t units = (int64_t)a->batch * a->heads_q;
     if (p.pair_tiles && 2 * (int64_t)pl.grid <= cus && pl.head_dim == 128 && !pl.varlen && !pl.pack &&
-        units <= cus)
+        units <= cus && a->batch <= 65535)
       slots = slot_schedule(pl.s_q, pl.s_k, pl.wl, pl.wr, cus / (int)units, &sch);
     if (debug_level() >= 1) {
       char buf[256];
@@ -157,13 +157,14 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     }
     hipError_t e;
     if (slots) {
-      static_assert(sizeof(SlotParams::slot) == sizeof(SlotSchedule::slot), "slot table");
+      static_assert(sizeof(SlotParams::slot) == 2 * sizeof(SlotSchedule::slot), "slot table");
       SlotParams sp{};
       sp.f = p;
-      sp.n_units = (int32_t)units;
       sp.n_wg = sch.n_wg;
-      sp.per_xcd = (int32_t)((units * sch.n_wg + 7) / 8);
-      memcpy(sp.slot, sch.slot, sizeof sp.slot);
+      for (int i = 0; i < 4 * sch.n_wg; ++i) {
+        sp.slot[2 * i] = sch.slot[i];
+        sp.slot[2 * i + 1] = sch.nb[i];
+      }
       e = launch_prefill_slots(sp, pl.bf16, pl.softcap, static_cast<hipStream_t>(stream));
     } else {
       e = launch_prefill(p, pl.bf16, pl.head_dim, pl.softcap, pl.grid, groups, static_cast<hipStream_t>(stream));

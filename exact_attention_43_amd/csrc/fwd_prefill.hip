@@ -108,6 +108,31 @@ prefill_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   uint8_t* gsm = smem + grp * GROUP_LDS;
 
+  // ---- fast start for dense launches with one tile per query head on the
+  // (unit, batch, tile) grid: the Q loads go out first, addressed from the
+  // block index and a few kernel arguments, ahead of the rest of the set-up
+  // (the general path below reaches them after a few hundred scalar
+  // instructions and dependent loads of kernel arguments).  Same rows and
+  // values as the general path.
+  u32x4_t qf[KS];
+  const bool fast_q = p.grid3 != 0 && p.pack == 0 && p.cu_q == nullptr;
+  if (fast_q) {
+    const int qt_ = p.n_qt - 1 - (int)blockIdx.z;
+    const int n64_ = (p.s_q + 63) / 64;
+    const int ta = PAIR ? qt_ : 2 * qt_, tb = PAIR ? n64_ - 1 - qt_ : 2 * qt_ + 1;
+    const bool a_ = PAIR ? (wg >> 1) == grp : wg < 2;
+    const int row = 64 * (a_ ? ta : tb) + 32 * (wg & 1) + l32;
+    if (2 * qt_ < n64_ && (a_ || (tb > ta && tb < n64_)) && row < p.s_q) {
+      const uint16_t* qp = p.q + (int64_t)blockIdx.y * p.q_sb + (int64_t)blockIdx.x * p.q_sh +
+                           (int64_t)row * p.q_ss + 8 * hsel;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+
   // ---- tile scheduler: heaviest query tiles first; (batch, head) fastest.
   // Packed GQA (p.pack): a unit is one KV head, and its tiles hold the rows of
   // all `group` query heads that read it, head fastest: virtual row R is
@@ -205,14 +230,15 @@ prefill_kernel(const FwdParams p) {
   const int qrow = q0 + 32 * (wg & 1) + l32;  // virtual row of this lane
   const int qpos = vpos(qrow);                 // its position
   const int qhead = h + vhead(qrow);           // its query head
-  u32x4_t qf[KS];
-  if (my_valid && qrow < sqv) {
-    const uint16_t* qp = p.q + qoff + (int64_t)qhead * p.q_sh + (int64_t)qpos * p.q_ss + 8 * hsel;
+  if (!fast_q) {
+    if (my_valid && qrow < sqv) {
+      const uint16_t* qp = p.q + qoff + (int64_t)qhead * p.q_sh + (int64_t)qpos * p.q_ss + 8 * hsel;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
-  } else {
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4_t*)(qp + 16 * ks);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
+    }
   }
   const uint16_t* kg = p.k + koff + (int64_t)hk * p.k_sh;
   const uint16_t* vg = p.v + voff + (int64_t)hk * p.v_sh;

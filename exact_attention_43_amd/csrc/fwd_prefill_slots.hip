@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
   constexpr int LDS = 4 * SLOT_LDS > XO + XM ? 4 * SLOT_LDS : XO + XM;
   static_assert(LDS <= 160 * 1024 && 4 * 64 * D * 2 <= LDS, "LDS budget (stages, partials, O tile)");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
-  static_assert(offsetof(SlotParams, slot) % 16 == 0, "a work group's 4 entries are one 16-byte load");
+  static_assert(offsetof(SlotParams, slot) % 32 == 0, "a work group's 4 pairs are one 32-byte load");
   const FwdParams p = sp.f;
 
   const int tid = threadIdx.x;
@@ -60,17 +60,11 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
   const int l32 = lane & 31;
   uint8_t* const ssm = smem + slot * SLOT_LDS;
 
-  // ---- schedule.  A unit is one (batch entry, query head) and runs n_wg work
-  // groups.  Work group ids go round-robin over the 8 XCDs (id % 8), so id L
-  // is taken as entry L / 8 of XCD L % 8's list, and the lists hold
-  // consecutive (unit, work group) pairs: the work groups of a unit, and of
-  // neighbouring heads (one KV head under GQA), read their K / V through one
-  // XCD's L2.
-  const int L = blockIdx.x;
-  const int gidx = (L & 7) * sp.per_xcd + (L >> 3);
-  if (gidx >= sp.n_units * sp.n_wg) return;  // padding of the last lists (uniform)
-  const int unit = gidx / sp.n_wg, wgi = gidx % sp.n_wg;
-  const int b = unit / p.h_q, h = unit % p.h_q;
+  // ---- schedule: grid (query head, batch entry, work group of the unit).
+  // Work groups are dispatched in linear order, x fastest, round-robin over the
+  // 8 XCDs (id % 8): when h_q x batch is a multiple of 8 every work group of a
+  // head (and the heads of one KV head) reads its K / V through one XCD's L2.
+  const int h = blockIdx.x, b = blockIdx.y, wgi = blockIdx.z;
   const int hk = p.group == 1 ? h : h / p.group;
   const int sq = p.s_q, sk = p.s_k, off = sk - sq;
   // visible 32-key blocks of a 64-row tile (bottom-right aligned masks)
@@ -86,25 +80,17 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
       hi = kmax / BN + 1;
     }
   };
-  auto slot_blocks = [&](uint32_t e, int& lo, int& kg, int& kgn) {
-    int hi;
-    tile_range((int)(e & 0xffffu), lo, hi);
-    kg = (int)((e >> 16) & 7u);
-    kgn = max(1, (int)((e >> 19) & 7u));
-    return ((e >> 24) & 1u) && hi - lo > kg ? (hi - lo - kg + kgn - 1) / kgn : 0;
-  };
-  const u32x4_t wg_slots = *reinterpret_cast<const u32x4_t*>(sp.slot + 4 * wgi);
-  int steps = 0;  // the work group's longest slot (uniform)
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    int lo_, kg_, kgn_;
-    steps = max(steps, slot_blocks(wg_slots[s], lo_, kg_, kgn_));
-  }
-  const uint32_t e = slot == 0 ? wg_slots[0] : slot == 1 ? wg_slots[1] : slot == 2 ? wg_slots[2] : wg_slots[3];
+  const u32x8_t ws8 = *reinterpret_cast<const u32x8_t*>(sp.slot + 8 * wgi);
+  // the work group's longest slot (uniform)
+  const int steps = (int)max(max(ws8[1], ws8[3]), max(ws8[5], ws8[7]));
+  const uint32_t e = slot == 0 ? ws8[0] : slot == 1 ? ws8[2] : slot == 2 ? ws8[4] : ws8[6];
+  const int nb = (int)(slot == 0 ? ws8[1] : slot == 1 ? ws8[3] : slot == 2 ? ws8[5] : ws8[7]);
   const bool used = (e >> 24) & 1u;
   const int tile = (int)(e & 0xffffu);
-  int lo, kg, kgn;
-  const int nb = slot_blocks(e, lo, kg, kgn);
+  const int kg = (int)((e >> 16) & 7u);
+  const int kgn = max(1, (int)((e >> 19) & 7u));
+  int lo, hi_;
+  tile_range(tile, lo, hi_);
   auto blk = [&](int i) { return lo + kg + kgn * i; };
 
   const int64_t qoff = (int64_t)b * p.q_sb, koff = (int64_t)b * p.k_sb, voff = (int64_t)b * p.v_sb;
@@ -389,7 +375,7 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
     const int idx = it * 512 + tid;
     const int row = idx / DCH, chunk = idx % DCH;
     const int rs = row >> 6;
-    const uint32_t es = rs == 0 ? wg_slots[0] : rs == 1 ? wg_slots[1] : rs == 2 ? wg_slots[2] : wg_slots[3];
+    const uint32_t es = rs == 0 ? ws8[0] : rs == 1 ? ws8[2] : rs == 2 ? ws8[4] : ws8[6];
     const int grow = 64 * (int)(es & 0xffffu) + (row & 63);
     if (((es >> 24) & 1u) && ((es >> 16) & 7u) == 0 && grow < sq) {
       const u32x4_t v = *(const u32x4_t*)(smem + row * OROW + 16 * (chunk ^ kswz<D>(row)));
@@ -401,7 +387,7 @@ __global__ void __launch_bounds__(512) prefill_slots_kernel(const SlotParams sp)
 }  // namespace
 
 hipError_t launch_prefill_slots(const SlotParams& sp, bool bf16, bool softcap, hipStream_t stream) {
-  const dim3 grid(8 * sp.per_xcd);
+  const dim3 grid(sp.f.h_q, sp.f.batch, sp.n_wg);
   if (bf16) {
     if (softcap)
       hipLaunchKernelGGL((prefill_slots_kernel<true, true>), grid, dim3(512), 0, stream, sp);

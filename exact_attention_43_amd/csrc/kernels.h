@@ -127,17 +127,17 @@ struct BwdParams {
   const int32_t* cu_k;
 };
 
-// Key-split prefill (head_dim 128, fixed lengths): n_units = batch x h_q units
-// run n_wg work groups each; work group w of every unit runs the 4 slots
-// slot[4 w .. 4 w + 3].  A slot entry holds a 64-row query tile (bits 0-15),
-// its key group kg (bits 16-18) of kgn (bits 19-21) and a used bit (24); key
-// group kg takes the tile's 32-key blocks lo + kg, lo + kg + kgn, ...  The
-// kgn slots of a tile sit in one work group at consecutive positions, kg 0
-// first.  per_xcd = ceil(n_units n_wg / 8).
+// Key-split prefill (head_dim 128, fixed lengths): every (batch entry, query
+// head) unit runs n_wg work groups, grid (h_q, batch, n_wg); work group w runs
+// the 4 slots of slot[8 w .. 8 w + 7], as (entry, block count) pairs.  An entry
+// holds a 64-row query tile (bits 0-15), its key group kg (bits 16-18) of kgn
+// (bits 19-21) and a used bit (24); key group kg takes the tile's 32-key blocks
+// lo + kg, lo + kg + kgn, ...  The kgn slots of a tile sit in one work group at
+// consecutive positions, kg 0 first.
 struct SlotParams {
   FwdParams f;
-  int32_t n_units, n_wg, per_xcd, pad;
-  alignas(16) uint32_t slot[256];  // starts at byte 256: a work group's 4 entries are one 16-byte load
+  int32_t n_wg, pad[3];
+  alignas(32) uint32_t slot[2 * 256];  // starts at byte 256: a work group's 4 pairs are one 32-byte load
 };
 hipError_t launch_prefill_slots(const SlotParams& sp, bool bf16, bool softcap, hipStream_t stream);
 

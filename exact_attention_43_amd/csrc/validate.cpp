@@ -300,6 +300,15 @@ void tile_key_blocks(int t, int s_q, int s_k, int wl, int wr, int* lo, int* hi) 
   }
 }
 
+namespace {
+// slot entry s: tile t's key group k of kgn (w visible blocks); keeps the step count
+void put_slot(SlotSchedule* out, int s, int t, int k, int kgn, int w) {
+  out->slot[s] = (uint32_t)t | ((uint32_t)k << 16) | ((uint32_t)kgn << 19) | (1u << 24);
+  out->nb[s] = w > k ? (uint32_t)((w - k + kgn - 1) / kgn) : 0u;
+  out->steps = std::max(out->steps, (int)out->nb[s]);
+}
+}  // namespace
+
 bool build_slot_schedule(const int* w, int n64, int wg_max, SlotSchedule* out) {
   *out = SlotSchedule{};
   if (n64 < 1 || wg_max < 1) return false;
@@ -341,14 +350,8 @@ bool build_slot_schedule(const int* w, int n64, int wg_max, SlotSchedule* out) {
     const int n_wg = pack();
     if (n_wg > max_wg) continue;
     out->n_wg = n_wg;
-    int steps = 0;
-    for (int t = 0; t < n64; ++t) {
-      steps = std::max(steps, load(t));
-      for (int k = 0; k < kg[t]; ++k)
-        out->slot[4 * bin[t] + pos[t] + k] =
-            (uint32_t)t | ((uint32_t)k << 16) | ((uint32_t)kg[t] << 19) | (1u << 24);
-    }
-    out->steps = steps;
+    for (int t = 0; t < n64; ++t)
+      for (int k = 0; k < kg[t]; ++k) put_slot(out, 4 * bin[t] + pos[t] + k, t, k, kg[t], w[t]);
     return true;
   }
   return false;

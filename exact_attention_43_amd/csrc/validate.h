@@ -112,14 +112,17 @@ constexpr int kMaxSlots = 256;
 struct SlotSchedule {
   int n_wg = 0;   // work groups per unit
   int steps = 0;  // the largest per-slot block count
-  // per slot: tile (bits 0-15), kg (16-18), kgn (19-21), used (bit 24)
+  // per slot: tile (bits 0-15), kg (16-18), kgn (19-21), used (bit 24), and the
+  // number of blocks it computes
   uint32_t slot[kMaxSlots] = {};
+  uint32_t nb[kMaxSlots] = {};
 };
 // Visible 32-key blocks [lo, hi) of 64-row query tile t (bottom-right causal /
 // window offsets; window edges < 0 unbounded).
 void tile_key_blocks(int t, int s_q, int s_k, int wl, int wr, int* lo, int* hi);
-// Builds the schedule for n64 tiles with w[t] visible blocks each, in at most
-// wg_max work groups per unit.  Returns false when the tiles do not fit.
+// For n64 tiles with w[t] visible blocks each, in at most wg_max work groups
+// per unit: the heaviest tiles get the most slots.  Returns false when the
+// tiles do not fit.
 bool build_slot_schedule(const int* w, int n64, int wg_max, SlotSchedule* out);
 
 }  // namespace exattn

@@ -355,6 +355,43 @@ void splits_case(long it, Count& c) {
   ++c.ok;
 }
 
+// the invariants the key-split kernel relies on
+void check_schedule(const SlotSchedule& sc, const int* w, int n64, int wg_max, long it) {
+  expect(sc.n_wg >= 1 && sc.n_wg <= wg_max && sc.n_wg <= kMaxSlots / 4, "schedule work groups", it);
+  static int seen[1024];
+  for (int t = 0; t < n64; ++t) seen[t] = 0;
+  int steps = 0;
+  for (int s = 0; s < 4 * sc.n_wg; ++s) {
+    const uint32_t e = sc.slot[s];
+    if (!(e >> 24)) {
+      expect(sc.nb[s] == 0, "an unused slot computes nothing", it);
+      continue;
+    }
+    const int t = (int)(e & 0xffff), k = (int)((e >> 16) & 7), kn = (int)((e >> 19) & 7);
+    if (t >= n64 || kn < 1 || kn > 4 || k >= kn) {
+      expect(false, "schedule entry out of range", it);
+      continue;
+    }
+    // the tile's slots are consecutive and inside one work group
+    const int first = s - k;
+    expect(first >= 0 && first / 4 == (first + kn - 1) / 4, "tile slots share one work group", it);
+    const int nb = w[t] > k ? (w[t] - k + kn - 1) / kn : 0;
+    expect((int)sc.nb[s] == nb, "slot block count", it);
+    expect(w[t] == 0 || k < w[t], "every slot of a tile with blocks has one", it);
+    ++seen[t];
+    steps = std::max(steps, nb);
+  }
+  for (int t = 0; t < n64; ++t) {
+    const uint32_t e0 = [&] {
+      for (int s = 0; s < 4 * sc.n_wg; ++s)
+        if ((sc.slot[s] >> 24) && (int)(sc.slot[s] & 0xffff) == t && ((sc.slot[s] >> 16) & 7) == 0) return sc.slot[s];
+      return 0u;
+    }();
+    expect(e0 != 0 && seen[t] == (int)((e0 >> 19) & 7), "every tile has its kgn slots", it);
+  }
+  expect(steps == sc.steps, "schedule steps", it);
+}
+
 void slots_case(long it, Count& c) {
   const int n64 = chance(80) ? 1 + pick(64) : size_val(300);
   const int wg_max = chance(80) ? 1 + pick(80) : size_val(100);
@@ -371,33 +408,7 @@ void slots_case(long it, Count& c) {
     return;
   }
   ++c.ok;
-  expect(sc.n_wg >= 1 && sc.n_wg <= wg_max && sc.n_wg <= kMaxSlots / 4, "schedule work groups", it);
-  static int seen[1024];
-  for (int t = 0; t < n64; ++t) seen[t] = 0;
-  int steps = 0;
-  for (int s = 0; s < 4 * sc.n_wg; ++s) {
-    const uint32_t e = sc.slot[s];
-    if (!(e >> 24)) continue;
-    const int t = (int)(e & 0xffff), k = (int)((e >> 16) & 7), kn = (int)((e >> 19) & 7);
-    if (t >= n64 || kn < 1 || kn > 4 || k >= kn) {
-      expect(false, "schedule entry out of range", it);
-      continue;
-    }
-    // the tile's slots are consecutive and inside one work group
-    const int first = s - k;
-    expect(first >= 0 && first / 4 == (first + kn - 1) / 4, "tile slots share one work group", it);
-    ++seen[t];
-    steps = std::max(steps, (w[t] + kn - 1) / kn);
-  }
-  for (int t = 0; t < n64; ++t) {
-    const uint32_t e0 = [&] {
-      for (int s = 0; s < 4 * sc.n_wg; ++s)
-        if ((sc.slot[s] >> 24) && (int)(sc.slot[s] & 0xffff) == t && ((sc.slot[s] >> 16) & 7) == 0) return sc.slot[s];
-      return 0u;
-    }();
-    expect(e0 != 0 && seen[t] == (int)((e0 >> 19) & 7), "every tile has its kgn slots", it);
-  }
-  expect(steps == sc.steps, "schedule steps", it);
+  check_schedule(sc, w, n64, wg_max, it);
 }
 
 }  // namespace

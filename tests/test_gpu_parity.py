@@ -131,7 +131,7 @@ def _launch(b, s_q, h_q, h_kv, d, masked, pack=False):
     groups = 1 if d == 256 or grid >= 2 * cus else 2
     paired = groups == 2 and masked and grid <= cus
     units = b * h_q
-    slots = (paired and 2 * grid <= cus and d == 128 and not pack and units <= cus
+    slots = (paired and 2 * grid <= cus and d == 128 and not pack and units <= cus and b <= 65535
              and math.ceil(s_q / 64) <= 4 * min(cus // units, 64))
     return groups, paired and not slots, slots
 
