@@ -649,14 +649,75 @@ __global__ void __launch_bounds__(512) bwd_dkdv2_kernel(const BwdParams p) {
       }
   };
   if constexpr (NSET == 4) {
-    if (set >= 2) publish(wave - 4);  // waves 4-7: slots 0-3
+    // All 8 waves finalize: wave (set s, w4) owns head-dim tile s of its 32
+    // keys.  It publishes the 3 tiles the other sets own, sums its own tile
+    // over the 4 sets in the fixed order (s0 + s2) + (s1 + s3), and writes it,
+    // rounded, into a [64 keys][128 dims] LDS tile that all threads then store
+    // as whole rows (16 bytes per thread); dK first, then dV.
+    static_assert(DT == NSET, "one head-dim tile per set");
+    static_assert(8 * DT * 16 * 64 * 4 + 2 * KEYS * D * 2 <= LDS, "partials and two output tiles");
+    float* const part = reinterpret_cast<float*>(smem);  // [wave][dt][j][lane][4]
+    uint8_t* const tile_k = smem + 8 * DT * 16 * 64 * 4;
+    uint8_t* const tile_v = tile_k + KEYS * D * 2;
+    auto pslot = [&](int w, int dt, int j) { return part + (((w * DT + dt) * 4 + j) * 64 + lane) * 4; };
+    auto publish_m = [&](const f32x16_t(&m)[DT]) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        if (dt != set) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(f32x4_t*)pslot(wave, dt, j) = f32x4_t{m[dt][4 * j], m[dt][4 * j + 1], m[dt][4 * j + 2], m[dt][4 * j + 3]};
+        }
+    };
+    // this wave's tile summed over the sets, rounded into the output tile,
+    // 4 registers (one row group J) at a time
+    auto finalize = [&](const f32x16_t(&m)[DT], uint8_t* tile, float mul) {
+      const int key = 32 * w4 + l32;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        f32x4_t x[4];  // set t's values of registers 4 J .. 4 J + 3
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t == set) {
+            x[t] = f32x4_t{m[0][4 * J], m[0][4 * J + 1], m[0][4 * J + 2], m[0][4 * J + 3]};
+#pragma unroll
+            for (int dt = 1; dt < DT; ++dt)
+              if (dt == set) x[t] = f32x4_t{m[dt][4 * J], m[dt][4 * J + 1], m[dt][4 * J + 2], m[dt][4 * J + 3]};
+          } else {
+            x[t] = *(const f32x4_t*)pslot(t * WPS + w4, set, J);
+          }
+        }
+        const f32x4_t r = (x[0] + x[2]) + (x[1] + x[3]);
+        u32x2_t w;  // head dims 32 set + 8 J + 4 hsel + 0..3
+        w[0] = E::pack2(r[0] * mul, r[1] * mul);
+        w[1] = E::pack2(r[2] * mul, r[3] * mul);
+        const int chunk = 4 * set + J;
+        *(u32x2_t*)(tile + key * (D * 2) + 16 * (chunk ^ kswz<D>(key)) + 8 * hsel) = w;
+      }
+    };
+    // the output tile to global memory, 16 bytes per thread, whole rows
+    auto store_tile = [&](const uint8_t* tile, uint16_t* base, int64_t ss, int64_t sh) {
+#pragma unroll
+      for (int it = 0; it < KEYS * DCH / 512; ++it) {
+        const int idx = it * 512 + tid;
+        const int key = idx / DCH, chunk = idx % DCH;
+        if (k0 + key < sk) {
+          const u32x4_t val = *(const u32x4_t*)(tile + key * (D * 2) + 16 * (chunk ^ kswz<D>(key)));
+          *(u32x4_t*)(base + (int64_t)(k0 + key) * ss + (int64_t)hk * sh + 8 * chunk) = val;
+        }
+      }
+    };
+    publish_m(dk);
     __syncthreads();
-    if (set < 2) absorb(wave);  // wave w (set 0 or 1) takes wave w + 4's partial
+    finalize(dk, tile_k, p.scale);
+    __syncthreads();  // every dK partial read: the region takes dV's
+    publish_m(dv);
+    store_tile(tile_k, p.dk + sp.dk, p.dk_ss, p.dk_sh);
     __syncthreads();
-    if (set == 1) publish(w4);
+    finalize(dv, tile_v, 1.0f);
     __syncthreads();
-    if (set != 0) return;
-    absorb(w4);
+    store_tile(tile_v, p.dv + sp.dv, p.dv_ss, p.dv_sh);
+    return;
   } else {
     if (set == 1) publish(w4);
     __syncthreads();
