@@ -938,32 +938,59 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
         if (nf + NG * (t + 1) < n_hi) step(k1s, v1s, k0s, v0s, nf + NG * (t + 1));
       }
     }
-    // group 1 hands its partial dQ^T to group 0 through LDS (the stages are free
-    // once every wave has passed the barrier)
+    // Both groups finalize: wave (group g, slice w) owns head-dim tiles
+    // g DT/2 .. (g + 1) DT/2 - 1 of its 32 rows.  It publishes the other half
+    // through LDS (the stages are free once every wave has passed the
+    // barrier), adds the partner group's partial of its own half (a sum of two
+    // terms: the same result in either order), and rounds it into an LDS tile
+    // of the 64 rows that all threads then store as whole rows (16 bytes per
+    // thread).
     static_assert(NG == 2, "two groups");
+    constexpr int HT = DT / 2;  // head-dim tiles per group
+    constexpr int XQ = NG * NW * HT * 16 * 64 * 4;
+    static_assert(XQ + kDqRows * D * 2 <= (int)sizeof(smem), "partials and the output tile");
     __syncthreads();
-    float* xq = reinterpret_cast<float*>(smem);  // [wave][dt][4][lane][4]
-    if (grp == 1) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4_t w = {dq[dt][4 * j], dq[dt][4 * j + 1], dq[dt][4 * j + 2], dq[dt][4 * j + 3]};
-          *(f32x4_t*)(xq + (((wave * DT + dt) * 4 + j) * 64 + lane) * 4) = w;
-        }
-    }
-    __syncthreads();
-    if (grp != 0) return;
+    float* const xq = reinterpret_cast<float*>(smem);  // [group][wave][half tile][j][lane][4]
+    uint8_t* const otile = smem + XQ;                  // [64 rows][D] 16-bit, chunks swizzled
+    auto xslot = [&](int g, int w, int t, int j) { return xq + ((((g * NW + w) * HT + t) * 4 + j) * 64 + lane) * 4; };
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
+      if (dt / HT != grp) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t w = *(const f32x4_t*)(xq + (((wave * DT + dt) * 4 + j) * 64 + lane) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dq[dt][4 * j + e] += w[e];
+        for (int j = 0; j < 4; ++j)
+          *(f32x4_t*)xslot(grp, wave, dt % HT, j) =
+              f32x4_t{dq[dt][4 * j], dq[dt][4 * j + 1], dq[dt][4 * j + 2], dq[dt][4 * j + 3]};
       }
+    __syncthreads();
+    const int orow = 32 * wave + l32;  // this lane's row in the tile
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      if (dt / HT == grp) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const f32x4_t o = *(const f32x4_t*)xslot(1 - grp, wave, dt % HT, J);
+          const f32x4_t r = f32x4_t{dq[dt][4 * J], dq[dt][4 * J + 1], dq[dt][4 * J + 2], dq[dt][4 * J + 3]} + o;
+          u32x2_t w;  // head dims 32 dt + 8 J + 4 hsel + 0..3
+          w[0] = E::pack2(r[0] * p.scale, r[1] * p.scale);
+          w[1] = E::pack2(r[2] * p.scale, r[3] * p.scale);
+          const int chunk = 4 * dt + J;
+          *(u32x2_t*)(otile + orow * (D * 2) + 16 * (chunk ^ qswz<D>(orow)) + 8 * hsel) = w;
+        }
+      }
+    __syncthreads();
+    constexpr int NTH = 64 * NW * NG;
+    static_assert(kDqRows * DCH % NTH == 0, "output tile copy");
+#pragma unroll
+    for (int it = 0; it < kDqRows * DCH / NTH; ++it) {
+      const int idx = it * NTH + tid;
+      const int row = idx / DCH, chunk = idx % DCH;
+      if (q0 + row < sq) {
+        const u32x4_t val = *(const u32x4_t*)(otile + row * (D * 2) + 16 * (chunk ^ qswz<D>(row)));
+        *(u32x4_t*)(p.dq + sp.dq + (int64_t)(q0 + row) * p.dq_ss + (int64_t)h * p.dq_sh + 8 * chunk) = val;
+      }
+    }
+    return;
   }
-
   // ---- dQ = scale (dQ^T)^T: lane holds head dims 32 dt + 8 J + 4 H + 0..3 of row qrow.
   if (qrow < sq) {
     uint16_t* op = p.dq + sp.dq + (int64_t)qrow * p.dq_ss + (int64_t)h * p.dq_sh;
