@@ -938,27 +938,30 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
         if (nf + NG * (t + 1) < n_hi) step(k1s, v1s, k0s, v0s, nf + NG * (t + 1));
       }
     }
-    // Both groups finalize: wave (group g, slice w) owns head-dim tiles
-    // g DT/2 .. (g + 1) DT/2 - 1 of its 32 rows.  It publishes the other half
-    // through LDS (the stages are free once every wave has passed the
-    // barrier), adds the partner group's partial of its own half (a sum of two
-    // terms: the same result in either order), and rounds it into an LDS tile
-    // of the 64 rows that all threads then store as whole rows (16 bytes per
-    // thread).
-    static_assert(NG == 2, "two groups");
-    constexpr int HT = DT / 2;  // head-dim tiles per group
-    constexpr int XQ = NG * NW * HT * 16 * 64 * 4;
+    // Every group finalizes: wave (group g, slice w) owns head-dim tiles
+    // g HT .. (g + 1) HT - 1 of its 32 rows (HT = DT / NG).  It publishes the
+    // other tiles through LDS (the stages are free once every wave has passed
+    // the barrier), sums its own tiles over the groups in a fixed order (g0 + g1;
+    // with 4 groups (g0 + g2) + (g1 + g3)), and rounds them into an LDS tile of
+    // the 64 rows that all threads then store as whole rows (16 bytes per thread).
+    static_assert(NG == 2 || NG == 4, "two or four groups");
+    constexpr int HT = DT / NG;      // head-dim tiles per group
+    constexpr int PT = DT - HT;      // tiles a wave publishes
+    static_assert(HT >= 1, "a head-dim tile per group");
+    constexpr int XQ = NG * NW * PT * 16 * 64 * 4;
     static_assert(XQ + kDqRows * D * 2 <= (int)sizeof(smem), "partials and the output tile");
     __syncthreads();
-    float* const xq = reinterpret_cast<float*>(smem);  // [group][wave][half tile][j][lane][4]
+    float* const xq = reinterpret_cast<float*>(smem);  // [group][wave][published tile][j][lane][4]
     uint8_t* const otile = smem + XQ;                  // [64 rows][D] 16-bit, chunks swizzled
-    auto xslot = [&](int g, int w, int t, int j) { return xq + ((((g * NW + w) * HT + t) * 4 + j) * 64 + lane) * 4; };
+    auto xslot = [&](int g, int w, int t, int j) { return xq + ((((g * NW + w) * PT + t) * 4 + j) * 64 + lane) * 4; };
+    // slot of tile dt among group g's published tiles
+    auto pidx = [](int g, int dt) { return dt < g * HT ? dt : dt - HT; };
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       if (dt / HT != grp) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *(f32x4_t*)xslot(grp, wave, dt % HT, j) =
+          *(f32x4_t*)xslot(grp, wave, pidx(grp, dt), j) =
               f32x4_t{dq[dt][4 * j], dq[dt][4 * j + 1], dq[dt][4 * j + 2], dq[dt][4 * j + 3]};
       }
     __syncthreads();
@@ -968,8 +971,16 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
       if (dt / HT == grp) {
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-          const f32x4_t o = *(const f32x4_t*)xslot(1 - grp, wave, dt % HT, J);
-          const f32x4_t r = f32x4_t{dq[dt][4 * J], dq[dt][4 * J + 1], dq[dt][4 * J + 2], dq[dt][4 * J + 3]} + o;
+          f32x4_t x[NG];  // group g's partial of registers 4 J .. 4 J + 3
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+            x[g] = g == grp ? f32x4_t{dq[dt][4 * J], dq[dt][4 * J + 1], dq[dt][4 * J + 2], dq[dt][4 * J + 3]}
+                            : *(const f32x4_t*)xslot(g, wave, pidx(g, dt), J);
+          f32x4_t r;
+          if constexpr (NG == 2)
+            r = x[0] + x[1];
+          else
+            r = (x[0] + x[2]) + (x[1] + x[3]);
           u32x2_t w;  // head dims 32 dt + 8 J + 4 hsel + 0..3
           w[0] = E::pack2(r[0] * p.scale, r[1] * p.scale);
           w[1] = E::pack2(r[2] * p.scale, r[3] * p.scale);
