@@ -243,6 +243,22 @@ def test_prefill_key_split(case):
         assert_lse_close(l_cpu[:, h], l_ref[:, h], f"key-split s{seed} h{h}")
 
 
+def test_prefill_key_split_full_table():
+    """The key-split schedule at its largest (256 tiles of 64 rows, one per slot of 64
+    work groups): b1 s16384 h1 causal, sampled rows at tile and work-group boundaries
+    against the oracle."""
+    b, sq, hq = 1, 16384, 1
+    assert _launch(b, sq, hq, hq, 128, True)[2], "shape does not take the key-split kernel"
+    q, k, v = W.qkv(b, sq, sq, hq, hq, 128, seed=611, dtype=torch.bfloat16)
+    out, lse = ex.attn_func(*_dev(q, k, v), causal=True)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 63, 64, 255, 256, 4095, 4096, 8191, 8192, 12287, 16320, 16383}
+                  | set(np.random.default_rng(611).integers(0, sq, 24).tolist()))
+    o_ref, l_ref = oracle.attention(q, k, v, causal=True, rows=rows)
+    assert_o_close(out[:, rows].cpu(), o_ref[:, rows], torch.bfloat16, "key-split full table")
+    assert_lse_close(lse[:, :, rows].cpu(), l_ref[:, :, rows], "key-split full table")
+
+
 # Packed GQA (FAQ Q15): the rows of all query heads of a KV head share the tiles.
 PACK_CASES = [
     # b, s_q, s_k, h_q, h_kv, d, dtype, causal, window, softcap, seed
