@@ -1,5 +1,6 @@
-// Key-split prefill for launches of about one work group per CU under a
-// causal or window mask (head_dim 128, fixed lengths).
+// Key-split prefill for causal or windowed launches whose one-tile-per-head
+// grid leaves CUs idle (head_dim 128, fixed lengths; the host takes it where
+// the paired launch would fill at most half of the CUs).
 //
 // It computes what fwd_prefill.hip computes (S = scale Q K^T, P = softmax(S),
 // O = P V with the online softmax of "FlashAttention完整说明", section 二.1, and
@@ -9,7 +10,8 @@
 // heavy tile per work group evens the work groups out, but inside one the SIMD
 // that holds a light tile's wave and a heavy tile's wave runs most steps with
 // one busy wave, and a lone wave leaves the MFMA unit idle while it waits for
-// LDS and runs its exponentials.  Here a work group has 4 slots of 2 waves
+// LDS and runs its exponentials; and a small grid leaves CUs with nothing to
+// do.  Here a work group has 4 slots of 2 waves
 // (32 rows each); a slot takes one 64-row tile and every kgn-th 32-key block
 // of the tile's visible range, starting at block kg.  The host picks kgn per
 // tile (heavy tiles get up to 4 slots, all in one work group) and packs the
