@@ -1174,9 +1174,12 @@ def test_graph_capture_decode_replays():
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
 
 
-def test_graph_capture_prefill_and_backward():
+@pytest.mark.parametrize("pack", [None, 0], ids=["auto", "unpacked"])
+def test_graph_capture_prefill_and_backward(pack):
     """The forward and the backward captured in one graph (fixed addresses, FAQ Q19) replay
-    to the eager results, with eager work and synchronisations between the replays."""
+    to the eager results, with eager work and synchronisations between the replays (the
+    automatic choice packs the GQA heads here; unpacked, the forward is the key-split
+    kernel)."""
     q, k, v = W.qkv(2, 300, 300, 8, 2, 128, seed=409)
     dout = W.qkv(2, 300, 1, 8, 1, 128, seed=410)[0]
     dq_, dk_, dv_, ddo = _dev(q, k, v, dout)
@@ -1185,8 +1188,11 @@ def test_graph_capture_prefill_and_backward():
     gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
 
+    if pack == 0:
+        assert _launch(2, 300, 8, 2, 128, True)[2], "unpacked, the shape takes the key-split kernel"
+
     def calls():
-        ex.attn_func(dq_, dk_, dv_, causal=True, out=out, lse=lse)
+        ex.attn_func(dq_, dk_, dv_, causal=True, out=out, lse=lse, pack_gqa=pack)
         ex.attn_backward(ddo, dq_, dk_, dv_, out, lse, causal=True, dq=gq, dk=gk, dv=gv, workspace=ws)
 
     calls()
