@@ -26,7 +26,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libexattn.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["fwd_prefill.hip", "fwd_prefill_slots.hip", "fwd_decode.hip", "fwd_fp8.hip", "bwd.hip", "exattn_api.cpp"]
+HIP_SOURCES = ["fwd_prefill.hip", "fwd_prefill_slots.hip", "fwd_prefill_dsplit.hip", "fwd_decode.hip", "fwd_fp8.hip", "bwd.hip", "exattn_api.cpp"]
 HOST_SOURCES = ["validate.cpp"]
 
 

@@ -145,18 +145,29 @@ exattn_status exattn_fwd(const exattn_fwd_args* a, void* stream) {
     if (p.pair_tiles && 2 * (int64_t)pl.grid <= cus && pl.head_dim == 128 && !pl.varlen && !pl.pack &&
         units <= cus && a->batch <= 65535)
       slots = slot_schedule(pl.s_q, pl.s_k, pl.wl, pl.wr, cus / (int)units, &sch);
+    // At d = 256 (not packed) the head-dim-split kernel runs: two waves per
+    // SIMD where the general kernel fits one.  With fewer 128-row tiles than
+    // CUs it takes 64-row tiles and splits their key blocks between two groups.
+    int dsplit = 0;
+    if (pl.head_dim == 256 && !pl.pack && a->batch <= 65535) {
+      const int64_t n64 = ((int64_t)pl.s_q + 63) / 64;
+      dsplit = pl.grid < cus && n64 <= 65535 ? 2 : 1;
+      if (dsplit == 2) p.n_qt = (int32_t)n64;
+    }
     if (debug_level() >= 1) {
       char buf[256];
       snprintf(buf, sizeof buf,
                "fwd %s d=%d softcap=%d varlen=%d b=%d sq=%d sk=%d hq=%d hkv=%d wl=%d wr=%d grid=%d groups=%d "
-               "pair=%d pack=%d slots=%d",
+               "pair=%d pack=%d slots=%d dsplit=%d",
                pl.bf16 ? "bf16" : "fp16", pl.head_dim, (int)pl.softcap, (int)pl.varlen, a->batch, pl.s_q,
                pl.s_k, a->heads_q, a->heads_kv, pl.wl, pl.wr, pl.grid, groups, p.pair_tiles, p.pack,
-               slots ? sch.n_wg : 0);
+               slots ? sch.n_wg : 0, dsplit);
       debug_once(buf, buf);
     }
     hipError_t e;
-    if (slots) {
+    if (dsplit) {
+      e = launch_prefill_dsplit(p, pl.bf16, dsplit, pl.softcap, static_cast<hipStream_t>(stream));
+    } else if (slots) {
       static_assert(sizeof(SlotParams::slot) == 2 * sizeof(SlotSchedule::slot), "slot table");
       SlotParams sp{};
       sp.f = p;

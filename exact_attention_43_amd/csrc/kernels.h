@@ -141,6 +141,13 @@ struct SlotParams {
 };
 hipError_t launch_prefill_slots(const SlotParams& sp, bool bf16, bool softcap, hipStream_t stream);
 
+// Head-dim-split prefill at head_dim 256 (not packed): two waves share 32 rows,
+// one per half of the head dims.  groups 1: 128-row tiles, all 8 waves on the
+// tile's key blocks; groups 2: 64-row tiles, two key groups of 4 waves.  Grid
+// (h_q, batch, n_qt) with n_qt counted in tiles of that size.
+hipError_t launch_prefill_dsplit(const FwdParams& p, bool bf16, int groups, bool softcap,
+                                 hipStream_t stream);
+
 int prefill_rows_per_tile();
 // groups: 1 or 2 groups of 4 waves per work group (d = 256 always uses 1).
 hipError_t launch_prefill(const FwdParams& p, bool bf16, int head_dim, bool softcap, int grid,

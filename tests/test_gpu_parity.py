@@ -123,17 +123,21 @@ def _dense_grid(b, s_q, h_q):
 
 def _launch(b, s_q, h_q, h_kv, d, masked, pack=False):
     """The prefill launch the library picks (exattn_api.cpp) for fixed lengths:
-    (groups, paired, key-split).  The key-split kernel replaces the paired launch at
-    d = 128 without packing when that launch fills at most half of the CUs and the
-    schedule fits (at most one unit per CU and 4 slots per work group)."""
+    (groups, paired, key-split, head-dim split).  The key-split kernel replaces the
+    paired launch at d = 128 without packing when that launch fills at most half of
+    the CUs and the schedule fits (at most one unit per CU and 4 slots per work
+    group).  At d = 256 without packing the head-dim-split kernel runs, with two key
+    groups (64-row tiles) when there are fewer 128-row tiles than CUs."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid = b * h_kv * math.ceil(s_q * (h_q // h_kv) / 128) if pack else _dense_grid(b, s_q, h_q)
+    if d == 256 and not pack:
+        return 0, False, False, 2 if grid < cus else 1
     groups = 1 if d == 256 or grid >= 2 * cus else 2
     paired = groups == 2 and masked and grid <= cus
     units = b * h_q
     slots = (paired and 2 * grid <= cus and d == 128 and not pack and units <= cus and b <= 65535
              and math.ceil(s_q / 64) <= 4 * min(cus // units, 64))
-    return groups, paired and not slots, slots
+    return groups, paired and not slots, slots, 0
 
 
 # Every instance of the prefill kernel template, each at a shape that makes the
@@ -144,7 +148,8 @@ INSTANCE_CASES = []
 for _dt in (torch.float16, torch.bfloat16):
     for _d in (64, 128, 256):
         for _cap in (0.0, 30.0):
-            for _kind in (("one",) if _d == 256 else ("one", "two", "paired") + (("slots",) if _d == 128 else ())):
+            for _kind in (("one", "dsplit1", "dsplit2") if _d == 256 else
+                          ("one", "two", "paired") + (("slots",) if _d == 128 else ())):
                 INSTANCE_CASES.append((_dt, _d, _cap, _kind))
 
 
@@ -152,6 +157,10 @@ def _instance_shape(d, kind):
     # (b, s_q, s_k, h_q, h_kv, causal, window)
     if kind == "one":
         return (2, 2100, 2100, 16, 4, True, (-1, -1)) if d < 256 else (2, 1100, 1100, 8, 4, True, (-1, -1))
+    if kind == "dsplit1":
+        return (2, 1100, 1300, 16, 4, True, (-1, -1))
+    if kind == "dsplit2":
+        return (1, 1000, 1100, 4, 2, False, (-1, -1))
     if kind == "two":
         return (1, 700, 900, 8, 2, False, (-1, -1))
     return (1, 1024, 1024, 4, 2, True, (-1, -1))
@@ -166,14 +175,17 @@ def test_prefill_instances(case):
     idx = INSTANCE_CASES.index(case)
     # a negative scale: causal one-group and paired launches at d = 128, and the
     # two-group launches with softcap
-    neg = (d == 128 and kind in ("one", "paired", "slots")) or (kind == "two" and cap > 0)
+    neg = (d == 128 and kind in ("one", "paired", "slots")) or (kind == "two" and cap > 0) or \
+        (kind == "dsplit2" and cap > 0)
     scale = -0.7 / math.sqrt(d) if neg else None
     # at d = 128 the paired kernel is reached through packed GQA (dense
-    # shapes take the key-split kernel there)
-    pack = kind == "paired" and d == 128
+    # shapes take the key-split kernel there), and so is the general kernel at
+    # d = 256 (dense shapes take the head-dim-split kernel)
+    pack = (kind == "paired" and d == 128) or (kind == "one" and d == 256)
     got = _launch(b, sq, hq, hkv, d, causal or window != (-1, -1), pack)
-    want = {"one": (1, False, False), "two": (2, False, False), "paired": (2, True, False),
-            "slots": (2, False, True)}[kind]
+    want = {"one": (1, False, False, 0), "two": (2, False, False, 0), "paired": (2, True, False, 0),
+            "slots": (2, False, True, 0), "dsplit1": (0, False, False, 1),
+            "dsplit2": (0, False, False, 2)}[kind]
     if kind == "one" and d != 256:
         assert _dense_grid(b, sq, hq) >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
     assert got == want, f"shape picks {got}, not {kind}"
@@ -259,6 +271,65 @@ def test_prefill_key_split_full_table():
     assert_lse_close(lse[:, :, rows].cpu(), l_ref[:, :, rows], "key-split full table")
 
 
+# Head-dim-split launches at d = 256 (fwd_prefill_dsplit.hip): two waves share 32
+# rows, one per half of the head dims, and add their half scores through LDS.  One
+# key group (128-row tiles) where there are at least as many tiles as CUs, else two
+# (64-row tiles whose key blocks alternate between the groups, merged at the end).
+# The shapes vary the launch, masks, GQA, softcap, the sign of the scale, empty
+# rows, odd and even block counts per group and ragged tails.
+DSPLIT_CASES = [
+    # b, s_q, s_k, h_q, h_kv, dtype, causal, window, softcap, scale, seed
+    (2, 2048, 2048, 8, 8, torch.bfloat16, False, (-1, -1), 0.0, None, 620),    # one group, plain
+    (4, 1024, 1024, 16, 4, torch.bfloat16, True, (200, 0), 0.0, None, 621),    # one group, window, GQA
+    (2, 1100, 1300, 16, 16, torch.float16, True, (-1, -1), 30.0, -0.05, 622),  # one group, cap, scale < 0
+    (2, 700, 700, 4, 4, torch.float16, False, (64, 64), 0.0, None, 623),       # two groups, two-sided
+    (1, 300, 100, 2, 1, torch.bfloat16, True, (-1, -1), 0.0, None, 624),       # rows without keys
+    (2, 33, 33, 3, 3, torch.float16, True, (-1, -1), 30.0, None, 625),         # one partial tile
+    (1, 64, 5000, 2, 2, torch.bfloat16, False, (-1, -1), 0.0, None, 626),      # 157 blocks: odd split
+    (1, 129, 129, 2, 1, torch.bfloat16, False, (0, 0), 0.0, None, 627),        # window of one key
+    (1, 500, 2000, 4, 2, torch.bfloat16, False, (-1, 100), 2.0, None, 628),    # right edge, saturating cap
+]
+
+
+@pytest.mark.parametrize("case", DSPLIT_CASES, ids=[f"s{c[-1]}" for c in DSPLIT_CASES])
+def test_prefill_dsplit(case):
+    b, sq, sk, hq, hkv, dt, causal, window, cap, scale, seed = case
+    masked = causal or window != (-1, -1)
+    assert _launch(b, sq, hq, hkv, 256, masked)[3], "shape does not take the head-dim-split kernel"
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, 256, seed=seed, dtype=dt)
+    if cap == 2.0:
+        q, k = (q.float() * 4).to(dt), (k.float() * 4).to(dt)
+    dq, dk, dv = _dev(q, k, v)
+    out = _poison_out(q.shape, dt)
+    lse = _poison_lse((b, hq, sq))
+    kw = dict(causal=causal, window_size=window, softcap=cap, softmax_scale=scale)
+    ex.attn_func(dq, dk, dv, out=out, lse=lse, pack_gqa=0, **kw)
+    torch.cuda.synchronize()
+    heads = None if b * hq * sq * sk <= (1 << 24) else sorted({0, hq // 2 + 1, hq - 1})
+    o_ref, l_ref = oracle.attention(q, k, v, heads=heads, **kw)
+    o_cpu, l_cpu = out.cpu(), lse.cpu()
+    for h in (range(hq) if heads is None else heads):
+        assert_o_close(o_cpu[:, :, h], o_ref[:, :, h], dt, f"dsplit {seed} h{h}")
+        assert_lse_close(l_cpu[:, h], l_ref[:, h], f"dsplit {seed} h{h}")
+
+
+def test_prefill_dsplit_varlen():
+    """Varlen at d = 256 through the head-dim-split kernel (unpacked GQA 8 / 2,
+    causal): an empty sequence, one of a single row, tails at every tile size."""
+    lens_q = [1, 130, 0, 64, 300]
+    lens_k = [5, 130, 9, 700, 200]
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, 8, 2, 256, seed=629)
+    dq, dk, dv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    out = _poison_out(q.shape, q.dtype)
+    lse = _poison_lse((8, q.shape[0]))
+    ex.attn_varlen_func(dq, dk, dv, dcq, dck, max(lens_q), max(lens_k), causal=True, pack_gqa=0, out=out,
+                        lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal=True)
+    assert_o_close(out, o_ref, q.dtype, "dsplit varlen")
+    assert_lse_close(lse, l_ref, "dsplit varlen")
+
+
 # Packed GQA (FAQ Q15): the rows of all query heads of a KV head share the tiles.
 PACK_CASES = [
     # b, s_q, s_k, h_q, h_kv, d, dtype, causal, window, softcap, seed
@@ -299,7 +370,7 @@ def test_pack_gqa(case):
                 assert_lse_close(l[:, h], l_ref[:, h], f"pack={pack} h{h}")
     masked = causal or window != (-1, -1)
     on, off = _launch(b, sq, hq, hkv, d, masked, True), _launch(b, sq, hq, hkv, d, masked, False)
-    if on[0] == off[0] and not on[2] and not off[2]:
+    if on[0] == off[0] and not on[2] and not off[2] and not on[3] and not off[3]:
         assert torch.equal(res[True][0], res[False][0]) and torch.equal(res[True][1], res[False][1])
 
 
