@@ -61,38 +61,38 @@ __device__ __forceinline__ int kswz(int key) { return D >= 128 ? key & 15 : key 
 template <int D>
 __device__ __forceinline__ int vswz(int key) { return D >= 128 ? 2 * (key & 7) : 2 * (key & 3); }
 
-// Buffer descriptor over the rows kbase .. min(nk, kbase + rows) - 1 of heads
-// hk0 .. hk0+nh-1 (row stride ss, head stride sh elements): loads past the
-// last valid element return zeros (per-dword range check of raw buffer loads).
-// Word 3 is the gfx9 default.
-template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* row0, int64_t ss, int64_t sh,
-                                                            int nrows, int nh) {
-  const int64_t last = (int64_t)(nrows - 1) * ss + (int64_t)(nh - 1) * sh + D;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)row0, 0, (int)(last * 2), 0x00020000);
+// 16 bytes per lane from a buffer into LDS at lds + 16 * lane (lds
+// wave-uniform).  The buffer starts at base and holds `bytes` bytes: raw buffer
+// loads past its end return zeros (a per-dword range check), which covers the
+// last step's missing rows; word 3 is the gfx9 default.  Issued from inline
+// asm so that the compiler does not track it: it cannot tell which ring slot
+// a load writes, and tracked, every LDS read after it would wait for all of
+// them.  The kernel waits with explicit vmcnt counts before its barriers.
+__device__ __forceinline__ void dma16(const uint16_t* base, int64_t bytes, uint8_t* lds, uint32_t voffset) {
+  const uint64_t a = (uint64_t)base;
+  const u32x4_t rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
 }
-
-// 16 bytes per lane from a buffer into LDS at lds + 16 * lane (lds must be
-// wave-uniform).  Kept out of lambdas: the host pass of the compiler drops the
-// kernel stub when this builtin sits in a lambda body.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset,
-                                           0, 0, 0);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <bool BF16, int D, bool SOFTCAP, int HPWV, bool PAGED>
 __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecParams p) {
   using E = Elem<BF16>;
   constexpr int NW = DecCfg<D>::NW;
-  constexpr int KTILE = 16 * NW * HPWV * 2 * D;  // bytes of the K (or V) tile of one stage
-  constexpr int STAGE = 2 * KTILE;
+  constexpr int KTILE = 16 * NW * HPWV * 2 * D;  // bytes of the K (or V) tile of one step
+  constexpr int NSLOT = 5;                       // ring of K / V tiles: a step's two, three in flight
   constexpr int KS = D / 32;                     // k-steps of S^T = K Q^T over head_dim
   constexpr int DT = D / 16;                     // 16-column tiles of O^T
   constexpr int KI = KTILE / (NW * 1024);        // DMA instructions per wave per tile
   constexpr int MERGE = NW * (2 * 64 + DT * 4 * 64) * 4;
-  constexpr int SMEM = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
+  constexpr int SMEM = NSLOT * KTILE > MERGE ? NSLOT * KTILE : MERGE;
   static_assert(KI >= 1 && KTILE % (NW * 1024) == 0, "tile / wave mismatch");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   prefetch_kernargs<sizeof(DecParams)>();
@@ -158,29 +158,40 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     const int pg = bt[(int64_t)b * p.bt_stride + key / p.page_size];
     return min(max(pg, 0), p.num_pages - 1);
   };
-  // DMA of step st's K and V tiles into the stage at dst; pg: its page if paged.
-  auto issue = [&](int st, uint8_t* dst, int pg) {
+  // DMA of step st's K (V) tile into the ring slot at dst; pg: its page if
+  // paged.  The descriptor covers the step's rows of the work group's heads.
+  auto issue_k = [&](int st, uint8_t* dst, int pg) {
     const int kbase = kb + st * KSTEP;
     const int nrows = min(nk - kbase, KSTEP);
     const uint16_t* k0 = kg + (int64_t)kbase * p.k_ss;
-    const uint16_t* v0 = vg + (int64_t)kbase * p.v_ss;
-    if (paged) {
-      const int64_t r = kbase % p.page_size;
-      k0 = p.k + (int64_t)pg * p.k_sp + r * p.k_ss + (int64_t)hk0 * p.k_sh;
-      v0 = p.v + (int64_t)pg * p.v_sp + r * p.v_ss + (int64_t)hk0 * p.v_sh;
-    }
-    const __amdgpu_buffer_rsrc_t rk = rows_rsrc<D>(k0, p.k_ss, p.k_sh, nrows, nh_valid);
-    const __amdgpu_buffer_rsrc_t rv = rows_rsrc<D>(v0, p.v_ss, p.v_sh, nrows, nh_valid);
+    if (paged) k0 = p.k + (int64_t)pg * p.k_sp + (int64_t)(kbase % p.page_size) * p.k_ss + (int64_t)hk0 * p.k_sh;
+    const int64_t bytes = ((int64_t)(nrows - 1) * p.k_ss + (int64_t)(nh_valid - 1) * p.k_sh + D) * 2;
 #pragma unroll
-    for (int t = 0; t < KI; ++t) buffer_load_lds16(rk, dst + (wave + NW * t) * 1024, kofs[t]);
-#pragma unroll
-    for (int t = 0; t < KI; ++t) buffer_load_lds16(rv, dst + KTILE + (wave + NW * t) * 1024, vofs[t]);
+    for (int t = 0; t < KI; ++t) dma16(k0, bytes, dst + (wave + NW * t) * 1024, kofs[t]);
   };
+  auto issue_v = [&](int st, uint8_t* dst, int pg) {
+    const int kbase = kb + st * KSTEP;
+    const int nrows = min(nk - kbase, KSTEP);
+    const uint16_t* v0 = vg + (int64_t)kbase * p.v_ss;
+    if (paged) v0 = p.v + (int64_t)pg * p.v_sp + (int64_t)(kbase % p.page_size) * p.v_ss + (int64_t)hk0 * p.v_sh;
+    const int64_t bytes = ((int64_t)(nrows - 1) * p.v_ss + (int64_t)(nh_valid - 1) * p.v_sh + D) * 2;
+#pragma unroll
+    for (int t = 0; t < KI; ++t) dma16(v0, bytes, dst + (wave + NW * t) * 1024, vofs[t]);
+  };
+  // ring slot of tile i (step s_lo + i / 2, K for even i, V for odd)
+  auto slot_of = [&](int i) { return smem + (i % NSLOT) * KTILE; };
 
   // the first step's DMA goes out before the Q loads (with an append it waits
   // for the new rows, below)
+  // (tiles 0-2: K and V of step s_lo and K of step s_lo + 1)
   const bool early = p.seq_add == 0 && s_lo < s_hi;
-  if (early) issue(s_lo, smem, paged ? page_of(kb + s_lo * KSTEP) : 0);
+  auto prologue = [&]() {
+    const int pg0 = paged ? page_of(kb + s_lo * KSTEP) : 0;
+    issue_k(s_lo, slot_of(0), pg0);
+    issue_v(s_lo, slot_of(1), pg0);
+    if (s_lo + 1 < s_hi) issue_k(s_lo + 1, slot_of(2), paged ? page_of(kb + (s_lo + 1) * KSTEP) : 0);
+  };
+  if (early) prologue();
 
   // ---- Q^T fragments (B operand): lane (query column l16, group g16) holds
   // Q[head][32 ks + 8 g16 .. + 7] of query head hk * group + hg * 16 + l16.
@@ -231,19 +242,8 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     for (int dt = 0; dt < DT; ++dt) oacc[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One step: start the DMA of step st + 1 into stage nxt, then compute step st
-  // from stage cur.  The two stages never overlap; restrict tells the compiler
-  // so, which lets the operand reads of cur proceed while the DMA into nxt is
-  // in flight (without it every LDS read waits for all outstanding DMA).
-  // pg_next: the page of the next step to issue, read one step ahead.
-  int pg_next = 0;
-  auto step = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int st) {
-    if (st + 1 < s_hi) {
-      issue(st + 1, nxt, pg_next);
-      if (paged && st + 2 < s_hi) pg_next = page_of(kb + (st + 2) * KSTEP);
-    }
-    const uint8_t* kt = cur;
-    const uint8_t* vt = cur + KTILE;
+  // One step: compute step st from its K and V tiles (kt, vt).
+  auto step = [&](const uint8_t* __restrict__ kt, const uint8_t* __restrict__ vt, int st) {
     const int key0 = kb + st * KSTEP + 16 * sub;  // first key of this wave's sub-block
 #pragma unroll
     for (int i = 0; i < HPWV; ++i) {
@@ -333,19 +333,27 @@ __global__ void __launch_bounds__(DecCfg<D>::NW * 64) decode_kernel(const DecPar
     __syncthreads();
   }
 
-  if (s_lo < s_hi) {
-    if (!early) issue(s_lo, smem, paged ? page_of(kb + s_lo * KSTEP) : 0);
-    if (paged && s_lo + 1 < s_hi) pg_next = page_of(kb + (s_lo + 1) * KSTEP);
-  }
+  if (s_lo < s_hi && !early) prologue();
+  // pages of steps st + 1 and st + 2, read ahead by scalar loads
+  int pg1 = paged && s_lo + 1 < s_hi ? page_of(kb + (s_lo + 1) * KSTEP) : 0;
+  int pg2 = paged && s_lo + 2 < s_hi ? page_of(kb + (s_lo + 2) * KSTEP) : 0;
   for (int st = s_lo; st < s_hi; ++st) {
-    // this work group's loads of step st have landed, and every wave is done
-    // with step st - 1, whose stage the next loads refill
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (((st - s_lo) & 1) == 0)
-      step(smem, smem + STAGE, st);
+    // Tiles 2r, 2r + 1 (step st) have landed once only this wave's K load of
+    // step st + 1 may still be in flight; after the barrier every wave is done
+    // with step st - 1, whose two slots take V of step st + 1 and K of st + 2.
+    const int r = st - s_lo;
+    if (st + 1 < s_hi)
+      wait_vmcnt<KI>();
     else
-      step(smem + STAGE, smem, st);
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (st + 1 < s_hi) issue_v(st + 1, slot_of(2 * r + 3), pg1);
+    if (st + 2 < s_hi) issue_k(st + 2, slot_of(2 * r + 4), pg2);
+    if (paged) {
+      pg1 = pg2;
+      if (st + 3 < s_hi) pg2 = page_of(kb + (st + 3) * KSTEP);
+    }
+    step(slot_of(2 * r), slot_of(2 * r + 1), st);
   }
 
   // ---- row sums over the four lane groups; merge the waves of a head slot.
