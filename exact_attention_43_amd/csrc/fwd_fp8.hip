@@ -17,7 +17,10 @@
 // Layout per work group: NW waves x 32 query rows of one query head; a wave's
 // lane owns one query row (S^T = K Q^T, Q^T the B operand from registers).
 // With NG = 2 a second group of NW waves takes every other key block of the
-// same rows, and the groups' (max, sum, O) merge through LDS at the end.
+// same rows, and the groups' (max, sum, O) merge through LDS at the end.  With
+// one group (large grids) and no softcap the loop is software-pipelined: the
+// QK MFMAs of a block are interleaved with the exponentials of the block
+// before, against a lazy reference max.
 // Key blocks of 64 rows stream by DMA into double-buffered LDS as FP8.  K is
 // read as A operands; V is read with the 8-bit transposing read, whose lane i
 // receives byte i % 8 of 8 rows (the rows of source lanes 2 e + i / 8 of its
@@ -81,7 +84,10 @@ __device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* p) {
       u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p)));
 }
 
-template <int D, int NW, int NG, bool SOFTCAP>
+constexpr float kLazyTau = 8.0f;   // the pipelined loop moves a row's reference only when its max grows by > 2^8
+constexpr float kSumCap = 256.0f;  // 2^tau: a lane's block sum below it means every p <= 2^tau
+
+template <int D, int NW, int NG, bool SOFTCAP, bool PIPE>
 __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Params p) {
   constexpr int BN = kF8Keys;
   constexpr int NT2 = BN / 32;       // 32-key tiles per block
@@ -294,7 +300,199 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
   // of iterations so that every wave meets every barrier.
   uint8_t* const s0 = smem + grp * 2 * STAGE;
   uint8_t* const s1 = s0 + STAGE;
-  if constexpr (NG == 1) {
+  if constexpr (PIPE) {
+    // ---- software-pipelined loop (one group, no softcap, scale != 0): step i
+    // computes S(b_i) = K(b_i) Q^T with the exponentials of S(b_{i-1})
+    // interleaved between its MFMAs, then the check, the softmax fix-up if
+    // needed and O += P V of b_{i-1}.  The exponentials use a lazy reference
+    // m_ref (moved only when a block's max exceeds it by more than 2^8, so O and
+    // the sum always share one reference), which needs no block max up front.
+    // K(b_i) and V(b_i) live in stage i & 1; step i loads K(b_{i+1}) and V(b_i)
+    // (their stage parts were last read in step i - 1).  Scores stay raw until
+    // the exponentials, exp2(s scale - m_ref) being one FMA and one exp; a
+    // masked score is set to -inf x sign(scale), which the FMA turns into -inf.
+    static_assert(NG == 1 && !SOFTCAP, "pipelined loop: one group, no softcap");
+    constexpr int NA = KS * NT2;        // FP8 MFMAs of S^T = K Q^T per block
+    constexpr int EPM = 16 * NT2 / NA;  // exponentials per such MFMA
+    static_assert(EPM >= 2 && EPM % 2 == 0, "exponential pairs per MFMA");
+    const float mval = p.scale_log2 > 0.f ? -__builtin_inff() : __builtin_inff();
+    const int nb = n_hi - n_lo;
+    float m_ref = -__builtin_inff();  // reference (log2 domain) of this lane's row
+    float l_run = 0.f;                // this lane's share of the row sum against m_ref
+    auto exps = [&](const f32x16_t (&sc)[NT2], u32x4_t (&pf)[NT2][2], float base) {
+      float psum = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float x0 = fast_exp2(__builtin_fmaf(sc[t2][r], p.scale_log2, -base));
+          const float x1 = fast_exp2(__builtin_fmaf(sc[t2][r + 1], p.scale_log2, -base));
+          pf[t2][r >> 3][(r & 7) >> 1] = Elem<true>::pack2(x0, x1);
+          psum += x0 + x1;
+        }
+      return psum;
+    };
+    // the block's max exceeds the reference by more than 2^8 for some row, or
+    // the reference is unset: move it (rescaling O and the sum) and redo the
+    // exponentials
+    auto slow = [&](const f32x16_t (&sc)[NT2], u32x4_t (&pf)[NT2][2]) {
+      float mb = -__builtin_inff();
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, sc[t2][r] * p.scale_log2);
+      mb = halves_max(mb);
+      const bool need = mb > m_ref + kLazyTau;
+      const float m_new = need ? mb : m_ref;
+      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
+      if (__builtin_amdgcn_ballot_w64(need && m_ref != -__builtin_inff()) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      }
+      l_run *= alpha;
+      m_ref = m_new;
+      return exps(sc, pf, m_ref == -__builtin_inff() ? 0.f : m_ref);
+    };
+    // S(b_i) into sn from K stage kc, interleaved with the exponentials of sc =
+    // S(b_{i-1}); then (ap) its check and O += P V from V stage vp
+    auto fused = [&](const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vp, const f32x16_t (&sc)[NT2],
+                     f32x16_t (&sn)[NT2], bool ap) {
+      // K(b_i) operands first, then V(b_{i-1}) (needed only after the
+      // exponentials): LDS reads complete in order
+      i32x8_t ka[KS][NT2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t2 = 0; t2 < NT2; ++t2) {
+          const u32x4_t lo = *(const u32x4_t*)(kc + kaddr[ks][0] + t2 * 32 * D);
+          const u32x4_t hi = *(const u32x4_t*)(kc + kaddr[ks][1] + t2 * 32 * D);
+          ka[ks][t2] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+      u32x2_t vw[NT2][2][DT];
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vw[t2][c][dt] = lds_read_tr8(vp + vaddr[dt] + (32 * t2 + 16 * c) * D);
+      u32x4_t pf[NT2][2];
+      float psum = 0.f;
+      const float base = m_ref;
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2) sn[t2] = f32x16_t{};
+      // one MFMA, then its share of the exponentials, in this order: a wave
+      // issues its exponentials while its MFMAs run (the scheduling barriers
+      // keep the compiler from regrouping them)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t2 = 0; t2 < NT2; ++t2) {
+          const int mi = ks * NT2 + t2;
+          __builtin_amdgcn_sched_barrier(0);
+          sn[t2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[ks][t2], qf[ks], sn[t2], 0, 0, 0, 127, 0, 127);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < EPM; u += 2) {
+            const int e = mi * EPM + u, t = e >> 4, r = e & 15;
+            const float x0 = fast_exp2(__builtin_fmaf(sc[t][r], p.scale_log2, -base));
+            const float x1 = fast_exp2(__builtin_fmaf(sc[t][r + 1], p.scale_log2, -base));
+            pf[t][r >> 3][(r & 7) >> 1] = Elem<true>::pack2(x0, x1);
+            psum += x0 + x1;
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      // consume the exponentials and the scores here: LLVM would otherwise sink
+      // the exponentials below the branch that follows and the score MFMAs
+      // below the PV products, out of one instruction stream
+#pragma unroll
+      for (int t = 0; t < NT2; ++t) asm volatile("" ::"v"(pf[t][0]), "v"(pf[t][1]));
+      asm volatile("" ::"v"(psum));
+#pragma unroll
+      for (int t2 = 0; t2 < NT2; ++t2) asm volatile("" ::"v"(sn[t2][0]));  // one word waits for the MFMA
+      if (ap) {
+        if (__builtin_amdgcn_ballot_w64(!(psum <= kSumCap)) != 0) psum = slow(sc, pf);  // also inf, NaN
+        l_run += psum;
+#pragma unroll
+        for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const u32x2_t w = vw[t2][c][dt];
+              u32x4_t av;
+              av[0] = f8pair_bf16<false>(w[0]), av[1] = f8pair_bf16<true>(w[0]);
+              av[2] = f8pair_bf16<false>(w[1]), av[3] = f8pair_bf16<true>(w[1]);
+              o[dt] = Elem<true>::mfma32x32x16(av, pf[t2][c], o[dt]);
+            }
+      }
+    };
+    auto issue_k = [&](int n, uint8_t* dst) {
+      const int kb = n * BN;
+      const int64_t lastk = (int64_t)min(sk - 1 - kb, BN - 1) * p.k_ss + D;
+      const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kg + (int64_t)kb * p.k_ss, lastk);
+#pragma unroll
+      for (int i = 0; i < SLICES / NW; ++i) buffer_load_lds16(rk, dst + (NW * i + wave) * 1024, kofs[i]);
+    };
+    auto issue_v = [&](int n, uint8_t* dst) {
+      const int kb = n * BN;
+      const int64_t lastv = (int64_t)min(sk - 1 - kb, BN - 1) * p.v_ss + D;
+      const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vg + (int64_t)kb * p.v_ss, lastv);
+#pragma unroll
+      for (int i = 0; i < SLICES / NW; ++i) buffer_load_lds16(rv, dst + F8TILE + (NW * i + wave) * 1024, vofs[i]);
+    };
+    // step i: kc = the stage of b_i (K read, V(b_i) loaded into it), vp = the
+    // stage of b_{i-1} (V read); the other stage takes K(b_{i+1})
+    auto step = [&](uint8_t* __restrict__ kc, uint8_t* __restrict__ vp, int i, const f32x16_t (&sc)[NT2],
+                    f32x16_t (&sn)[NT2]) {
+      uint8_t* const kn = kc == s0 ? s1 : s0;
+      if (i + 1 < nb) issue_k(n_lo + i + 1, kn);
+      if (i < nb) issue_v(n_lo + i, kc);
+      // A wave's first step still runs the exponentials, on stale registers, and
+      // its last runs S = K Q^T on a stale stage: both results are discarded.
+      fused(kc, vp + F8TILE, sc, sn, i > 0);
+      if (i < nb) {
+        const int kb0 = (n_lo + i) * BN;
+        const bool full = q0w + 32 <= sq && kb0 + BN <= sk && (p.wr < 0 || kb0 + BN - 1 <= q0w + off + p.wr) &&
+                          (p.wl < 0 || kb0 >= q0w + 31 + off - p.wl);
+        if (!full) {
+#pragma unroll
+          for (int t2 = 0; t2 < NT2; ++t2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb0 + 32 * t2 + 16 * (r >> 3) + 8 * hsel + (r & 7);
+              if (!f8_visible(qrow, key, sk, off, p.wl, p.wr)) sn[t2][r] = mval;
+            }
+        }
+      }
+    };
+    // consume Q before the loop (one word of each 16-byte load), so that the
+    // compiler waits for those loads once instead of inside the steps
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks][0]), "v"(qf[ks][4]));
+    f32x16_t sa[NT2], sb[NT2];
+#pragma unroll
+    for (int t2 = 0; t2 < NT2; ++t2) sa[t2] = sb[t2] = f32x16_t{};
+    if (nb > 0) issue_k(n_lo, s0);
+    // Unrolled by two so each call sees fixed stages and score registers.
+    // Before each step: K(b_i) and V(b_{i-1}) have landed, and every wave is
+    // done with the previous step.
+    int i = 0;
+    for (; i + 1 <= nb; i += 2) {
+      wait_vmem_all();
+      __syncthreads();
+      step(s0, s1, i, sb, sa);
+      wait_vmem_all();
+      __syncthreads();
+      step(s1, s0, i + 1, sa, sb);
+    }
+    if (i <= nb) {
+      wait_vmem_all();
+      __syncthreads();
+      step(s0, s1, i, sb, sa);
+    }
+    m = m_ref;
+    l = halves_sum(l_run);
+  } else if constexpr (NG == 1) {
     if (n_lo < n_hi) issue(n_lo, s0);
     for (int n = n_lo; n < n_hi; n += 2) {
       wait_vmem_all();
@@ -388,9 +586,13 @@ hipError_t launch_fp8_t(const Fp8Params& p, hipStream_t stream) {
   // causal b2 s1024 h16 d128 shape); with more tiles the split only adds the merge
   // (1114 us against 1032 at s16384).
   if (grid < 1024)
-    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 2, SOFTCAP>), dim3((unsigned)grid), dim3(64 * NW * 2), 0, stream, p);
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 2, SOFTCAP, false>), dim3((unsigned)grid), dim3(64 * NW * 2), 0,
+                       stream, p);
+  else if (!SOFTCAP && p.scale_log2 != 0.f)
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 1, false, true>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 1, SOFTCAP>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((fp8_prefill_kernel<D, NW, 1, SOFTCAP, false>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       p);
   return hipGetLastError();
 }
 

@@ -932,14 +932,14 @@ FP8_CASES = [
 ]
 
 
-def _check_fp8(out, lse, q, k, v, ds, causal, window, cap, where):
+def _check_fp8(out, lse, q, k, v, ds, causal, window, cap, where, scale=None):
     """O and LSE of one FP8 call (4-D tensors, one batch entry or more) against the oracle on
     the decoded inputs."""
     dsq, dsk, dsv = ds
     b, sq, hq, d = q.shape
     sk, hkv = k.shape[1], k.shape[2]
     ro, rl = oracle.attention_fp8(q, k, v, q_descale=dsq, k_descale=dsk, v_descale=dsv, causal=causal,
-                                  window_size=window, softcap=cap)
+                                  window_size=window, softcap=cap, softmax_scale=scale)
     # FAQ Q10's FP8 tolerance is for values at the codes' own scale: O is compared after
     # dividing by v_descale (the real V is code x v_descale, so P's rounding moves O by
     # amounts proportional to it).
@@ -956,7 +956,7 @@ def _check_fp8(out, lse, q, k, v, ds, causal, window, cap, where):
     g = hq // hkv
     mag = np.stack([np.stack([(qa[bi, :, h] @ ka[bi, :, h // g].T).max(axis=1) if sk else np.zeros(sq)
                               for h in range(hq)]) for bi in range(b)])  # (b, h, s_q)
-    scale_eff = abs(dsq * dsk) / math.sqrt(d)
+    scale_eff = abs(dsq * dsk) * (abs(scale) if scale is not None else 1.0 / math.sqrt(d))
     lg = lse.detach().cpu().numpy().astype(np.float64)
     assert np.array_equal(np.isneginf(lg), np.isneginf(rl)), f"{where} LSE: -inf pattern differs"
     fin = ~np.isneginf(rl)
@@ -983,6 +983,52 @@ def test_fp8_forward(case):
     assert out.dtype == torch.bfloat16
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
     _check_fp8(out, lse, q, k, v, (dsq, dsk, dsv), causal, window, 0.0, "fp8")
+
+
+# 1024 tiles and more without softcap take the software-pipelined loop (QK of one
+# block beside the exponentials of the one before, a lazy softmax reference),
+# unless scale x descales is 0.
+FP8_PIPE_CASES = [
+    # b, s_q, s_k, h_q, h_kv, d, causal, window, (q, k, v descale), softmax scale, seed
+    (1, 2048, 2048, 32, 32, 128, True, (-1, -1), (1.0, 1.0, 1.0), -0.06, 230),   # negative scale
+    (1, 4096, 1000, 16, 4, 64, True, (-1, -1), (1.0, 2.0, 1.0), None, 231),      # rows without keys
+    (1, 2048, 2048, 32, 32, 128, False, (200, 50), (0.0, 1.0, 1.0), None, 232),  # scale 0: plain loop
+    (1, 2048, 2048, 32, 8, 128, False, (-1, -1), (4.0, 4.0, 1.0), None, 233),    # large scores: rescales
+]
+
+
+@pytest.mark.parametrize("case", FP8_PIPE_CASES, ids=[f"f{c[-1]}" for c in FP8_PIPE_CASES])
+def test_fp8_pipelined(case):
+    b, sq, sk, hq, hkv, d, causal, window, ds, scale, seed = case
+    assert b * hq * math.ceil(sq / 64) >= 1024, "shape does not take the one-group kernel"
+    q, k, v = W.qkv(b, sq, sk, hq, hkv, d, seed=seed, dtype=torch.float8_e4m3fn)
+    gq, gk, gv = _dev(q, k, v)
+    out, lse = ex.attn_func_fp8(gq, gk, gv, q_descale=ds[0], k_descale=ds[1], v_descale=ds[2],
+                                softmax_scale=scale, causal=causal, window_size=window)
+    torch.cuda.synchronize()
+    _check_fp8(out, lse, q, k, v, ds, causal, window, 0.0, "fp8 pipelined", scale=scale)
+
+
+def test_fp8_varlen_pipelined():
+    """Varlen FP8 through the pipelined loop (1024 tiles and more over the longest
+    sequence): sequences of 1, 3000 and 2500 rows, causal."""
+    lens_q = [3000, 1, 2500]
+    lens_k = [3000, 40, 2600]
+    hq, hkv, d, ds = 16, 4, 128, (0.5, 2.0, 1.5)
+    assert len(lens_q) * hq * math.ceil(max(lens_q) / 64) >= 1024
+    q, k, v, cu_q, cu_k = W.varlen_qkv(lens_q, lens_k, hq, hkv, d, seed=234, dtype=torch.float8_e4m3fn)
+    gq, gk, gv, dcq, dck = _dev(q, k, v, cu_q, cu_k)
+    out = torch.full((q.shape[0], hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((hq, q.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+    ex.attn_varlen_func_fp8(gq, gk, gv, dcq, dck, max(lens_q), max(lens_k), q_descale=ds[0], k_descale=ds[1],
+                            v_descale=ds[2], causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    for i in range(len(lens_q)):
+        a, e = int(cu_q[i]), int(cu_q[i + 1])
+        ka, ke = int(cu_k[i]), int(cu_k[i + 1])
+        _check_fp8(out[None, a:e], lse[None, :, a:e], q[None, a:e], k[None, ka:ke], v[None, ka:ke], ds, True,
+                   (-1, -1), 0.0, f"fp8 varlen pipelined seq {i}")
 
 
 FP8_CAP_CASES = [
