@@ -427,6 +427,8 @@ def fp8_timing(ex, W, w, steps, warmup):
     a.lse_stride[:] = [lse.stride(0), lse.stride(1)]
     a.causal = 1 if w.causal else 0
     a.window_left = a.window_right = -1
+    a.softmax_scale = float("nan")  # the default 1/sqrt(head_dim), as in the 16-bit forward
+    a.softcap = 0.0
     ds = ex.Fp8Descale(1.0, 1.0, 1.0)
     L = ex.lib()
     ref, dref = C.byref(a), C.byref(ds)
