@@ -7,7 +7,9 @@
 // a KV head's dK and dV sum over the query heads that read it.
 //
 // gfx950 design, deterministic (no atomics):
-// - bwd_prep_kernel: D_i = dO_i . O_i and LSE in the log2 domain per row;
+// - bwd_dq_kernel (launched first, below) also forms each query row's
+//   statistics, D_i = dO_i . O_i and LSE in the log2 domain, from the O and dO
+//   rows it loads, and stores them for the dK/dV kernel;
 // - bwd_dkdv_kernel: a work group owns 128 keys (32 per wave) of one KV head and
 //   walks the query blocks (32 rows) of every query head in its group.  K and V
 //   of its keys stay in registers; Q, dO and the rows' statistics stream
@@ -71,47 +73,6 @@ __device__ __forceinline__ float hi_f32(uint32_t w) {
     return __builtin_bit_cast(float, w & 0xffff0000u);
   else
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
-// Per row: LSE log2 e (+inf for a row without keys, so that exp2(s - lse2) = 0
-// everywhere) and D_i = dO_i . O_i (fp32), stored as one pair.  D / 8 lanes per
-// row read 16 bytes of O and dO each; grid (row blocks, heads, batch).
-template <bool BF16, int D>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const int i = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  const int h = blockIdx.y, b = blockIdx.z;
-  // row i of sequence b: token offsets (varlen) or batch offsets
-  int sq = p.s_q;
-  int64_t ob = (int64_t)b * p.o_sb, db = (int64_t)b * p.do_sb, lb = (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
-  if (p.cu_q != nullptr) {
-    const int qs = p.cu_q[b];
-    sq = p.cu_q[b + 1] - qs;
-    ob = (int64_t)qs * p.o_ss;
-    db = (int64_t)qs * p.do_ss;
-    lb = (int64_t)h * p.lse_sh + qs;
-  }
-  const bool in = i < sq;
-  float acc = 0.f;
-  if (in) {
-    const u32x4_t a = *(const u32x4_t*)(p.o + ob + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh + 8 * part);
-    const u32x4_t g = *(const u32x4_t*)(p.dout + db + (int64_t)i * p.do_ss + (int64_t)h * p.do_sh + 8 * part);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = __builtin_fmaf(lo_f32<BF16>(a[e]), lo_f32<BF16>(g[e]), acc);
-      acc = __builtin_fmaf(hi_f32<BF16>(a[e]), hi_f32<BF16>(g[e]), acc);
-    }
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (in && part == 0) {
-    const float lse = p.lse[lb + i];
-    f32x2_t st;
-    st[0] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
-    st[1] = acc;
-    *(f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * p.s_q + i)) = st;
-  }
 }
 
 // Softcap: P = 2^(c log2 e tanh(s scale / c) - LSE log2 e), and the gradient
@@ -803,10 +764,19 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
       df[ks] = in ? *(const u32x4_t*)(dp + 16 * ks) : u32x4_t{0, 0, 0, 0};
     }
   }
-  f32x2_t rst;  // (lse2, D) of this lane's row
-  rst[0] = __builtin_inff(), rst[1] = 0.f;
-  if (qrow < sq) rst = *(const f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * sqm + qrow));
-  const float lse2 = rst[0], drow = rst[1];
+  // O of this lane's row in the layout of dO^T (for D_i = dO_i . O_i), and its LSE
+  u32x4_t of[KS];
+  float lse_in = kNegInf;
+  {
+    const bool in = qrow < sq;
+    const uint16_t* op = p.o + sp.o + (int64_t)qrow * p.o_ss + (int64_t)h * p.o_sh + 8 * hsel;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) of[ks] = in ? *(const u32x4_t*)(op + 16 * ks) : u32x4_t{0, 0, 0, 0};
+    const int64_t lb = p.cu_q != nullptr ? (int64_t)h * p.lse_sh + p.cu_q[b]
+                                         : (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
+    if (in) lse_in = p.lse[lb + qrow];
+  }
+  float lse2, drow;  // the row's statistics, formed below
 
   const uint16_t* kg = p.k + sp.k + (int64_t)hk * p.k_sh;
   const uint16_t* vg = p.v + sp.v + (int64_t)hk * p.v_sh;
@@ -911,8 +881,30 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
     if (n + NG < n_hi) issue(n + NG, kn, vn);
     block(n, kc, vc);
   };
+  // The rows' statistics, (LSE log2 e, D_i): LSE -inf (a row without keys) becomes +inf, so
+  // that exp2(s - lse2) = 0 everywhere.  Work group 0 of the tile publishes them for the
+  // dK/dV kernel, which runs after this one.  Computed after the first K/V DMA is issued,
+  // so that waiting for O does not delay it.
+  auto row_stats = [&]() __attribute__((always_inline)) {
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(lo_f32<BF16>(of[ks][e]), lo_f32<BF16>(df[ks][e]), acc);
+        acc = __builtin_fmaf(hi_f32<BF16>(of[ks][e]), hi_f32<BF16>(df[ks][e]), acc);
+      }
+    drow = acc + xor32(acc);  // the lane halves hold the two halves of the head dims
+    lse2 = lse_in == kNegInf ? __builtin_inff() : lse_in * kLog2e;
+    if (grp == 0 && hsel == 0 && qrow < sq) {
+      f32x2_t st;
+      st[0] = lse2, st[1] = drow;
+      *(f32x2_t*)(p.ws_stats + 2 * (((int64_t)b * p.h_q + h) * sqm + qrow)) = st;
+    }
+  };
   if constexpr (NG == 1) {
     if (n_lo < n_hi) issue(n_lo, k0s, v0s);
+    row_stats();
     for (int n = n_lo; n < n_hi; n += 2) {
       wait_vmem_all();
       __syncthreads();
@@ -928,6 +920,7 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
     const int iters = (n_hi - n_lo + NG - 1) / NG;
     const int nf = n_lo + grp;
     if (nf < n_hi) issue(nf, k0s, v0s);
+    row_stats();
     for (int t = 0; t < iters; t += 2) {
       wait_vmem_all();
       __syncthreads();
@@ -1019,16 +1012,27 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
 
 template <bool BF16, int D, bool SOFTCAP>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  // A kernel whose grid would be empty is skipped: with no query rows dK and dV
-  // are zero (the dK/dV kernel sees no query block), with no keys dQ is zero
-  // (the dQ kernel sees no key block).
-  const int64_t rows = (int64_t)p.batch * p.s_q * p.h_q;
+  // The dQ kernel runs first: it also writes every query row's statistics
+  // (LSE log2 e, dO . O), which the dK/dV kernel reads.  A kernel whose grid
+  // would be empty is skipped: with no query rows dK and dV are zero (the dK/dV
+  // kernel sees no query block), with no keys dQ is zero (the dQ kernel sees no
+  // key block).
   hipError_t e = hipSuccess;
-  if (rows > 0) {
-    constexpr int rows_per_wg = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>),
-                       dim3((unsigned)((p.s_q + rows_per_wg - 1) / rows_per_wg), p.h_q, p.batch), dim3(256), 0,
-                       stream, p);
+  const int n_qt = (p.s_q + kDqRows - 1) / kDqRows;
+  if (n_qt > 0) {
+    const int grid = n_qt * p.h_q * p.batch;
+    // Fewer than 1024 tiles leave under two waves per SIMD on 256 CUs: split each
+    // tile's key blocks between two wave groups then.  At d = 256 the one-group
+    // kernel's 64-key blocks need more registers than a wave has: two groups of
+    // 32-key blocks always.
+    bool two = true;
+    if constexpr (D != 256) two = grid < 1024;
+    if (two) {
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves * 2), 0, stream, p);
+    } else {
+      if constexpr (D != 256)
+        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1057,24 +1061,6 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, SOFTCAP, 1>), dim3(n_kt * p.h_kv * p.batch), dim3(256), 0,
                          stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int n_qt = (p.s_q + kDqRows - 1) / kDqRows;
-  if (n_qt > 0) {
-    const int grid = n_qt * p.h_q * p.batch;
-    // Fewer than 1024 tiles leave under two waves per SIMD on 256 CUs: split each
-    // tile's key blocks between two wave groups then.  At d = 256 the one-group
-    // kernel's 64-key blocks need more registers than a wave has: two groups of
-    // 32-key blocks always.
-    bool two = true;
-    if constexpr (D != 256) two = grid < 1024;
-    if (two) {
-      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves * 2), 0, stream, p);
-    } else {
-      if constexpr (D != 256)
-        hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 1, SOFTCAP>), dim3(grid), dim3(64 * kDqWaves), 0, stream, p);
-    }
     e = hipGetLastError();
   }
   return e;
