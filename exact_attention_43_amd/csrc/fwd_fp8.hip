@@ -112,7 +112,20 @@ __global__ void __launch_bounds__(64 * NW * NG) fp8_prefill_kernel(const Fp8Para
   const int rows_wg = 32 * NW;
   const int n_qt = (p.s_q + rows_wg - 1) / rows_wg;
   const int units = p.batch * p.h_q;
-  const int qt = n_qt - 1 - (int)blockIdx.x / units;  // heaviest (last) tiles first
+  // Tiles heaviest (last) first.  With two groups under a one-sided mask (causal),
+  // where the whole grid is resident at once (two work groups per CU), the second
+  // half of the grid runs lightest first instead: work groups i and i + grid/2 tend to
+  // share a CU, and then carry a heavy and a light tile (measured 22.2 -> 21.4 us at
+  // causal b2 s1024 h16 d128, -3% at b4 s1024 h8).
+  int qt;
+  {
+    const int kq = (int)blockIdx.x / units;
+    const int half = (n_qt + 1) / 2;
+    if (NG == 2 && (p.wr >= 0) != (p.wl >= 0))
+      qt = kq < half ? n_qt - 1 - kq : kq - half;
+    else
+      qt = n_qt - 1 - kq;
+  }
   const int u = blockIdx.x % units;
   const int b = u / p.h_q, h = u % p.h_q;
   const int hk = h / p.group;
