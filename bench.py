@@ -355,8 +355,8 @@ def run_decode(ex, W, args):
 
 
 def run_backward(ex, W, args):
-    """The backward of the causal prefill workload: one step is one exattn_bwd call (three
-    kernels: row statistics, dK/dV, dQ) on resident q, k, v, o, lse and dO."""
+    """The backward of the causal prefill workload: one step is one exattn_bwd call (two
+    kernels: dQ with the row statistics, then dK/dV) on resident q, k, v, o, lse and dO."""
     import ctypes as C
     import torch
     w = W.WORKLOADS["causal_prefill"]
