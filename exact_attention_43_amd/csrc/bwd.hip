@@ -882,9 +882,9 @@ __global__ void __launch_bounds__(64 * kDqWaves * NG) bwd_dq_kernel(const BwdPar
     block(n, kc, vc);
   };
   // The rows' statistics, (LSE log2 e, D_i): LSE -inf (a row without keys) becomes +inf, so
-  // that exp2(s - lse2) = 0 everywhere.  Work group 0 of the tile publishes them for the
-  // dK/dV kernel, which runs after this one.  Computed after the first K/V DMA is issued,
-  // so that waiting for O does not delay it.
+  // that exp2(s - lse2) = 0 everywhere.  The waves of group 0 store them for the dK/dV
+  // kernel, which runs after this one.  Computed after the first K/V DMA is issued, so
+  // that waiting for O does not delay it.
   auto row_stats = [&]() __attribute__((always_inline)) {
     float acc = 0.f;
 #pragma unroll
